@@ -1,0 +1,201 @@
+"""Benchmark of the WKV-7 state-slot hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one decode call of the 256-active-slot workload: a pool of 1024
+fp32 state slots, H=32 heads of N=64, one token per active slot with bf16
+r,w,k,v,a,b drawn from the synthetic recipe (fresh inputs every step, all
+pre-generated in HBM before timing). W untimed steps, then exactly K timed
+steps bracketed by device synchronisation. Prints ONE JSON line.
+
+The line carries the decode kernel's roofline (algorithmic bytes per launch
+over its average duration, timed with HIP events on the launch stream), the
+float64 CPU oracle's rate on a bounded sample of the same workload, and, when
+built, a chunked-prefill leg (8 sequences of 4096 tokens, H=32).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+METRIC = ("WKV-7 tokens/s (decode B slots; prefill) + % of HBM peak / MFMA "
+          "util, 1 GPU")
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+N = 64
+
+
+def decode_bytes_per_token_head(in_bytes: int = 2) -> int:
+    """State read + written (fp32), six input vectors, fp32 output."""
+    return 2 * 4 * N * N + 6 * N * in_bytes + N * 4
+
+
+def kernel_sha(name: str) -> str:
+    p = os.path.join(ROOT, "linear_attention_rnn_amd", "csrc", name)
+    with open(p, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(kind: str, bytes_alg: float):
+    """HBM bytes per launch from committed rocprofv3 PMC counters, if they
+    were taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", f"{kind}_traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        t = json.load(f)
+    if t.get("kernel_sha") != kernel_sha(t["kernel_src"]):
+        return None
+    return float(t["hbm_bytes_per_launch"])
+
+
+def run_decode(steps: int, warmup: int, seed: int = 1):
+    import torch
+    import wkv7_inputs as G
+    from linear_attention_rnn_amd import wkv7 as W
+
+    dev = torch.device("cuda:0")
+    n_slots, n_active, H = 1024, 256, 32
+    rng = np.random.default_rng(seed)
+    ids = rng.permutation(n_slots)[:n_active].astype(np.int32)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    pool = W.wkv7_pool_create(n_slots, H, N)
+    try:
+        # resident states N(0, 0.1) in every slot
+        init = torch.randn((n_slots, H, N, N), device=dev, generator=gen) * 0.1
+        W.wkv7_resume(pool, np.arange(n_slots, dtype=np.int32), init)
+        del init
+        total = steps + warmup
+        xs = [G.draw_tokens_device(gen, n_active, H, N, "bf16", dev)
+              for _ in range(total)]
+        cu = np.arange(n_active + 1, dtype=np.int32)
+        o = torch.empty((n_active, H, N), dtype=torch.float32, device=dev)
+        stream = torch.cuda.current_stream()
+        torch.cuda.synchronize()
+
+        def step(x):
+            W.wkv7_forward(pool, ids, cu, x["r"], x["w"], x["k"], x["v"],
+                           x["a"], x["b"], o, stream=stream)
+
+        for i in range(warmup):
+            step(xs[i])
+        ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            ev0[i].record(stream)
+            step(xs[warmup + i])
+            ev1[i].record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        k_ms = [a.elapsed_time(b) for a, b in zip(ev0, ev1)]
+    finally:
+        W.wkv7_pool_destroy(pool)
+    wall = t1 - t0
+    kernel_ms = float(np.mean(k_ms))
+    bytes_launch = n_active * H * decode_bytes_per_token_head(2)
+    return {
+        "tokens": n_active * steps, "wall_s": wall,
+        "ms_per_step": wall / steps * 1e3,
+        "kernel_ms": kernel_ms, "kernel_ms_median": float(np.median(k_ms)),
+        "bytes_per_launch": bytes_launch, "n_active": n_active, "H": H,
+        "n_slots": n_slots,
+    }
+
+
+def cpu_baseline(seconds: float, seed: int = 1):
+    """The float64 oracle on a bounded sample: whole decode steps of the same
+    256-slot, H=32 batch, repeated until `seconds` have passed."""
+    import wkv7_inputs as G
+    from oracle import wkv7_decode_batch
+
+    wl = G.cfg_decode(seed=seed)
+    S = G.as_f64(wl.init_states)
+    n_steps, t_used = 0, 0.0
+    while t_used < seconds:
+        b = G.decode_step_inputs(seed, n_steps, wl.batch.slot_ids, wl.H, wl.N)
+        x = b.inputs64()
+        t0 = time.perf_counter()
+        _, S = wkv7_decode_batch(S, x)
+        t_used += time.perf_counter() - t0
+        n_steps += 1
+    return {
+        "value": len(wl.batch.slot_ids) * n_steps / t_used,
+        "unit": "tokens/s", "cores": 1, "kind": "oracle",
+        "sample": (f"{n_steps} decode step(s) of the 256-slot H=32 batch "
+                   f"({t_used:.1f} s of CPU time, numpy float64, one thread)"),
+    }
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not "
+              "supported (slots shard across GPUs with no exchange, but no "
+              "multi-GPU run is built)", file=sys.stderr)
+        return 2
+    if args.steps < 1 or args.warmup < 0:
+        print("bench.py: --steps must be >= 1 and --warmup >= 0",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 2
+
+    d = run_decode(args.steps, args.warmup)
+    achieved = d["bytes_per_launch"] / (d["kernel_ms"] * 1e-3) / 1e9
+    traffic = load_traffic("decode", d["bytes_per_launch"])
+    line = {
+        "metric": METRIC,
+        "value": d["tokens"] / d["wall_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": d["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "decode_b256_h32_pool1024_bf16in_f32state",
+            "n_slots": d["n_slots"], "active_slots": d["n_active"],
+            "H": d["H"], "N": N, "input_dtype": "bf16",
+            "state_dtype": "f32", "output_dtype": "f32",
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+            "traffic": traffic,
+            "kernel": "seq_kernel<bf16> (decode)",
+            "kernel_ms": d["kernel_ms"],
+            "bytes_per_launch": d["bytes_per_launch"],
+        },
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

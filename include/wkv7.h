@@ -1,0 +1,187 @@
+/*
+ * libwkv7 — the RWKV-7 WKV state-slot hot path on MI355X (gfx950).
+ *
+ * C ABI. Every argument is a plain pointer or size; no framework types.
+ *
+ * The operation (page "RWKV-X Architecture", section "WKV-7 Kernel
+ * (Generalized Delta Rule)"): per head, a fixed-size [N, N] recurrent state
+ * is updated each timestep. Reading of that section taken here:
+ *
+ *     S_t = S_{t-1} (diag(w_t) + a_t b_t^T) + v_t k_t^T,      o_t = S_t r_t
+ *
+ * with S[i][j], i = value index (row), j = key index (column): the delta-rule
+ * term reads the state before this step's decay, the readout uses the
+ * updated state. w is used as given (expected in (0, 1]).
+ *
+ * State slots (page "wkvm: state-slot inference for RWKV, GDN and Mamba
+ * hybrids", section "The allocation unit wkvm changes"): each request owns a
+ * fixed-size slot instead of a growing KV chain, and slots support the verbs
+ * create, snapshot, fork, hibernate and resume. A pool is one device
+ * allocation of n_slots slots made up front (page "Virtual Memory for KV
+ * Cache and Model Weights": recurrent states stay resident and are reserved
+ * separately; admission needs a free recurrent-state slot).
+ *
+ * Layouts (all row-major, little-endian):
+ *   slot image      float32 [H][N][N], S[h][i][j] at ((h*N)+i)*N+j.
+ *                   wkv7_slot_bytes() = H*N*N*4. The pool is
+ *                   float32 [n_slots][H][N][N].
+ *   r,w,k,v,a,b     [T_tot][H][N] in the call's dtype (fp32 or bf16);
+ *                   the tokens of sequence s are rows
+ *                   cu_seqlens[s] .. cu_seqlens[s+1]-1.
+ *   o               float32 [T_tot][H][N].
+ *   N must be 64. Device pointers must be 16-byte aligned.
+ *
+ * Errors: every call returns a wkv7_status. On any non-zero status no device
+ * work has been enqueued and the pool is unchanged, except WKV7_ERR_HIP,
+ * which reports a failed HIP runtime call (message from the runtime).
+ * wkv7_last_error() returns the calling thread's last message. There is no
+ * fallback path: an unsupported shape or dtype is an error.
+ *
+ * Threading and ordering: a pool belongs to one host thread; calls on one
+ * pool are not thread-safe. Device work is enqueued on the caller's stream
+ * (a hipStream_t passed as void*, NULL = the null stream) and the library
+ * never waits for it, except in wkv7_pool_destroy. Calls on one pool that
+ * use different streams must be ordered by the caller.
+ */
+#ifndef WKV7_H
+#define WKV7_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t wkv7_status;
+
+enum {
+  WKV7_OK = 0,
+  WKV7_ERR_INVALID_ARG = -1,    /* null pointer, bad size, bad cu_seqlens */
+  WKV7_ERR_OUT_OF_RANGE = -2,   /* a slot id outside [0, n_slots) */
+  WKV7_ERR_DUPLICATE_SLOT = -3, /* a slot named twice where it would race */
+  WKV7_ERR_POOL_FULL = -4,      /* fewer free slots than requested */
+  WKV7_ERR_UNSUPPORTED = -5,    /* N != 64, unknown dtype or option */
+  WKV7_ERR_OOM = -6,            /* device or pinned host allocation failed */
+  WKV7_ERR_HIP = -7             /* a HIP runtime call failed */
+};
+
+/* dtype of r, w, k, v, a, b. The state and o are always float32. */
+enum { WKV7_F32 = 0, WKV7_BF16 = 1 };
+
+/* options for wkv7_pool_set_option */
+enum {
+  /* Sequences with at least this many tokens take the chunked-prefill
+   * kernel; shorter ones (including every decode token) take the
+   * sequential kernel. Default 2^30 (every sequence sequential); must be
+   * >= 1. The choice depends on the
+   * sequence length only, so a slot's result never depends on the rest of
+   * the batch. */
+  WKV7_OPT_PREFILL_MIN_LEN = 1
+};
+
+typedef struct wkv7_pool wkv7_pool;
+
+/* Message for the calling thread's last failed call ("" if none). The
+ * string stays valid until the thread's next libwkv7 call. */
+const char* wkv7_last_error(void);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t wkv7_version(void);
+
+/* create — allocate a pool of n_slots slots of H heads of N x N float32 on
+ * the current device, zero-filled (synchronously), plus pinned staging for
+ * per-call metadata. The pool owns that memory. n_slots >= 1, H >= 1,
+ * N == 64 (else WKV7_ERR_UNSUPPORTED). *out receives the handle. */
+wkv7_status wkv7_pool_create(int32_t n_slots, int32_t H, int32_t N,
+                             wkv7_pool** out);
+
+/* Wait for the pool's enqueued work on every stream it has seen, then free
+ * everything it owns. A NULL pool is a no-op. */
+wkv7_status wkv7_pool_destroy(wkv7_pool* pool);
+
+/* Bytes in one slot image: H*N*N*4 (0 for NULL). */
+size_t wkv7_slot_bytes(const wkv7_pool* pool);
+
+/* Device address of slot 0 (the pool is float32 [n_slots][H][N][N]).
+ * Borrowed; for inspection by tests and benchmarks. */
+void* wkv7_pool_state_ptr(wkv7_pool* pool);
+
+/* Shape of the pool; any out pointer may be NULL. */
+wkv7_status wkv7_pool_shape(const wkv7_pool* pool, int32_t* n_slots,
+                            int32_t* H, int32_t* N);
+
+/* Set a pool option (see WKV7_OPT_*). */
+wkv7_status wkv7_pool_set_option(wkv7_pool* pool, int32_t opt, int64_t val);
+
+/* admission — take n free slot ids from the host free list into ids_out
+ * (host array of n). WKV7_ERR_POOL_FULL if fewer than n are free; then
+ * nothing is taken. Allocation does not clear the slots (see wkv7_reset). */
+wkv7_status wkv7_slot_alloc(wkv7_pool* pool, int32_t n, int32_t* ids_out);
+
+/* Return n allocated ids (host array) to the free list. Every id must be
+ * allocated and appear once, else nothing is freed. */
+wkv7_status wkv7_slot_free(wkv7_pool* pool, const int32_t* ids, int32_t n);
+
+/* forward — run the recurrence for a packed batch of sequences.
+ *
+ * slot_ids[n_seqs] and cu_seqlens[n_seqs+1] are HOST int32 arrays;
+ * cu_seqlens[0] == 0 and it is non-decreasing. Sequence s starts from the
+ * state in slot slot_ids[s], consumes tokens cu_seqlens[s]..cu_seqlens[s+1]-1
+ * of r,w,k,v,a,b (device, [T_tot][H][N], dtype WKV7_F32 or WKV7_BF16), writes
+ * those rows of o (device, float32 [T_tot][H][N]) and leaves its final state
+ * in the slot. A zero-length sequence is a no-op. Slots not named are not
+ * touched. Any slot id in range is accepted, allocated or not.
+ *
+ * Errors: WKV7_ERR_OUT_OF_RANGE (an id outside the pool),
+ * WKV7_ERR_DUPLICATE_SLOT (an id named twice), WKV7_ERR_INVALID_ARG (null
+ * or misaligned pointers with T_tot > 0, bad cu_seqlens, n_seqs < 0),
+ * WKV7_ERR_UNSUPPORTED (dtype). The host arrays may be reused as soon as
+ * the call returns (they are staged); the device arrays must stay alive
+ * until the stream has passed the call. */
+wkv7_status wkv7_forward(wkv7_pool* pool, const int32_t* slot_ids,
+                         const int32_t* cu_seqlens, int32_t n_seqs,
+                         int32_t dtype, const void* r, const void* w,
+                         const void* k, const void* v, const void* a,
+                         const void* b, float* o, void* stream);
+
+/* snapshot — copy slot `slot` (slot_bytes) into caller-owned device memory
+ * dst_device, bit-exact (page "Virtual Memory for KV Cache and Model
+ * Weights": a recoverable linear-state checkpoint). */
+wkv7_status wkv7_snapshot(wkv7_pool* pool, int32_t slot, void* dst_device,
+                          void* stream);
+
+/* fork — pool[dst[i]] <- pool[src[i]] for i < n (host arrays), bit-exact.
+ * dst ids must be distinct and disjoint from src ids
+ * (WKV7_ERR_DUPLICATE_SLOT otherwise); src ids may repeat. */
+wkv7_status wkv7_fork(wkv7_pool* pool, const int32_t* src, const int32_t* dst,
+                      int32_t n, void* stream);
+
+/* reset — zero-fill n slots (host array of distinct ids) (page "RWKV-X
+ * Architecture", section "Dual State": resetting a session zeroes its
+ * recurrent state). */
+wkv7_status wkv7_reset(wkv7_pool* pool, const int32_t* ids, int32_t n,
+                       void* stream);
+
+/* hibernate — copy n slots (host array of ids; repeats allowed) into
+ * caller-owned host memory host_dst as n consecutive slot images,
+ * bit-exact. host_dst must be pinned (page-locked, e.g. hipHostMalloc) and
+ * must stay alive and untouched until the stream has passed the call (page
+ * "Virtual Memory for KV Cache and Model Weights": blocks stay retained
+ * until their transfers finish). bytes >= n*slot_bytes, else
+ * WKV7_ERR_INVALID_ARG. The slots stay valid on the device. */
+wkv7_status wkv7_hibernate(wkv7_pool* pool, const int32_t* ids, int32_t n,
+                           void* host_dst, size_t bytes, void* stream);
+
+/* resume — copy n consecutive slot images from src (pinned host memory or
+ * device memory, e.g. a snapshot) into slots ids[0..n) (distinct),
+ * bit-exact. bytes >= n*slot_bytes, else WKV7_ERR_INVALID_ARG. src must
+ * stay alive until the stream has passed the call. */
+wkv7_status wkv7_resume(wkv7_pool* pool, const int32_t* ids, int32_t n,
+                        const void* src, size_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WKV7_H */

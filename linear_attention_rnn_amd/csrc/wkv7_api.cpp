@@ -1,0 +1,519 @@
+// libwkv7 host library: the C ABI, argument validation, the slot pool and
+// its free list, per-call metadata staging, kernel dispatch and slot verbs.
+//
+// Every entry point validates all of its arguments before it enqueues any
+// device work, so a failed call leaves the pool and the stream untouched.
+
+#include "../../include/wkv7.h"
+#include "internal.h"
+
+#include <algorithm>
+#include <climits>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+using wkv7::WorkItem;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+wkv7_status fail(wkv7_status code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+wkv7_status fail_hip(hipError_t e, const char* what) {
+  return fail(WKV7_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e),
+              static_cast<int>(e));
+}
+
+// Metadata staging: a ring of pinned host buffers and device buffers. An
+// entry is reused only after the event recorded behind its last use has
+// completed, so the host never overwrites data a queued copy still reads,
+// whatever stream the calls used.
+constexpr int kRing = 8;
+
+struct Stage {
+  int32_t* host = nullptr;
+  int32_t* dev = nullptr;
+  size_t cap_ints = 0;
+  size_t n_ints = 0;          // what `dev` holds (a copy of host[0, n_ints))
+  hipStream_t stream = nullptr;
+  hipEvent_t ev = nullptr;
+  bool pending = false;
+};
+
+// Runs a call on the pool's device and restores the caller's device.
+struct DeviceGuard {
+  int prev = -1;
+  bool ok = true;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) { ok = false; return; }
+    if (prev != dev && hipSetDevice(dev) != hipSuccess) ok = false;
+  }
+  ~DeviceGuard() {
+    int cur = -1;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev)
+      (void)hipSetDevice(prev);
+  }
+};
+
+}  // namespace
+
+struct wkv7_pool {
+  int device = 0;
+  int32_t n_slots = 0, H = 0, N = 0;
+  float* state = nullptr;
+  size_t slot_floats = 0;
+  int64_t prefill_min_len = int64_t(1) << 30;
+  std::vector<int32_t> free_ids;     // stack; top = back
+  std::vector<uint8_t> allocated;
+  Stage ring[kRing];
+  int ring_pos = 0;
+};
+
+namespace {
+
+size_t slot_bytes_of(const wkv7_pool* p) { return p->slot_floats * sizeof(float); }
+
+// Copy `n` int32 values to the device through the staging ring. On success
+// *dev_out points at them and *stage_out must be committed after the
+// launches that read them.
+//
+// Steady-state decode passes the same metadata every step. If an entry last
+// used on the same stream already holds identical data on the device, that
+// copy is reused and nothing is uploaded: stream order puts the new launches
+// after the old upload, and the entry cannot be overwritten before its event
+// (re-recorded at commit) has passed.
+wkv7_status stage_upload(wkv7_pool* p, const int32_t* data, size_t n,
+                         hipStream_t stream, const int32_t** dev_out,
+                         Stage** stage_out) {
+  for (int i = 0; i < kRing; ++i) {
+    Stage& c = p->ring[i];
+    if (c.dev && c.n_ints == n && c.stream == stream &&
+        std::memcmp(c.host, data, n * 4) == 0) {
+      *dev_out = c.dev;
+      *stage_out = &c;
+      return WKV7_OK;
+    }
+  }
+  Stage& s = p->ring[p->ring_pos];
+  p->ring_pos = (p->ring_pos + 1) % kRing;
+  hipError_t e;
+  if (s.pending) {
+    e = hipEventSynchronize(s.ev);
+    if (e != hipSuccess) return fail_hip(e, "hipEventSynchronize(staging)");
+    s.pending = false;
+  }
+  if (s.cap_ints < n) {
+    size_t cap = std::max<size_t>(n, 4096);
+    if (s.host) (void)hipHostFree(s.host);
+    if (s.dev) (void)hipFree(s.dev);
+    s.host = nullptr;
+    s.dev = nullptr;
+    s.cap_ints = 0;
+    if (hipHostMalloc(reinterpret_cast<void**>(&s.host), cap * 4) != hipSuccess)
+      return fail(WKV7_ERR_OOM, "pinned staging allocation of %zu bytes failed",
+                  cap * 4);
+    if (hipMalloc(reinterpret_cast<void**>(&s.dev), cap * 4) != hipSuccess) {
+      (void)hipHostFree(s.host);
+      s.host = nullptr;
+      return fail(WKV7_ERR_OOM, "device staging allocation of %zu bytes failed",
+                  cap * 4);
+    }
+    s.cap_ints = cap;
+  }
+  s.n_ints = 0;
+  std::memcpy(s.host, data, n * 4);
+  e = hipMemcpyAsync(s.dev, s.host, n * 4, hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) return fail_hip(e, "hipMemcpyAsync(metadata)");
+  s.n_ints = n;
+  s.stream = stream;
+  // Guard the copy at once, so that a failed launch after it cannot let the
+  // next call overwrite a host buffer still being read.
+  e = hipEventRecord(s.ev, stream);
+  if (e != hipSuccess) return fail_hip(e, "hipEventRecord(staging)");
+  s.pending = true;
+  *dev_out = s.dev;
+  *stage_out = &s;
+  return WKV7_OK;
+}
+
+wkv7_status stage_commit(Stage* s, hipStream_t stream) {
+  hipError_t e = hipEventRecord(s->ev, stream);
+  if (e != hipSuccess) return fail_hip(e, "hipEventRecord(staging)");
+  s->pending = true;
+  return WKV7_OK;
+}
+
+wkv7_status check_pool(const wkv7_pool* p) {
+  if (!p) return fail(WKV7_ERR_INVALID_ARG, "pool is NULL");
+  return WKV7_OK;
+}
+
+// ids[0..n) in range; if `distinct`, no id twice.
+wkv7_status check_ids(const wkv7_pool* p, const int32_t* ids, int32_t n,
+                      bool distinct, const char* what) {
+  if (n < 0) return fail(WKV7_ERR_INVALID_ARG, "%s: n=%d < 0", what, n);
+  if (n > 0 && !ids) return fail(WKV7_ERR_INVALID_ARG, "%s: ids is NULL", what);
+  std::vector<uint8_t> seen;
+  if (distinct) seen.assign(static_cast<size_t>(p->n_slots), 0);
+  for (int32_t i = 0; i < n; ++i) {
+    int32_t id = ids[i];
+    if (id < 0 || id >= p->n_slots)
+      return fail(WKV7_ERR_OUT_OF_RANGE, "%s: slot id %d at %d outside [0, %d)",
+                  what, id, i, p->n_slots);
+    if (distinct) {
+      if (seen[id]) return fail(WKV7_ERR_DUPLICATE_SLOT,
+                                "%s: slot id %d appears twice", what, id);
+      seen[id] = 1;
+    }
+  }
+  return WKV7_OK;
+}
+
+bool aligned16(const void* q) {
+  return (reinterpret_cast<uintptr_t>(q) & 15u) == 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* wkv7_last_error(void) { return g_last_error.c_str(); }
+
+int32_t wkv7_version(void) { return 100; }  // 0.1.0
+
+wkv7_status wkv7_pool_create(int32_t n_slots, int32_t H, int32_t N,
+                             wkv7_pool** out) {
+  g_last_error.clear();
+  if (!out) return fail(WKV7_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (n_slots < 1 || H < 1)
+    return fail(WKV7_ERR_INVALID_ARG, "n_slots=%d and H=%d must be >= 1",
+                n_slots, H);
+  if (N != wkv7::kN)
+    return fail(WKV7_ERR_UNSUPPORTED, "head size N=%d unsupported (only %d)",
+                N, wkv7::kN);
+  const size_t slot_floats = static_cast<size_t>(H) * N * N;
+  if (slot_floats > (size_t(1) << 40) / static_cast<size_t>(n_slots))
+    return fail(WKV7_ERR_INVALID_ARG, "pool of %d x %zu floats is too large",
+                n_slots, slot_floats);
+  wkv7_pool* p = new (std::nothrow) wkv7_pool();
+  if (!p) return fail(WKV7_ERR_OOM, "host allocation failed");
+  hipError_t e = hipGetDevice(&p->device);
+  if (e != hipSuccess) { delete p; return fail_hip(e, "hipGetDevice"); }
+  p->n_slots = n_slots;
+  p->H = H;
+  p->N = N;
+  p->slot_floats = slot_floats;
+  const size_t bytes = slot_floats * sizeof(float) * static_cast<size_t>(n_slots);
+  e = hipMalloc(reinterpret_cast<void**>(&p->state), bytes);
+  if (e != hipSuccess) {
+    delete p;
+    return fail(WKV7_ERR_OOM, "hipMalloc of %zu bytes for the pool failed: %s",
+                bytes, hipGetErrorString(e));
+  }
+  e = hipMemset(p->state, 0, bytes);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  for (int i = 0; e == hipSuccess && i < kRing; ++i)
+    e = hipEventCreateWithFlags(&p->ring[i].ev, hipEventDisableTiming);
+  if (e != hipSuccess) {
+    std::string msg = std::string("pool initialisation: ") + hipGetErrorString(e);
+    wkv7_pool_destroy(p);
+    return fail(WKV7_ERR_HIP, "%s", msg.c_str());
+  }
+  p->allocated.assign(static_cast<size_t>(n_slots), 0);
+  p->free_ids.resize(static_cast<size_t>(n_slots));
+  for (int32_t i = 0; i < n_slots; ++i) p->free_ids[i] = n_slots - 1 - i;
+  *out = p;
+  return WKV7_OK;
+}
+
+wkv7_status wkv7_pool_destroy(wkv7_pool* p) {
+  g_last_error.clear();
+  if (!p) return WKV7_OK;
+  DeviceGuard guard(p->device);
+  hipError_t e = hipDeviceSynchronize();
+  for (int i = 0; i < kRing; ++i) {
+    Stage& s = p->ring[i];
+    if (s.host) (void)hipHostFree(s.host);
+    if (s.dev) (void)hipFree(s.dev);
+    if (s.ev) (void)hipEventDestroy(s.ev);
+  }
+  if (p->state) (void)hipFree(p->state);
+  delete p;
+  if (e != hipSuccess) return fail_hip(e, "hipDeviceSynchronize(destroy)");
+  return WKV7_OK;
+}
+
+size_t wkv7_slot_bytes(const wkv7_pool* p) { return p ? slot_bytes_of(p) : 0; }
+
+void* wkv7_pool_state_ptr(wkv7_pool* p) { return p ? p->state : nullptr; }
+
+wkv7_status wkv7_pool_shape(const wkv7_pool* p, int32_t* n_slots, int32_t* H,
+                            int32_t* N) {
+  g_last_error.clear();
+  if (wkv7_status st = check_pool(p)) return st;
+  if (n_slots) *n_slots = p->n_slots;
+  if (H) *H = p->H;
+  if (N) *N = p->N;
+  return WKV7_OK;
+}
+
+wkv7_status wkv7_pool_set_option(wkv7_pool* p, int32_t opt, int64_t val) {
+  g_last_error.clear();
+  if (wkv7_status st = check_pool(p)) return st;
+  if (opt == WKV7_OPT_PREFILL_MIN_LEN) {
+    if (val < 1) return fail(WKV7_ERR_INVALID_ARG,
+                             "PREFILL_MIN_LEN=%lld must be >= 1",
+                             static_cast<long long>(val));
+    p->prefill_min_len = val;
+    return WKV7_OK;
+  }
+  return fail(WKV7_ERR_UNSUPPORTED, "unknown option %d", opt);
+}
+
+wkv7_status wkv7_slot_alloc(wkv7_pool* p, int32_t n, int32_t* ids_out) {
+  g_last_error.clear();
+  if (wkv7_status st = check_pool(p)) return st;
+  if (n < 0) return fail(WKV7_ERR_INVALID_ARG, "n=%d < 0", n);
+  if (n > 0 && !ids_out) return fail(WKV7_ERR_INVALID_ARG, "ids_out is NULL");
+  if (static_cast<size_t>(n) > p->free_ids.size())
+    return fail(WKV7_ERR_POOL_FULL, "%d slots requested, %zu free", n,
+                p->free_ids.size());
+  for (int32_t i = 0; i < n; ++i) {
+    int32_t id = p->free_ids.back();
+    p->free_ids.pop_back();
+    p->allocated[id] = 1;
+    ids_out[i] = id;
+  }
+  return WKV7_OK;
+}
+
+wkv7_status wkv7_slot_free(wkv7_pool* p, const int32_t* ids, int32_t n) {
+  g_last_error.clear();
+  if (wkv7_status st = check_pool(p)) return st;
+  if (wkv7_status st = check_ids(p, ids, n, true, "slot_free")) return st;
+  for (int32_t i = 0; i < n; ++i)
+    if (!p->allocated[ids[i]])
+      return fail(WKV7_ERR_INVALID_ARG, "slot_free: slot %d is not allocated",
+                  ids[i]);
+  for (int32_t i = 0; i < n; ++i) {
+    p->allocated[ids[i]] = 0;
+    p->free_ids.push_back(ids[i]);
+  }
+  return WKV7_OK;
+}
+
+wkv7_status wkv7_forward(wkv7_pool* p, const int32_t* slot_ids,
+                         const int32_t* cu_seqlens, int32_t n_seqs,
+                         int32_t dtype, const void* r, const void* w,
+                         const void* k, const void* v, const void* a,
+                         const void* b, float* o, void* stream) {
+  g_last_error.clear();
+  if (wkv7_status st = check_pool(p)) return st;
+  if (n_seqs < 0) return fail(WKV7_ERR_INVALID_ARG, "n_seqs=%d < 0", n_seqs);
+  if (dtype != WKV7_F32 && dtype != WKV7_BF16)
+    return fail(WKV7_ERR_UNSUPPORTED, "dtype %d unsupported", dtype);
+  if (n_seqs == 0) return WKV7_OK;
+  if (!cu_seqlens) return fail(WKV7_ERR_INVALID_ARG, "cu_seqlens is NULL");
+  if (cu_seqlens[0] != 0)
+    return fail(WKV7_ERR_INVALID_ARG, "cu_seqlens[0]=%d, must be 0",
+                cu_seqlens[0]);
+  for (int32_t s = 0; s < n_seqs; ++s)
+    if (cu_seqlens[s + 1] < cu_seqlens[s])
+      return fail(WKV7_ERR_INVALID_ARG,
+                  "cu_seqlens decreases at %d (%d -> %d)", s, cu_seqlens[s],
+                  cu_seqlens[s + 1]);
+  if (wkv7_status st = check_ids(p, slot_ids, n_seqs, true, "forward"))
+    return st;
+  const int64_t T_tot = cu_seqlens[n_seqs];
+  if (T_tot == 0) return WKV7_OK;
+  const void* ptrs[7] = {r, w, k, v, a, b, o};
+  const char* names[7] = {"r", "w", "k", "v", "a", "b", "o"};
+  for (int i = 0; i < 7; ++i) {
+    if (!ptrs[i]) return fail(WKV7_ERR_INVALID_ARG, "%s is NULL", names[i]);
+    if (!aligned16(ptrs[i]))
+      return fail(WKV7_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[i]);
+  }
+
+  // Split by length: short sequences take the sequential kernel, long ones
+  // the chunked kernel, longest first.
+  std::vector<WorkItem> seq_items, chunk_items;
+  for (int32_t s = 0; s < n_seqs; ++s) {
+    const int32_t len = cu_seqlens[s + 1] - cu_seqlens[s];
+    if (len == 0) continue;
+    WorkItem it{slot_ids[s], cu_seqlens[s], len, 0};
+    if (len >= p->prefill_min_len) chunk_items.push_back(it);
+    else seq_items.push_back(it);
+  }
+  std::stable_sort(chunk_items.begin(), chunk_items.end(),
+                   [](const WorkItem& x, const WorkItem& y) {
+                     return x.len > y.len;
+                   });
+  std::vector<WorkItem> all(seq_items);
+  all.insert(all.end(), chunk_items.begin(), chunk_items.end());
+
+  DeviceGuard guard(p->device);
+  if (!guard.ok) return fail(WKV7_ERR_HIP, "cannot select the pool's device");
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const int32_t* dev = nullptr;
+  Stage* stage = nullptr;
+  if (wkv7_status st = stage_upload(p, reinterpret_cast<const int32_t*>(all.data()),
+                                    all.size() * 4, hs, &dev, &stage))
+    return st;
+  wkv7::SeqArgs args{p->state, nullptr, 0, p->H, dtype, r, w, k, v, a, b, o};
+  hipError_t e = hipSuccess;
+  if (!seq_items.empty()) {
+    args.items = reinterpret_cast<const WorkItem*>(dev);
+    args.n_items = static_cast<int32_t>(seq_items.size());
+    e = wkv7::launch_seq(args, hs);
+    if (e != hipSuccess) return fail_hip(e, "sequential kernel launch");
+  }
+  if (!chunk_items.empty()) {
+    args.items = reinterpret_cast<const WorkItem*>(dev) + seq_items.size();
+    args.n_items = static_cast<int32_t>(chunk_items.size());
+    e = wkv7::launch_chunked(args, chunk_items.front().len, hs);
+    if (e != hipSuccess) return fail_hip(e, "chunked kernel launch");
+  }
+  return stage_commit(stage, hs);
+}
+
+wkv7_status wkv7_snapshot(wkv7_pool* p, int32_t slot, void* dst_device,
+                          void* stream) {
+  g_last_error.clear();
+  if (wkv7_status st = check_pool(p)) return st;
+  if (wkv7_status st = check_ids(p, &slot, 1, false, "snapshot")) return st;
+  if (!dst_device) return fail(WKV7_ERR_INVALID_ARG, "dst_device is NULL");
+  DeviceGuard guard(p->device);
+  if (!guard.ok) return fail(WKV7_ERR_HIP, "cannot select the pool's device");
+  hipError_t e = hipMemcpyAsync(dst_device, p->state + slot * p->slot_floats,
+                                slot_bytes_of(p), hipMemcpyDeviceToDevice,
+                                static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail_hip(e, "hipMemcpyAsync(snapshot)");
+  return WKV7_OK;
+}
+
+wkv7_status wkv7_fork(wkv7_pool* p, const int32_t* src, const int32_t* dst,
+                      int32_t n, void* stream) {
+  g_last_error.clear();
+  if (wkv7_status st = check_pool(p)) return st;
+  if (wkv7_status st = check_ids(p, src, n, false, "fork src")) return st;
+  if (wkv7_status st = check_ids(p, dst, n, true, "fork dst")) return st;
+  if (n == 0) return WKV7_OK;
+  std::vector<uint8_t> is_src(static_cast<size_t>(p->n_slots), 0);
+  for (int32_t i = 0; i < n; ++i) is_src[src[i]] = 1;
+  for (int32_t i = 0; i < n; ++i)
+    if (is_src[dst[i]])
+      return fail(WKV7_ERR_DUPLICATE_SLOT,
+                  "fork: slot %d is both a source and a destination", dst[i]);
+  std::vector<int32_t> pairs(2 * static_cast<size_t>(n));
+  for (int32_t i = 0; i < n; ++i) {
+    pairs[2 * i] = src[i];
+    pairs[2 * i + 1] = dst[i];
+  }
+  DeviceGuard guard(p->device);
+  if (!guard.ok) return fail(WKV7_ERR_HIP, "cannot select the pool's device");
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const int32_t* dev = nullptr;
+  Stage* stage = nullptr;
+  if (wkv7_status st = stage_upload(p, pairs.data(), pairs.size(), hs, &dev,
+                                    &stage))
+    return st;
+  hipError_t e = wkv7::launch_copy_slots(p->state, p->slot_floats, dev, n, hs);
+  if (e != hipSuccess) return fail_hip(e, "slot copy launch");
+  return stage_commit(stage, hs);
+}
+
+wkv7_status wkv7_reset(wkv7_pool* p, const int32_t* ids, int32_t n,
+                       void* stream) {
+  g_last_error.clear();
+  if (wkv7_status st = check_pool(p)) return st;
+  if (wkv7_status st = check_ids(p, ids, n, true, "reset")) return st;
+  if (n == 0) return WKV7_OK;
+  DeviceGuard guard(p->device);
+  if (!guard.ok) return fail(WKV7_ERR_HIP, "cannot select the pool's device");
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const int32_t* dev = nullptr;
+  Stage* stage = nullptr;
+  if (wkv7_status st = stage_upload(p, ids, static_cast<size_t>(n), hs, &dev,
+                                    &stage))
+    return st;
+  hipError_t e = wkv7::launch_zero_slots(p->state, p->slot_floats, dev, n, hs);
+  if (e != hipSuccess) return fail_hip(e, "slot zero-fill launch");
+  return stage_commit(stage, hs);
+}
+
+namespace {
+
+// Copies between n slots and n consecutive images in `buf`, one copy per
+// run of consecutive slot ids.
+wkv7_status copy_runs(wkv7_pool* p, const int32_t* ids, int32_t n, char* buf,
+                      bool to_pool, hipStream_t hs) {
+  const size_t sb = slot_bytes_of(p);
+  int32_t i = 0;
+  while (i < n) {
+    int32_t j = i + 1;
+    while (j < n && ids[j] == ids[j - 1] + 1) ++j;
+    char* slot_ptr = reinterpret_cast<char*>(p->state) + ids[i] * sb;
+    char* img = buf + static_cast<size_t>(i) * sb;
+    const size_t bytes = static_cast<size_t>(j - i) * sb;
+    hipError_t e = to_pool
+        ? hipMemcpyAsync(slot_ptr, img, bytes, hipMemcpyDefault, hs)
+        : hipMemcpyAsync(img, slot_ptr, bytes, hipMemcpyDefault, hs);
+    if (e != hipSuccess)
+      return fail_hip(e, to_pool ? "hipMemcpyAsync(resume)"
+                                 : "hipMemcpyAsync(hibernate)");
+    i = j;
+  }
+  return WKV7_OK;
+}
+
+}  // namespace
+
+wkv7_status wkv7_hibernate(wkv7_pool* p, const int32_t* ids, int32_t n,
+                           void* host_dst, size_t bytes, void* stream) {
+  g_last_error.clear();
+  if (wkv7_status st = check_pool(p)) return st;
+  if (wkv7_status st = check_ids(p, ids, n, false, "hibernate")) return st;
+  if (n == 0) return WKV7_OK;
+  if (!host_dst) return fail(WKV7_ERR_INVALID_ARG, "host_dst is NULL");
+  if (bytes < static_cast<size_t>(n) * slot_bytes_of(p))
+    return fail(WKV7_ERR_INVALID_ARG,
+                "hibernate: %zu bytes given, %zu needed for %d slots", bytes,
+                static_cast<size_t>(n) * slot_bytes_of(p), n);
+  DeviceGuard guard(p->device);
+  if (!guard.ok) return fail(WKV7_ERR_HIP, "cannot select the pool's device");
+  return copy_runs(p, ids, n, static_cast<char*>(host_dst), false,
+                   static_cast<hipStream_t>(stream));
+}
+
+wkv7_status wkv7_resume(wkv7_pool* p, const int32_t* ids, int32_t n,
+                        const void* src, size_t bytes, void* stream) {
+  g_last_error.clear();
+  if (wkv7_status st = check_pool(p)) return st;
+  if (wkv7_status st = check_ids(p, ids, n, true, "resume")) return st;
+  if (n == 0) return WKV7_OK;
+  if (!src) return fail(WKV7_ERR_INVALID_ARG, "src is NULL");
+  if (bytes < static_cast<size_t>(n) * slot_bytes_of(p))
+    return fail(WKV7_ERR_INVALID_ARG,
+                "resume: %zu bytes given, %zu needed for %d slots", bytes,
+                static_cast<size_t>(n) * slot_bytes_of(p), n);
+  DeviceGuard guard(p->device);
+  if (!guard.ok) return fail(WKV7_ERR_HIP, "cannot select the pool's device");
+  return copy_runs(p, ids, n, const_cast<char*>(static_cast<const char*>(src)),
+                   true, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,262 @@
+"""Python binding of libwkv7 (ctypes): argument marshalling only.
+
+Each function has the name of the C entry point it calls and the same
+argument order. Device buffers are passed as torch tensors (their
+data_ptr() is handed over), host int32 arrays as numpy arrays or sequences,
+streams as torch streams (or None for the current stream). A non-zero status
+raises `Wkv7Error` carrying the library's message. Every computation happens
+in the library's HIP kernels; nothing here computes.
+
+The library must have been built (`python -m linear_attention_rnn_amd.build`);
+importing this module without it raises ImportError.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libwkv7.so")
+
+WKV7_OK = 0
+WKV7_ERR_INVALID_ARG = -1
+WKV7_ERR_OUT_OF_RANGE = -2
+WKV7_ERR_DUPLICATE_SLOT = -3
+WKV7_ERR_POOL_FULL = -4
+WKV7_ERR_UNSUPPORTED = -5
+WKV7_ERR_OOM = -6
+WKV7_ERR_HIP = -7
+
+WKV7_F32 = 0
+WKV7_BF16 = 1
+
+WKV7_OPT_PREFILL_MIN_LEN = 1
+
+# Every symbol include/wkv7.h declares.
+EXPORTS = (
+    "wkv7_last_error", "wkv7_version", "wkv7_pool_create", "wkv7_pool_destroy",
+    "wkv7_slot_bytes", "wkv7_pool_state_ptr", "wkv7_pool_shape",
+    "wkv7_pool_set_option", "wkv7_slot_alloc", "wkv7_slot_free",
+    "wkv7_forward", "wkv7_snapshot", "wkv7_fork", "wkv7_reset",
+    "wkv7_hibernate", "wkv7_resume",
+)
+
+
+class Wkv7Error(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"libwkv7 status {status}: {message}")
+        self.status = status
+        self.message = message
+
+
+def _load() -> ctypes.CDLL:
+    # One HIP runtime per process: torch ships its own libamdhip64 (same
+    # soname as the system one). Loading torch first makes the library bind
+    # to that already-loaded runtime instead of pulling in a second copy.
+    import torch  # noqa: F401
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with "
+            "`python -m linear_attention_rnn_amd.build` (there is no fallback)")
+    return ctypes.CDLL(LIB_PATH)
+
+
+lib = _load()
+
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+_sz = ctypes.c_size_t
+_vp = ctypes.c_void_p
+_pi32 = ctypes.POINTER(ctypes.c_int32)
+
+lib.wkv7_last_error.restype = ctypes.c_char_p
+lib.wkv7_last_error.argtypes = []
+lib.wkv7_version.restype = _i32
+lib.wkv7_version.argtypes = []
+lib.wkv7_pool_create.restype = _i32
+lib.wkv7_pool_create.argtypes = [_i32, _i32, _i32, ctypes.POINTER(_vp)]
+lib.wkv7_pool_destroy.restype = _i32
+lib.wkv7_pool_destroy.argtypes = [_vp]
+lib.wkv7_slot_bytes.restype = _sz
+lib.wkv7_slot_bytes.argtypes = [_vp]
+lib.wkv7_pool_state_ptr.restype = _vp
+lib.wkv7_pool_state_ptr.argtypes = [_vp]
+lib.wkv7_pool_shape.restype = _i32
+lib.wkv7_pool_shape.argtypes = [_vp, _pi32, _pi32, _pi32]
+lib.wkv7_pool_set_option.restype = _i32
+lib.wkv7_pool_set_option.argtypes = [_vp, _i32, _i64]
+lib.wkv7_slot_alloc.restype = _i32
+lib.wkv7_slot_alloc.argtypes = [_vp, _i32, _pi32]
+lib.wkv7_slot_free.restype = _i32
+lib.wkv7_slot_free.argtypes = [_vp, _pi32, _i32]
+lib.wkv7_forward.restype = _i32
+lib.wkv7_forward.argtypes = [_vp, _pi32, _pi32, _i32, _i32, _vp, _vp, _vp,
+                             _vp, _vp, _vp, _vp, _vp]
+lib.wkv7_snapshot.restype = _i32
+lib.wkv7_snapshot.argtypes = [_vp, _i32, _vp, _vp]
+lib.wkv7_fork.restype = _i32
+lib.wkv7_fork.argtypes = [_vp, _pi32, _pi32, _i32, _vp]
+lib.wkv7_reset.restype = _i32
+lib.wkv7_reset.argtypes = [_vp, _pi32, _i32, _vp]
+lib.wkv7_hibernate.restype = _i32
+lib.wkv7_hibernate.argtypes = [_vp, _pi32, _i32, _vp, _sz, _vp]
+lib.wkv7_resume.restype = _i32
+lib.wkv7_resume.argtypes = [_vp, _pi32, _i32, _vp, _sz, _vp]
+
+
+def _check(status: int) -> None:
+    if status != WKV7_OK:
+        raise Wkv7Error(status, lib.wkv7_last_error().decode(errors="replace"))
+
+
+def _ids(x) -> np.ndarray:
+    """Host int32 array (contiguous) from a sequence or numpy array."""
+    return np.ascontiguousarray(np.asarray(x, dtype=np.int32).reshape(-1))
+
+
+def _iptr(a: np.ndarray):
+    return a.ctypes.data_as(_pi32) if a.size else None
+
+
+def _dptr(t) -> Optional[int]:
+    """Address of a tensor's storage (device or pinned host), or None."""
+    if t is None:
+        return None
+    return int(t.data_ptr()) if t.numel() else None
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return int(torch.cuda.current_stream().cuda_stream) or None
+    if isinstance(stream, int):
+        return stream or None
+    return int(stream.cuda_stream) or None
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return WKV7_F32
+    if t.dtype == torch.bfloat16:
+        return WKV7_BF16
+    return -1  # the library reports WKV7_ERR_UNSUPPORTED
+
+
+def wkv7_version() -> int:
+    return int(lib.wkv7_version())
+
+
+def wkv7_last_error() -> str:
+    return lib.wkv7_last_error().decode(errors="replace")
+
+
+def wkv7_pool_create(n_slots: int, H: int, N: int) -> int:
+    handle = _vp()
+    _check(lib.wkv7_pool_create(n_slots, H, N, ctypes.byref(handle)))
+    return int(handle.value)
+
+
+def wkv7_pool_destroy(pool: int) -> None:
+    _check(lib.wkv7_pool_destroy(pool))
+
+
+def wkv7_slot_bytes(pool: int) -> int:
+    return int(lib.wkv7_slot_bytes(pool))
+
+
+def wkv7_pool_state_ptr(pool: int) -> int:
+    return int(lib.wkv7_pool_state_ptr(pool) or 0)
+
+
+def wkv7_pool_shape(pool: int):
+    n, h, d = _i32(), _i32(), _i32()
+    _check(lib.wkv7_pool_shape(pool, ctypes.byref(n), ctypes.byref(h),
+                               ctypes.byref(d)))
+    return n.value, h.value, d.value
+
+
+def wkv7_pool_set_option(pool: int, opt: int, val: int) -> None:
+    _check(lib.wkv7_pool_set_option(pool, opt, val))
+
+
+def wkv7_slot_alloc(pool: int, n: int) -> np.ndarray:
+    out = np.zeros(max(n, 0), dtype=np.int32)
+    _check(lib.wkv7_slot_alloc(pool, n, _iptr(out)))
+    return out
+
+
+def wkv7_slot_free(pool: int, ids: Sequence[int]) -> None:
+    a = _ids(ids)
+    _check(lib.wkv7_slot_free(pool, _iptr(a), a.size))
+
+
+def wkv7_forward(pool: int, slot_ids, cu_seqlens, r, w, k, v, a, b, o,
+                 stream=None, dtype: Optional[int] = None) -> None:
+    """o[T_tot, H, N] fp32 <- recurrence over the packed batch (in place)."""
+    ids = _ids(slot_ids)
+    cu = _ids(cu_seqlens)
+    if cu.size != ids.size + 1:
+        raise ValueError("cu_seqlens must have len(slot_ids) + 1 entries")
+    code = _dtype_code(r) if dtype is None else dtype
+    _check(lib.wkv7_forward(pool, _iptr(ids), _iptr(cu), ids.size, code,
+                            _dptr(r), _dptr(w), _dptr(k), _dptr(v), _dptr(a),
+                            _dptr(b), _dptr(o), _stream(stream)))
+
+
+def wkv7_snapshot(pool: int, slot: int, dst, stream=None) -> None:
+    _check(lib.wkv7_snapshot(pool, slot, _dptr(dst), _stream(stream)))
+
+
+def wkv7_fork(pool: int, src, dst, stream=None) -> None:
+    s, d = _ids(src), _ids(dst)
+    if s.size != d.size:
+        raise ValueError("fork: src and dst differ in length")
+    _check(lib.wkv7_fork(pool, _iptr(s), _iptr(d), s.size, _stream(stream)))
+
+
+def wkv7_reset(pool: int, ids, stream=None) -> None:
+    a = _ids(ids)
+    _check(lib.wkv7_reset(pool, _iptr(a), a.size, _stream(stream)))
+
+
+def wkv7_hibernate(pool: int, ids, host_dst, stream=None) -> None:
+    """host_dst: pinned CPU tensor of at least len(ids) * slot_bytes bytes."""
+    a = _ids(ids)
+    nbytes = host_dst.numel() * host_dst.element_size()
+    _check(lib.wkv7_hibernate(pool, _iptr(a), a.size, _dptr(host_dst), nbytes,
+                              _stream(stream)))
+
+
+def wkv7_resume(pool: int, ids, src, stream=None) -> None:
+    """src: pinned CPU tensor or device tensor of slot images."""
+    a = _ids(ids)
+    nbytes = src.numel() * src.element_size()
+    _check(lib.wkv7_resume(pool, _iptr(a), a.size, _dptr(src), nbytes,
+                           _stream(stream)))
+
+
+def pool_state(pool: int):
+    """The pool's state as a torch float32 tensor view [n_slots, H, N, N].
+
+    A zero-copy view of the library-owned device buffer (valid until the
+    pool is destroyed); for inspection and set-up by tests and benchmarks.
+    """
+    import torch
+    n, h, d = wkv7_pool_shape(pool)
+    ptr = wkv7_pool_state_ptr(pool)
+    return _device_view(ptr, (n, h, d, d), torch.float32)
+
+
+def _device_view(ptr: int, shape, dtype):
+    import torch
+
+    class _Iface:
+        __cuda_array_interface__ = {
+            "shape": tuple(shape), "typestr": "<f4", "data": (ptr, False),
+            "version": 2, "strides": None,
+        }
+    return torch.as_tensor(_Iface(), device="cuda")

@@ -1,0 +1,79 @@
+"""libwkv7 on the CPU: it loads, exports every declared symbol, and rejects
+bad arguments before touching a device (no compute calls without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from linear_attention_rnn_amd import wkv7 as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    with open(os.path.join(ROOT, "include", "wkv7.h")) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(wkv7_[a-z_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_symbols()
+    assert len(names) >= 16
+    lib = ctypes.CDLL(W.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/wkv7.h but not exported"
+    assert sorted(W.EXPORTS) == names
+
+
+def test_version():
+    assert W.wkv7_version() == 100
+
+
+@pytest.mark.parametrize("args,code", [
+    ((4, 2, 32), W.WKV7_ERR_UNSUPPORTED),
+    ((4, 2, 128), W.WKV7_ERR_UNSUPPORTED),
+    ((0, 2, 64), W.WKV7_ERR_INVALID_ARG),
+    ((4, 0, 64), W.WKV7_ERR_INVALID_ARG),
+    ((-1, 2, 64), W.WKV7_ERR_INVALID_ARG),
+])
+def test_pool_create_rejects_before_device(args, code):
+    with pytest.raises(W.Wkv7Error) as e:
+        W.wkv7_pool_create(*args)
+    assert e.value.status == code
+    assert e.value.message
+
+
+def test_null_pool_everywhere():
+    L = W.lib
+    assert L.wkv7_pool_create(4, 2, 64, None) == W.WKV7_ERR_INVALID_ARG
+    assert L.wkv7_forward(None, None, None, 0, 0, *([None] * 8)) == \
+        W.WKV7_ERR_INVALID_ARG
+    assert b"NULL" in L.wkv7_last_error()
+    assert L.wkv7_snapshot(None, 0, None, None) == W.WKV7_ERR_INVALID_ARG
+    assert L.wkv7_fork(None, None, None, 0, None) == W.WKV7_ERR_INVALID_ARG
+    assert L.wkv7_reset(None, None, 0, None) == W.WKV7_ERR_INVALID_ARG
+    assert L.wkv7_hibernate(None, None, 0, None, 0, None) == W.WKV7_ERR_INVALID_ARG
+    assert L.wkv7_resume(None, None, 0, None, 0, None) == W.WKV7_ERR_INVALID_ARG
+    assert L.wkv7_slot_alloc(None, 1, None) == W.WKV7_ERR_INVALID_ARG
+    assert L.wkv7_slot_free(None, None, 0) == W.WKV7_ERR_INVALID_ARG
+    assert L.wkv7_pool_set_option(None, 1, 64) == W.WKV7_ERR_INVALID_ARG
+    assert L.wkv7_pool_shape(None, None, None, None) == W.WKV7_ERR_INVALID_ARG
+    assert L.wkv7_slot_bytes(None) == 0
+    assert L.wkv7_pool_state_ptr(None) is None
+    assert L.wkv7_pool_destroy(None) == W.WKV7_OK
+
+
+def test_last_error_is_per_thread():
+    import threading
+    W.lib.wkv7_forward(None, None, None, 0, 0, *([None] * 8))
+    seen = {}
+
+    def other():
+        seen["msg"] = W.wkv7_last_error()
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen["msg"] == ""
+    assert "NULL" in W.wkv7_last_error()

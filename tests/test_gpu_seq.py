@@ -1,0 +1,190 @@
+"""Parity of the sequential kernel (decode and short sequences) with the
+float64 oracle, on the GPU through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import wkv7_inputs as G
+from linear_attention_rnn_amd import wkv7 as W
+from oracle import wkv7_forward as oracle_forward, wkv7_decode_batch
+from tests.gpu_util import (DEV, say, set_states, get_states, run_forward,
+                            rel_err, tol_for)
+
+pytestmark = pytest.mark.gpu
+
+ALL_SEQUENTIAL = 1 << 30
+
+
+def _pool(n, H, seq_only=False):
+    p = W.wkv7_pool_create(n, H, 64)
+    if seq_only:
+        W.wkv7_pool_set_option(p, W.WKV7_OPT_PREFILL_MIN_LEN, ALL_SEQUENTIAL)
+    return p
+
+
+def _oracle(batch, states):
+    return oracle_forward(states, batch.slot_ids, batch.cu_seqlens,
+                          batch.inputs64(), batch.H, batch.N)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_small_config_sequential(dtype):
+    """H=2, one sequence of T=64, zero state, every token sequentially."""
+    say(f"small config, sequential kernel, dtype={dtype}")
+    rng = np.random.default_rng(0)
+    b = G.make_batch(rng, [0], [64], 2, 64, dtype)
+    pool = _pool(1, 2, seq_only=True)
+    try:
+        o = run_forward(pool, b)
+        S = get_states(pool, [0])
+    finally:
+        W.wkv7_pool_destroy(pool)
+    o_ref, S_ref = _oracle(b, {})
+    e_o, e_s = rel_err(o, o_ref), rel_err(S[0], S_ref[0])
+    say(f"  o err {e_o:.3e}  S err {e_s:.3e}")
+    assert e_o < 1e-5 and e_s < 1e-5   # fp32 sequential: rounding only
+    assert e_o < tol_for(dtype)
+
+
+def test_decode_full_size_steps():
+    """Decode: 256 random ids of a 1024-slot pool, H=32, bf16; 3 steps.
+
+    Also checks that the 768 inactive slots stay bit-identical.
+    """
+    wl = G.cfg_decode(seed=1)
+    ids = wl.batch.slot_ids
+    say(f"decode {wl.name}: ids={len(ids)} H={wl.H}")
+    pool = _pool(wl.n_slots, wl.H)
+    try:
+        # inactive slots hold a recognisable random pattern
+        rng = np.random.default_rng(99)
+        others = np.setdiff1d(np.arange(wl.n_slots), ids).astype(np.int32)
+        other_states = G.draw_states(rng, len(others), wl.H, wl.N, std=1.0)
+        set_states(pool, others, other_states)
+        set_states(pool, ids, wl.init_states)
+        S = G.as_f64(wl.init_states)
+        for step in range(3):
+            b = G.decode_step_inputs(1, step, ids, wl.H, wl.N)
+            o = run_forward(pool, b)
+            o_ref, S = wkv7_decode_batch(S, b.inputs64())
+            got_S = get_states(pool, ids)
+            e_o, e_s = rel_err(o, o_ref), rel_err(got_S, S)
+            say(f"  step {step}: o err {e_o:.3e}  S err {e_s:.3e}")
+            assert e_o < 1e-5 and e_s < 1e-5
+            S = G.as_f64(got_S)   # continue from the device state
+        after = get_states(pool, others)
+        assert torch.equal(after.view(torch.int32),
+                           other_states.view(torch.int32)), \
+            "inactive slots changed"
+    finally:
+        W.wkv7_pool_destroy(pool)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_ragged_sequential(dtype):
+    """Ragged lengths incl. 0, 1, a tile edge and a ragged tail; mixed
+    initial states; every sequence on the sequential kernel."""
+    lens = [1, 0, 5, 63, 64, 65, 130, 2]
+    H = 3
+    rng = np.random.default_rng(7)
+    ids = rng.permutation(20)[:len(lens)].astype(np.int32)
+    say(f"ragged sequential dtype={dtype} lens={lens} ids={ids.tolist()}")
+    b = G.make_batch(rng, ids, lens, H, 64, dtype)
+    init = G.draw_states(rng, len(ids), H, 64)
+    pool = _pool(20, H, seq_only=True)
+    try:
+        set_states(pool, ids, init)
+        o = run_forward(pool, b)
+        S = get_states(pool, ids)
+    finally:
+        W.wkv7_pool_destroy(pool)
+    states = {int(i): G.as_f64(init[n]) for n, i in enumerate(ids)}
+    o_ref, S_ref = _oracle(b, states)
+    e_o = rel_err(o, o_ref)
+    e_s = max(rel_err(S[n], S_ref[int(i)]) for n, i in enumerate(ids))
+    say(f"  o err {e_o:.3e}  S err {e_s:.3e}")
+    assert e_o < 1e-5 and e_s < 1e-5
+
+
+def test_same_call_twice_and_permuted_order_bitwise():
+    """A slot's result depends only on its own state and inputs."""
+    H = 4
+    rng = np.random.default_rng(8)
+    lens = [1, 3, 1, 7, 1]
+    ids = np.array([5, 2, 9, 0, 7], np.int32)
+    b = G.make_batch(rng, ids, lens, H, 64, "bf16")
+    init = G.draw_states(rng, len(ids), H, 64)
+    outs = []
+    for order in (None, None, [3, 0, 4, 1, 2]):
+        pool = _pool(10, H)
+        try:
+            set_states(pool, ids, init)
+            if order is None:
+                o = run_forward(pool, b)
+                S = get_states(pool, ids)
+            else:
+                lens_p = [lens[i] for i in order]
+                cu = np.concatenate([[0], np.cumsum(lens_p)]).astype(np.int32)
+                rows = np.concatenate([np.arange(b.cu_seqlens[i],
+                                                 b.cu_seqlens[i + 1])
+                                       for i in order]).astype(np.int64)
+                bp = G.Batch(b.dtype, H, 64, ids[order], cu,
+                             {n: b.inputs[n][rows] for n in G.NAMES})
+                op = run_forward(pool, bp)
+                o = torch.empty_like(op)
+                o[torch.from_numpy(rows)] = op
+                S = get_states(pool, ids)
+        finally:
+            W.wkv7_pool_destroy(pool)
+        outs.append((o, S))
+    for o, S in outs[1:]:
+        assert torch.equal(o.view(torch.int32), outs[0][0].view(torch.int32))
+        assert torch.equal(S.view(torch.int32), outs[0][1].view(torch.int32))
+
+
+def test_forward_errors_leave_pool_untouched():
+    H = 2
+    rng = np.random.default_rng(9)
+    pool = _pool(4, H)
+    try:
+        init = G.draw_states(rng, 4, H, 64)
+        ids = np.arange(4, dtype=np.int32)
+        set_states(pool, ids, init)
+        b = G.make_batch(rng, [0, 1], [1, 1], H, 64, "bf16")
+        x = {n: b.inputs[n].to(DEV) for n in G.NAMES}
+        o = torch.zeros((2, H, 64), dtype=torch.float32, device=DEV)
+        cases = [
+            ([0, 4], [0, 1, 2], W.WKV7_ERR_OUT_OF_RANGE),
+            ([1, 1], [0, 1, 2], W.WKV7_ERR_DUPLICATE_SLOT),
+            ([0, 1], [0, 2, 1], W.WKV7_ERR_INVALID_ARG),
+            ([0, 1], [1, 1, 2], W.WKV7_ERR_INVALID_ARG),
+        ]
+        for sids, cu, code in cases:
+            with pytest.raises(W.Wkv7Error) as e:
+                W.wkv7_forward(pool, sids, cu, x["r"], x["w"], x["k"], x["v"],
+                               x["a"], x["b"], o)
+            assert e.value.status == code, e.value.message
+        with pytest.raises(W.Wkv7Error) as e:
+            W.wkv7_forward(pool, [0, 1], [0, 1, 2], x["r"].half(), x["w"],
+                           x["k"], x["v"], x["a"], x["b"], o)
+        assert e.value.status == W.WKV7_ERR_UNSUPPORTED
+        # misaligned device pointer
+        rr = torch.zeros(2 * H * 64 + 1, dtype=torch.bfloat16, device=DEV)[1:]
+        with pytest.raises(W.Wkv7Error) as e:
+            W.wkv7_forward(pool, [0, 1], [0, 1, 2], rr, x["w"], x["k"],
+                           x["v"], x["a"], x["b"], o, dtype=W.WKV7_BF16)
+        assert e.value.status == W.WKV7_ERR_INVALID_ARG
+        torch.cuda.synchronize()
+        assert torch.equal(o, torch.zeros_like(o))
+        after = get_states(pool, ids)
+        assert torch.equal(after.view(torch.int32), init.view(torch.int32))
+        # zero tokens / zero sequences are no-ops
+        W.wkv7_forward(pool, [], [0], x["r"], x["w"], x["k"], x["v"], x["a"],
+                       x["b"], o)
+        W.wkv7_forward(pool, [2, 3], [0, 0, 0], x["r"], x["w"], x["k"],
+                       x["v"], x["a"], x["b"], o)
+        torch.cuda.synchronize()
+        assert torch.equal(get_states(pool, ids).view(torch.int32),
+                           init.view(torch.int32))
+    finally:
+        W.wkv7_pool_destroy(pool)

@@ -225,3 +225,25 @@ def cfg_large_pool(seed: int = 4, n_slots: int = 4096, H: int = 64,
     lens = rng.integers(min_len, max_len + 1, size=n_prefill)
     pre = make_batch(rng, pre_ids, lens, H, N, BF16)
     return dec, states, pre
+
+
+def draw_tokens_device(gen: "torch.Generator", T: int, H: int, N: int,
+                       dtype: str, device) -> Dict[str, torch.Tensor]:
+    """The same recipe drawn with a seeded torch generator on `device`.
+
+    Used where many steps of fresh inputs are needed on the device (the
+    benchmark); parity tests use the float64 draws above.
+    """
+    shape = (T, H, N)
+    f = dict(dtype=torch.float32, device=device, generator=gen)
+    r = torch.randn(shape, **f)
+    k = torch.randn(shape, **f)
+    v = torch.randn(shape, **f)
+    x = torch.randn(shape, **f) * 0.5 - 0.6
+    w = torch.exp(-torch.exp(x))
+    z = torch.randn(shape, **f)
+    kk = z / torch.linalg.vector_norm(z, dim=-1, keepdim=True)
+    alpha = torch.sigmoid(torch.randn(shape, **f))
+    td = _torch_dtype(dtype)
+    out = {"r": r, "w": w, "k": k, "v": v, "a": -kk, "b": kk * alpha}
+    return {n: out[n].to(td).contiguous() for n in NAMES}
