@@ -112,6 +112,82 @@ def run_decode(steps: int, warmup: int, seed: int = 1):
     }
 
 
+def chunk_mfma_flops_per_chunk_head() -> int:
+    """bf16 MFMA flops the chunked kernel issues per 64-token chunk and head
+    (each 16x16x32 instruction is 16384 flops, 16x16x16 is 8192): Gram
+    matrices 240, value side 4 x 148 and the inverse's off-diagonal blocks 9
+    16x16x32 instructions, plus 30 16x16x16 ones."""
+    return (240 + 4 * 148 + 9) * 16384 + 30 * 8192
+
+
+def prefill_alg_flops_per_token_head(L: int = 64) -> float:
+    """Dense flop count of the chunked form per token and head:
+    16 L N + 8 N^2 + (2/3) L^2 + N^2 / L."""
+    return 16 * L * N + 8 * N * N + (2.0 / 3.0) * L * L + N * N / L
+
+
+def run_prefill(steps: int, warmup: int, seed: int = 2):
+    """8 fresh sequences of 4096 tokens, H=32, bf16 inputs, zero state; one
+    step = reset the 8 slots + one forward over the packed batch. The
+    forward is timed with HIP events on the launch stream."""
+    import torch
+    import wkv7_inputs as G
+    from linear_attention_rnn_amd import wkv7 as W
+
+    dev = torch.device("cuda:0")
+    n_seq, T, H = 8, 4096, 32
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    x = G.draw_tokens_device(gen, n_seq * T, H, N, "bf16", dev)
+    ids = np.arange(n_seq, dtype=np.int32)
+    cu = (np.arange(n_seq + 1) * T).astype(np.int32)
+    o = torch.empty((n_seq * T, H, N), dtype=torch.float32, device=dev)
+    pool = W.wkv7_pool_create(n_seq, H, N)
+    stream = torch.cuda.current_stream()
+    try:
+        def step():
+            W.wkv7_reset(pool, ids, stream=stream)
+            W.wkv7_forward(pool, ids, cu, x["r"], x["w"], x["k"], x["v"],
+                           x["a"], x["b"], o, stream=stream)
+
+        for _ in range(warmup):
+            step()
+        ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        torch.cuda.synchronize()
+        for i in range(steps):
+            W.wkv7_reset(pool, ids, stream=stream)
+            ev0[i].record(stream)
+            W.wkv7_forward(pool, ids, cu, x["r"], x["w"], x["k"], x["v"],
+                           x["a"], x["b"], o, stream=stream)
+            ev1[i].record(stream)
+        torch.cuda.synchronize()
+        k_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(ev0, ev1)]))
+    finally:
+        W.wkv7_pool_destroy(pool)
+    tokens = n_seq * T
+    chunks = n_seq * (T // 64)
+    bytes_alg = tokens * H * (6 * N * 2 + N * 4) + n_seq * H * 2 * 4 * N * N
+    issued = chunks * H * chunk_mfma_flops_per_chunk_head()
+    alg = tokens * H * prefill_alg_flops_per_token_head()
+    sec = k_ms * 1e-3
+    return {
+        "workload": "prefill_b8_t4096_h32_bf16in_f32state",
+        "tokens_per_s": tokens / sec,
+        "kernel": "chunk_kernel<bf16>",
+        "kernel_ms": k_ms,
+        "hbm": {"achieved": bytes_alg / sec / 1e9, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": bytes_alg / sec / 1e9 / HBM_PEAK_GBS,
+                "bytes_per_launch": bytes_alg},
+        "mfma": {"issued_tflops": issued / sec / 1e12,
+                 "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                 "util": issued / sec / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+                 "issued_flops_per_launch": issued,
+                 "algorithmic_tflops": alg / sec / 1e12},
+        "steps": steps, "warmup": warmup,
+    }
+
+
 def cpu_baseline(seconds: float, seed: int = 1):
     """The float64 oracle on a bounded sample: whole decode steps of the same
     256-slot, H=32 batch, repeated until `seconds` have passed."""
@@ -144,6 +220,8 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--prefill-steps", type=int, default=10)
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not "
@@ -191,6 +269,8 @@ def main(argv=None) -> int:
             "bytes_per_launch": d["bytes_per_launch"],
         },
     }
+    if not args.no_prefill:
+        line["prefill"] = run_prefill(args.prefill_steps, 2)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -75,7 +75,7 @@ struct wkv7_pool {
   int32_t n_slots = 0, H = 0, N = 0;
   float* state = nullptr;
   size_t slot_floats = 0;
-  int64_t prefill_min_len = int64_t(1) << 30;
+  int64_t prefill_min_len = 64;
   std::vector<int32_t> free_ids;     // stack; top = back
   std::vector<uint8_t> allocated;
   Stage ring[kRing];

@@ -1,0 +1,130 @@
+"""Parity of the chunked-prefill kernel with the float64 oracle (GPU)."""
+import numpy as np
+import pytest
+import torch
+
+import wkv7_inputs as G
+from linear_attention_rnn_amd import wkv7 as W
+from oracle import wkv7_forward as oracle_forward, wkv7_sequence
+from tests.gpu_util import (DEV, say, set_states, get_states, run_forward,
+                            rel_err, tol_for)
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(ids, lens, H, dtype, n_slots, init=None, min_len=None, seed=0,
+         **draw):
+    rng = np.random.default_rng(seed)
+    b = G.make_batch(rng, ids, lens, H, 64, dtype, **draw)
+    pool = W.wkv7_pool_create(n_slots, H, 64)
+    try:
+        if min_len is not None:
+            W.wkv7_pool_set_option(pool, W.WKV7_OPT_PREFILL_MIN_LEN, min_len)
+        if init is not None:
+            set_states(pool, ids, init)
+        o = run_forward(pool, b)
+        S = get_states(pool, ids)
+    finally:
+        W.wkv7_pool_destroy(pool)
+    states = {} if init is None else \
+        {int(i): G.as_f64(init[n]) for n, i in enumerate(ids)}
+    o_ref, S_ref = oracle_forward(states, b.slot_ids, b.cu_seqlens,
+                                  b.inputs64(), H, 64)
+    e_o = rel_err(o, o_ref)
+    e_s = max(rel_err(S[n], S_ref[int(i)]) for n, i in enumerate(ids))
+    return e_o, e_s, o, S
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_small_config_chunked(dtype):
+    """H=2, one sequence of T=64 (exactly one chunk), zero state."""
+    say(f"small config chunked dtype={dtype}")
+    e_o, e_s, _, _ = _run([0], [64], 2, dtype, 1)
+    say(f"  o err {e_o:.3e}  S err {e_s:.3e}")
+    assert e_o < tol_for(dtype) and e_s < tol_for(dtype)
+    assert e_o < 5e-4 and e_s < 5e-4
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_ragged_chunked_with_state(dtype):
+    """Several tiles and ragged tails, non-zero initial states, chunked and
+    sequential sequences in one call."""
+    lens = [64, 65, 1, 127, 200, 3, 130, 128]
+    H = 3
+    ids = np.arange(len(lens), dtype=np.int32)[::-1].copy()
+    init = G.draw_states(np.random.default_rng(11), len(ids), H, 64)
+    say(f"ragged chunked dtype={dtype} lens={lens}")
+    e_o, e_s, _, _ = _run(ids, lens, H, dtype, len(ids), init=init, seed=1)
+    say(f"  o err {e_o:.3e}  S err {e_s:.3e}")
+    assert e_o < 5e-4 and e_s < 5e-4
+
+
+def test_every_length_chunked():
+    """PREFILL_MIN_LEN=1: every sequence (lengths 1..70) on the chunked
+    kernel, so single partial chunks of every size are covered."""
+    lens = list(range(1, 71))
+    H = 1
+    ids = np.arange(len(lens), dtype=np.int32)
+    init = G.draw_states(np.random.default_rng(12), len(ids), H, 64)
+    e_o, e_s, _, _ = _run(ids, lens, H, "bf16", len(ids), init=init,
+                          min_len=1, seed=2)
+    say(f"every length: o err {e_o:.3e}  S err {e_s:.3e}")
+    assert e_o < 5e-4 and e_s < 5e-4
+
+
+@pytest.mark.parametrize("w", [0.02, 1e-4])
+def test_extreme_decay_chunks(w):
+    """Decay so strong that the scaled operands would overflow: those
+    chunks run token by token inside the chunked kernel."""
+    lens = [64, 150]
+    H = 2
+    ids = np.array([0, 1], np.int32)
+    init = G.draw_states(np.random.default_rng(13), 2, H, 64)
+    e_o, e_s, o, S = _run(ids, lens, H, "f32", 2, init=init, seed=3,
+                          w_override=w)
+    say(f"extreme w={w}: o err {e_o:.3e}  S err {e_s:.3e}")
+    assert np.all(np.isfinite(o.numpy())) and np.all(np.isfinite(S.numpy()))
+    assert e_o < 5e-4 and e_s < 5e-4
+
+
+def test_chunked_matches_sequential_within_rounding():
+    """Both kernels on the same inputs agree to fp32 rounding, not bitwise."""
+    lens = [300, 64]
+    H = 4
+    ids = np.array([0, 1], np.int32)
+    init = G.draw_states(np.random.default_rng(14), 2, H, 64)
+    _, _, o1, S1 = _run(ids, lens, H, "bf16", 2, init=init, seed=4)
+    _, _, o2, S2 = _run(ids, lens, H, "bf16", 2, init=init, seed=4,
+                        min_len=1 << 30)
+    assert rel_err(o1, o2.double().numpy()) < 5e-4
+    assert rel_err(S1, S2.double().numpy()) < 5e-4
+
+
+def test_prefill_full_size_sampled():
+    """8 sequences of T=4096, H=32, bf16, zero state, in the launch
+    configuration the benchmark times; outputs and final states of sampled
+    (sequence, head) pairs against the oracle, run one pair at a time."""
+    wl = G.cfg_prefill(seed=2)
+    b = wl.batch
+    say(f"prefill {wl.name}: T_tot={b.T_tot}")
+    pool = W.wkv7_pool_create(wl.n_slots, wl.H, 64)
+    try:
+        o = run_forward(pool, b)
+        S = get_states(pool, b.slot_ids)
+    finally:
+        W.wkv7_pool_destroy(pool)
+    assert np.all(np.isfinite(o.numpy()))
+    rng = np.random.default_rng(5)
+    pairs = [(int(s), int(hh)) for s, hh in
+             zip(rng.integers(0, 8, 6), rng.integers(0, wl.H, 6))]
+    worst_o = worst_s = 0.0
+    for s, hh in pairs:
+        lo, hi = b.cu_seqlens[s], b.cu_seqlens[s + 1]
+        x = {n: G.as_f64(b.inputs[n][lo:hi, hh]) for n in G.NAMES}
+        o_ref, S_ref = wkv7_sequence(np.zeros((64, 64)), **x)
+        e_o = rel_err(o[lo:hi, hh], o_ref)
+        e_s = rel_err(S[s, hh], S_ref)
+        say(f"  seq {s} head {hh}: o err {e_o:.3e}  S err {e_s:.3e}")
+        worst_o, worst_s = max(worst_o, e_o), max(worst_s, e_s)
+    assert worst_o < 2e-2 and worst_s < 2e-2
+    assert worst_o < 1e-3 and worst_s < 1e-3   # bf16x3 operands: far inside
