@@ -178,7 +178,8 @@ def run_prefill(steps: int, warmup: int, seed: int = 2):
         "kernel_ms": k_ms,
         "hbm": {"achieved": bytes_alg / sec / 1e9, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": bytes_alg / sec / 1e9 / HBM_PEAK_GBS,
-                "bytes_per_launch": bytes_alg},
+                "bytes_per_launch": bytes_alg,
+                "traffic": load_traffic("prefill", bytes_alg)},
         "mfma": {"issued_tflops": issued / sec / 1e12,
                  "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                  "util": issued / sec / 1e12 / BF16_MFMA_PEAK_TFLOPS,
@@ -221,6 +222,8 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--legs", default="decode,prefill",
+                    help="comma list of legs to run (profiling one kernel)")
     ap.add_argument("--prefill-steps", type=int, default=10)
     args = ap.parse_args(argv)
     if args.gpus != 1:
@@ -238,6 +241,11 @@ def main(argv=None) -> int:
         print("bench.py: no GPU visible", file=sys.stderr)
         return 2
 
+    legs = set(args.legs.split(","))
+    if legs == {"prefill"}:
+        print(json.dumps({"prefill": run_prefill(args.prefill_steps, 2)}),
+              flush=True)
+        return 0
     d = run_decode(args.steps, args.warmup)
     achieved = d["bytes_per_launch"] / (d["kernel_ms"] * 1e-3) / 1e9
     traffic = load_traffic("decode", d["bytes_per_launch"])
@@ -269,7 +277,7 @@ def main(argv=None) -> int:
             "bytes_per_launch": d["bytes_per_launch"],
         },
     }
-    if not args.no_prefill:
+    if not args.no_prefill and "prefill" in legs:
         line["prefill"] = run_prefill(args.prefill_steps, 2)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
