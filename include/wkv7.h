@@ -78,7 +78,14 @@ enum {
    * the batch. The chunked kernel runs a chunk token by token when its
    * decay exceeds the range of its scaled operands, so both paths accept
    * any w in (0, 1]. */
-  WKV7_OPT_PREFILL_MIN_LEN = 1
+  WKV7_OPT_PREFILL_MIN_LEN = 1,
+  /* Operand precision of the chunked kernel for bf16 inputs. 0 (default):
+   * the key-side Gram products use split bf16 (hi + lo) operands and the
+   * value-side products single fp16 operands (the state and intermediates
+   * scaled by powers of two), about 3e-3 of max|err|/rms(o) on the
+   * workloads' inputs. 1: every product uses split bf16 operands, about
+   * 1e-4, roughly twice the work. fp32 inputs always use 1. */
+  WKV7_OPT_CHUNK_PRECISE = 2
 };
 
 typedef struct wkv7_pool wkv7_pool;

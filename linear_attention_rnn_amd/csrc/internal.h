@@ -31,9 +31,14 @@ struct SeqArgs {
 // Sequential kernel: one wavefront per (sequence, head), state in registers.
 hipError_t launch_seq(const SeqArgs& args, hipStream_t stream);
 
-// Chunked-prefill kernel for sequences of at least one chunk.
-hipError_t launch_chunked(const SeqArgs& args, int32_t max_len,
+// Chunked-prefill kernel for sequences of at least one chunk. bf16 inputs
+// take the fp16-value-side kernel unless `precise`; fp32 inputs always take
+// the split-bf16 kernel.
+hipError_t launch_chunked(const SeqArgs& args, bool precise,
                           hipStream_t stream);
+
+// Chunked-prefill kernel for bf16 inputs (fp16 value side).
+hipError_t launch_chunked_h(const SeqArgs& args, hipStream_t stream);
 
 // Slot copies. `pairs` holds n (src, dst) int32 pairs on the device.
 hipError_t launch_copy_slots(float* pool, size_t slot_floats,

@@ -76,6 +76,7 @@ struct wkv7_pool {
   float* state = nullptr;
   size_t slot_floats = 0;
   int64_t prefill_min_len = 64;
+  bool chunk_precise = false;
   std::vector<int32_t> free_ids;     // stack; top = back
   std::vector<uint8_t> allocated;
   Stage ring[kRing];
@@ -281,6 +282,13 @@ wkv7_status wkv7_pool_set_option(wkv7_pool* p, int32_t opt, int64_t val) {
     p->prefill_min_len = val;
     return WKV7_OK;
   }
+  if (opt == WKV7_OPT_CHUNK_PRECISE) {
+    if (val != 0 && val != 1)
+      return fail(WKV7_ERR_INVALID_ARG, "CHUNK_PRECISE=%lld must be 0 or 1",
+                  static_cast<long long>(val));
+    p->chunk_precise = val != 0;
+    return WKV7_OK;
+  }
   return fail(WKV7_ERR_UNSUPPORTED, "unknown option %d", opt);
 }
 
@@ -384,7 +392,7 @@ wkv7_status wkv7_forward(wkv7_pool* p, const int32_t* slot_ids,
   if (!chunk_items.empty()) {
     args.items = reinterpret_cast<const WorkItem*>(dev) + seq_items.size();
     args.n_items = static_cast<int32_t>(chunk_items.size());
-    e = wkv7::launch_chunked(args, chunk_items.front().len, hs);
+    e = wkv7::launch_chunked(args, p->chunk_precise, hs);
     if (e != hipSuccess) return fail_hip(e, "chunked kernel launch");
   }
   return stage_commit(stage, hs);

@@ -34,6 +34,7 @@ WKV7_F32 = 0
 WKV7_BF16 = 1
 
 WKV7_OPT_PREFILL_MIN_LEN = 1
+WKV7_OPT_CHUNK_PRECISE = 2
 
 # Every symbol include/wkv7.h declares.
 EXPORTS = (

@@ -19,7 +19,7 @@ from tests.gpu_util import (DEV, say, set_states, get_states, run_forward,
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-2          # bf16 inputs
-TIGHT = 1e-3        # what the kernels actually reach, with margin
+TIGHT = 1e-2        # what the default kernels reach, with margin
 
 
 def _bits_equal(a, b):
