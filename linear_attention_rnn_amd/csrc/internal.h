@@ -37,8 +37,11 @@ hipError_t launch_seq(const SeqArgs& args, hipStream_t stream);
 hipError_t launch_chunked(const SeqArgs& args, bool precise,
                           hipStream_t stream);
 
-// Chunked-prefill kernel for bf16 inputs (fp16 value side).
+// Chunked-prefill kernels for bf16 inputs with an fp16 value side: the
+// single-stage one (64-token chunks) and the two-stage pipelined one
+// (32-token chunks).
 hipError_t launch_chunked_h(const SeqArgs& args, hipStream_t stream);
+hipError_t launch_chunked_p(const SeqArgs& args, hipStream_t stream);
 
 // Slot copies. `pairs` holds n (src, dst) int32 pairs on the device.
 hipError_t launch_copy_slots(float* pool, size_t slot_floats,

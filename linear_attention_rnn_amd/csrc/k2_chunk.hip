@@ -595,7 +595,7 @@ hipError_t launch_chunked(const SeqArgs& args, bool precise,
   if (args.n_items <= 0) return hipSuccess;
   const int64_t blocks = static_cast<int64_t>(args.n_items) * args.H;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  if (args.dtype == WKV7_BF16 && !precise) return launch_chunked_h(args, stream);
+  if (args.dtype == WKV7_BF16 && !precise) return launch_chunked_p(args, stream);
   dim3 grid(static_cast<unsigned>(blocks)), block(256);
   if (args.dtype == WKV7_BF16)
     hipLaunchKernelGGL(chunk_kernel<WKV7_BF16>, grid, block, 0, stream, args);

@@ -1,0 +1,735 @@
+// Pipelined chunked-prefill WKV-7 kernel for bf16 inputs on gfx950.
+//
+// Same operation as the other kernels (page "RWKV-X Architecture", section
+// "WKV-7 Kernel (Generalized Delta Rule)", product-form reading
+// S_t = S_{t-1}(diag(w_t) + a_t b_t^T) + v_t k_t^T, o_t = S_t r_t), in the
+// chunked (WY/UT) form with chunks of L = 32 tokens. Per chunk, with
+// Lambda_t = prod_{u<=t} w_u and suf_t = prod_{u>t} w_u per key channel,
+//   Abar_t = a_t Lambda_{t-1}, Rbar_t = r_t Lambda_t,
+//   Bbar_s = b_s suf_s,        Kbar_s = k_s suf_s,
+//   A_ab = strict_lower(<Abar_t / Lambda_L, Bbar_s>), A_ak likewise with Kbar,
+//   M_rb = lower(<Rbar_t / Lambda_L, Bbar_s>),        M_rk likewise with Kbar,
+//   T = (I - A_ab)^-1,
+//   X = Abar S0^T + A_ak V,  U = T X,
+//   O = Rbar S0^T + M_rb U + M_rk V,
+//   S_L = Lambda_L S0 + U^T Bbar + V^T Kbar.
+// Every Gram term <., .> is the exact decay between s and t (<= 1) times
+// the inputs; only the operands Abar / Lambda_L, Rbar / Lambda_L are large.
+//
+// Organisation: one 512-thread workgroup (8 wavefronts, two per SIMD) per
+// (sequence, head), as a pipeline over chunks. In step c:
+//   * key wavefronts 0-3 build chunk c: running-product decays, the scaled
+//     operands (into one of two LDS buffers), then the four Gram matrices
+//     (wavefront w computes matrix w);
+//   * key wavefront 0 also builds T for chunk c - 1 (diagonal 16x16 blocks by
+//     forward substitution, the off-diagonal block by two MFMA products),
+//     its latency hidden behind the element-wise work;
+//   * value wavefronts 4-7 consume chunk c - 1: wavefront 4 + w owns state
+//     rows i in [16 w, 16 w + 16), kept in registers as MFMA accumulator
+//     tiles of S^T, and computes X, then U, O (written to HBM) and the state
+//     update.
+// Three workgroup barriers per step; fallback flags travel with the second
+// and third (a ballot per wavefront, posted to LDS).
+//
+// Precision: Gram products use split bf16 (hi + lo) operands, three MFMAs
+// with fp32 accumulation; the diagonal blocks of T are fp32; every
+// value-side product uses single fp16 operands, with the state, X and U
+// scaled by powers of two (exact) before conversion. About 3e-3 of
+// max|err|/rms against the float64 oracle on the workloads' inputs (bf16
+// bar: 2e-2). A chunk whose Lambda_L falls below 2^-100 in some channel, or
+// whose fp16 operands would leave the fp16 range, runs token by token on the
+// value wavefronts instead (exact for any w in (0, 1]).
+//
+// MFMA fragments (verified lane layout of v_mfma_f32_16x16x32_{bf16,f16}
+// and 16x16x16): lane l = 16 g + n holds operand row n and, for a 32-wide k
+// range at kb, k = kb + {4g..4g+3, 16+4g..16+4g+3}; the result lane holds
+// C[4g + r][n]. With this k order two 16-row result tiles form the operand
+// fragment of the next product in registers.
+
+#include "internal.h"
+#include "../../include/wkv7.h"
+
+namespace wkv7 {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kL = 32;                   // chunk length
+constexpr int kP64 = 68;                 // pitch of 64-wide rows (elements)
+constexpr int kP32 = 36;                 // pitch of 32-wide rows (elements)
+constexpr int kM64 = kL * kP64;          // [32][64] matrix, elements
+constexpr int kM32 = kL * kP32;          // [32][32] matrix
+constexpr int kMT = 64 * kP32;           // [64][32] matrix
+
+// LDS map (bytes)
+constexpr int kOffGR = 0;                                  // 4 pairs [32][64]
+constexpr int kOffAB = kOffGR + 4 * 2 * kM64 * 2;          // fp16 A_ab, A_ab^T
+constexpr int kOffTOT = kOffAB + 2 * kM32 * 2;             // fp32 [8][64]
+constexpr int kVOBytes = (2 * kM64 + 3 * kMT) * 2;         // per buffer
+constexpr int kOffVO = kOffTOT + 8 * 64 * 4;               // 2 buffers
+constexpr int kLLBytes = 3 * kM32 * 2;
+constexpr int kOffLL = kOffVO + 2 * kVOBytes;              // 2 buffers
+constexpr int kOffLAM = kOffLL + 2 * kLLBytes;             // fp32 [2][64]
+constexpr int kOffFLG = kOffLAM + 2 * 64 * 4;              // u32 [2][8]
+constexpr int kLdsBytes = kOffFLG + 2 * 8 * 4;
+static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+
+constexpr float kHalfSafe = 32768.f;            // fp16 operand bound
+constexpr float kMinLamL = 7.88860905e-31f;     // 2^-100
+
+struct F8 { bf16x8 h, l; };
+struct F4 { bf16x4 h, l; };
+
+__device__ __forceinline__ void split(float x, __bf16& h, __bf16& l) {
+  h = static_cast<__bf16>(x);
+  l = static_cast<__bf16>(x - static_cast<float>(h));
+}
+__device__ __forceinline__ f32x4 mmab(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mmab16(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mmah(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mm3(const F8& p, const F8& q, f32x4 c) {
+  c = mmab(p.l, q.h, c);
+  c = mmab(p.h, q.l, c);
+  return mmab(p.h, q.h, c);
+}
+__device__ __forceinline__ f32x4 mm3(const F4& p, const F4& q, f32x4 c) {
+  c = mmab16(p.l, q.h, c);
+  c = mmab16(p.h, q.l, c);
+  return mmab16(p.h, q.h, c);
+}
+
+template <typename V8, typename V4, typename E>
+__device__ __forceinline__ V8 ld8(const E* m, int pitch, int row, int kb,
+                                  int g) {
+  const E* p = m + row * pitch + kb + 4 * g;
+  V4 a = *reinterpret_cast<const V4*>(p);
+  V4 b = *reinterpret_cast<const V4*>(p + 16);
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+// split-bf16 pair fragment; the lo matrix follows the hi matrix at +mat
+__device__ __forceinline__ F8 ldp8(const __bf16* pair, int mat, int pitch,
+                                   int row, int kb, int g) {
+  return F8{ld8<bf16x8, bf16x4>(pair, pitch, row, kb, g),
+            ld8<bf16x8, bf16x4>(pair + mat, pitch, row, kb, g)};
+}
+__device__ __forceinline__ F4 ldp4(const __bf16* pair, int mat, int pitch,
+                                   int row, int kb, int g) {
+  const int o = row * pitch + kb + 4 * g;
+  return F4{*reinterpret_cast<const bf16x4*>(pair + o),
+            *reinterpret_cast<const bf16x4*>(pair + mat + o)};
+}
+__device__ __forceinline__ f16x8 ldh8(const _Float16* m, int pitch, int row,
+                                      int kb, int g) {
+  return ld8<f16x8, f16x4>(m, pitch, row, kb, g);
+}
+__device__ __forceinline__ F4 frag4(f32x4 t) {
+  F4 f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    __bf16 h, l;
+    split(t[r], h, l); f.h[r] = h; f.l[r] = l;
+  }
+  return f;
+}
+__device__ __forceinline__ f16x8 frag8h(f32x4 t0, f32x4 t1, float s) {
+  f16x8 f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    f[r] = static_cast<_Float16>(t0[r] * s);
+    f[4 + r] = static_cast<_Float16>(t1[r] * s);
+  }
+  return f;
+}
+__device__ __forceinline__ float bf_lo(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+
+__device__ __forceinline__ void put2p(__bf16* pair, int mat, int pitch,
+                                      int row, int col, float x0, float x1) {
+  __bf16 h0, l0, h1, l1;
+  split(x0, h0, l0);
+  split(x1, h1, l1);
+  bf16x2 h = {h0, h1}, l = {l0, l1};
+  *reinterpret_cast<bf16x2*>(pair + row * pitch + col) = h;
+  *reinterpret_cast<bf16x2*>(pair + mat + row * pitch + col) = l;
+}
+__device__ __forceinline__ void put2h(_Float16* m, int pitch, int row, int col,
+                                      float x0, float x1) {
+  f16x2 v = {static_cast<_Float16>(x0), static_cast<_Float16>(x1)};
+  *reinterpret_cast<f16x2*>(m + row * pitch + col) = v;
+}
+__device__ __forceinline__ void put4h(_Float16* m, int pitch, int row, int col,
+                                      f32x4 x) {
+  f16x4 v;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) v[r] = static_cast<_Float16>(x[r]);
+  *reinterpret_cast<f16x4*>(m + row * pitch + col) = v;
+}
+
+// Maxima of non-negative floats as unsigned bit patterns: the same order,
+// and a NaN (any sign cleared) sorts above +Inf, so it is never dropped.
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint32_t dpp_umax16(uint32_t x) {
+  x = umax(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0xB1, 0xF, 0xF, false)));
+  x = umax(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x4E, 0xF, 0xF, false)));
+  x = umax(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x141, 0xF, 0xF, false)));
+  x = umax(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x140, 0xF, 0xF, false)));
+  return x;
+}
+// max over the wavefront of x >= 0 (or NaN): rows of 16 by DPP, then across rows
+__device__ __forceinline__ float wave_max(float x) {
+  uint32_t u = dpp_umax16(__float_as_uint(x));
+  u = umax(u, static_cast<uint32_t>(__shfl_xor(static_cast<int>(u), 16)));
+  u = umax(u, static_cast<uint32_t>(__shfl_xor(static_cast<int>(u), 32)));
+  return __uint_as_float(u);
+}
+// power of two s with max|x s| < 2^14 for max|x| = m (1 if m is 0 or not
+// finite); 1/s in *inv
+__device__ __forceinline__ float pow2_scale(float m, float* inv) {
+  const uint32_t bits = __float_as_uint(m);
+  const int e = static_cast<int>((bits >> 23) & 0xffu) - 127;
+  if (!(m > 0.f) || e > 126 || e < -100) { *inv = 1.f; return 1.f; }
+  const int k = 13 - e;
+  *inv = __uint_as_float(static_cast<uint32_t>(127 - k) << 23);
+  return __uint_as_float(static_cast<uint32_t>(127 + k) << 23);
+}
+// max(m, |x_r|) on bit patterns (NaN propagates, see umax)
+__device__ __forceinline__ float abs_max4(f32x4 x, float m) {
+  uint32_t u = __float_as_uint(m);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) u = umax(u, __float_as_uint(x[r]) & 0x7fffffffu);
+  return __uint_as_float(u);
+}
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+// per-half max of |bf16| bit patterns (sign cleared); NaN/Inf sort highest
+__device__ __forceinline__ uint32_t absmax_bits(uint32_t m, uint32_t x) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(
+      __builtin_bit_cast(u16x2, m), __builtin_bit_cast(u16x2, x & 0x7fff7fffu)));
+}
+// true if either half of a per-half max of bf16 bit patterns is >= limit
+__device__ __forceinline__ bool any_half_ge(uint32_t m, uint32_t limit) {
+  return (m & 0xffffu) >= limit || (m >> 16) >= limit;
+}
+
+// raw inputs of a key thread: rows 4 rg + e (e < 4), channels 2 jp, 2 jp + 1
+struct Raw { uint32_t r[4], w[4], k[4], a[4], b[4], v[4]; };
+
+// Loads through buffer resources based at the chunk's first row, with a
+// 32-bit lane offset and no branch: a row past the chunk's end re-reads the
+// last valid row (always in bounds). The caller replaces such rows by
+// padding (pad_raw) when it consumes them, so nothing waits on the loads
+// here.
+__device__ __forceinline__ void load_raw(Raw& x, const SeqArgs& p, int t0,
+                                         int n, int h, int rg, int jp) {
+  const size_t row0 = (static_cast<size_t>(t0) * p.H + h) * (kN * 2);  // bytes
+  const uint32_t rowb = static_cast<uint32_t>(p.H) * (kN * 2);
+  const int bytes = static_cast<int>(static_cast<uint32_t>(n) * rowb);
+  const char* base[6] = {static_cast<const char*>(p.r), static_cast<const char*>(p.w),
+                         static_cast<const char*>(p.k), static_cast<const char*>(p.a),
+                         static_cast<const char*>(p.b), static_cast<const char*>(p.v)};
+  __amdgpu_buffer_rsrc_t rs[6];
+#pragma unroll
+  for (int u = 0; u < 6; ++u)
+    rs[u] = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base[u] + row0),
+                                              0, bytes, 0x00020000);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int voff = static_cast<int>(
+        static_cast<uint32_t>(min(4 * rg + e, n - 1)) * rowb + 4 * jp);
+    x.r[e] = __builtin_amdgcn_raw_buffer_load_b32(rs[0], voff, 0, 0);
+    x.w[e] = __builtin_amdgcn_raw_buffer_load_b32(rs[1], voff, 0, 0);
+    x.k[e] = __builtin_amdgcn_raw_buffer_load_b32(rs[2], voff, 0, 0);
+    x.a[e] = __builtin_amdgcn_raw_buffer_load_b32(rs[3], voff, 0, 0);
+    x.b[e] = __builtin_amdgcn_raw_buffer_load_b32(rs[4], voff, 0, 0);
+    x.v[e] = __builtin_amdgcn_raw_buffer_load_b32(rs[5], voff, 0, 0);
+  }
+}
+// rows 4 rg + e >= n become padding: w = 1, everything else 0 (state unchanged)
+__device__ __forceinline__ void pad_raw(Raw& x, int n, int rg) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const bool pad = 4 * rg + e >= n;
+    x.r[e] = pad ? 0u : x.r[e];
+    x.w[e] = pad ? 0x3f803f80u : x.w[e];
+    x.k[e] = pad ? 0u : x.k[e];
+    x.a[e] = pad ? 0u : x.a[e];
+    x.b[e] = pad ? 0u : x.b[e];
+    x.v[e] = pad ? 0u : x.v[e];
+  }
+}
+
+// ---- T = (I - A_ab)^-1 on a value wavefront, all in registers ----
+// A 16x16 matrix M is held as two fp16 operand fragments and their fp32
+// values:
+//   row(M): lane (g, n) holds M[n][4g + e]   (left operand of a product)
+//   col(M): lane (g, n) holds M[4g + e][n]   (right operand; also the
+//                                             result layout of a product)
+// so L*R gives col(LR) = mfma(row(L), col(R)) and row(LR) = col((LR)^T) =
+// mfma(col(R), row(L)): every product yields both fragments of its result.
+// T is consumed as fp16, so fp16 operands with fp32 accumulation suffice.
+struct Frag { f16x4 row, col; f32x4 frow, fcol; };
+
+__device__ __forceinline__ f32x4 mmh16(f16x4 a, f16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f16x4 h4(f32x4 x) {
+  f16x4 h;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) h[r] = static_cast<_Float16>(x[r]);
+  return h;
+}
+__device__ __forceinline__ Frag frag_of(f32x4 frow, f32x4 fcol) {
+  return Frag{h4(frow), h4(fcol), frow, fcol};
+}
+__device__ __forceinline__ Frag product(const Frag& L, const Frag& R) {
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  return frag_of(mmh16(R.col, L.row, z), mmh16(L.row, R.col, z));
+}
+// P + P*N
+__device__ __forceinline__ Frag product_add(const Frag& P, const Frag& N) {
+  return frag_of(mmh16(N.col, P.row, P.frow), mmh16(P.row, N.col, P.fcol));
+}
+__device__ __forceinline__ f32x4 f32_of(f16x4 h) {
+  f32x4 x;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) x[r] = static_cast<float>(h[r]);
+  return x;
+}
+// D = (I - A)^-1 = (I + A)(I + A^2)(I + A^4)(I + A^8) for strictly lower
+// 16x16 A (A^16 = 0)
+__device__ __forceinline__ Frag inverse_unit_lower(f16x4 arow, f16x4 acol,
+                                                   int g, int n16) {
+  Frag N{arow, acol, f32_of(arow), f32_of(acol)};
+  f32x4 prow = N.frow, pcol = N.fcol;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    if (4 * g + r == n16) { prow[r] += 1.f; pcol[r] += 1.f; }
+  }
+  Frag P = frag_of(prow, pcol);
+#pragma unroll
+  for (int it = 0; it < 3; ++it) {
+    N = product(N, N);
+    P = product_add(P, N);
+  }
+  return P;
+}
+__device__ __forceinline__ f16x4 ldh4(const _Float16* m, int pitch, int row,
+                                      int col) {
+  return *reinterpret_cast<const f16x4*>(m + row * pitch + col);
+}
+
+// Workgroup OR of two flag bits with one barrier: lane 0 of every wave
+// posts its wave's bits; all threads read the eight posts after the barrier.
+__device__ __forceinline__ uint32_t barrier_or2(uint32_t* slot, int wv,
+                                                int lane, bool b0, bool b1) {
+  const uint32_t m0 = __builtin_amdgcn_ballot_w64(b0) != 0 ? 1u : 0u;
+  const uint32_t m1 = __builtin_amdgcn_ballot_w64(b1) != 0 ? 2u : 0u;
+  if (lane == 0) slot[wv] = m0 | m1;
+  __syncthreads();
+  uint32_t r = 0;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) r |= slot[w];
+  return r;
+}
+
+// Exact token-by-token recurrence for one chunk on a value wavefront (rows
+// i = 16 vb + n16 of the state, held as S[jt][r] = S[i][16 jt + 4 g + r]).
+__device__ __forceinline__ void exact_chunk(const SeqArgs& p, f32x4* S, int t0,
+                                         int n, int h, int vb, int g,
+                                         int n16) {
+  const uint16_t* R = static_cast<const uint16_t*>(p.r);
+  const uint16_t* Wp = static_cast<const uint16_t*>(p.w);
+  const uint16_t* K = static_cast<const uint16_t*>(p.k);
+  const uint16_t* A = static_cast<const uint16_t*>(p.a);
+  const uint16_t* B = static_cast<const uint16_t*>(p.b);
+  const uint16_t* V = static_cast<const uint16_t*>(p.v);
+  const int i = 16 * vb + n16;
+  for (int t = 0; t < n; ++t) {
+    const size_t base = (static_cast<size_t>(t0 + t) * p.H + h) * kN;
+    float rr[16], ww[16], kk[16], aa[16], bb[16];
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const size_t o = base + 16 * jt + 4 * g + r;
+        rr[4 * jt + r] = __uint_as_float(static_cast<uint32_t>(R[o]) << 16);
+        ww[4 * jt + r] = __uint_as_float(static_cast<uint32_t>(Wp[o]) << 16);
+        kk[4 * jt + r] = __uint_as_float(static_cast<uint32_t>(K[o]) << 16);
+        aa[4 * jt + r] = __uint_as_float(static_cast<uint32_t>(A[o]) << 16);
+        bb[4 * jt + r] = __uint_as_float(static_cast<uint32_t>(B[o]) << 16);
+      }
+    }
+    const float vi = __uint_as_float(static_cast<uint32_t>(V[base + i]) << 16);
+    float sa = 0.f;
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sa = fmaf(S[jt][r], aa[4 * jt + r], sa);
+    sa += __shfl_xor(sa, 16);
+    sa += __shfl_xor(sa, 32);
+    float o = 0.f;
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        S[jt][r] = fmaf(S[jt][r], ww[4 * jt + r],
+                        fmaf(sa, bb[4 * jt + r], vi * kk[4 * jt + r]));
+        o = fmaf(S[jt][r], rr[4 * jt + r], o);
+      }
+    o += __shfl_xor(o, 16);
+    o += __shfl_xor(o, 32);
+    if (g == 0) p.o[base + i] = o;
+  }
+}
+
+__global__ __launch_bounds__(512, 1)
+void chunk_p_kernel(SeqArgs p) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
+  __bf16* GR = reinterpret_cast<__bf16*>(lds + kOffGR);
+  __bf16* Ahat = GR;                       // pair [t][j]
+  __bf16* Rhat = GR + 2 * kM64;            // pair [t][j]
+  __bf16* Bbar = GR + 4 * kM64;            // pair [s][j]
+  __bf16* Kbar = GR + 6 * kM64;            // pair [s][j]
+  _Float16* AB = reinterpret_cast<_Float16*>(lds + kOffAB);   // A_ab [t][s], then [s][t]
+  float* TOT = reinterpret_cast<float*>(lds + kOffTOT);
+  float* LAMb = reinterpret_cast<float*>(lds + kOffLAM);
+  uint32_t* FLG = reinterpret_cast<uint32_t*>(lds + kOffFLG);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool is_key = wv < 4;
+  const int g = lane >> 4;
+  const int n16 = lane & 15;
+  const int item = blockIdx.x / p.H;
+  const int h = blockIdx.x - item * p.H;
+  if (item >= p.n_items) return;
+  const WorkItem it = p.items[item];
+  const int nch = (it.len + kL - 1) / kL;
+  const size_t rowstride = static_cast<size_t>(p.H) * kN;
+
+  // key-thread ownership: channel pair jp, rows 4 rg .. 4 rg + 3
+  const int jp = lane & 31;
+  const int j0 = 2 * jp;
+  const int rg = 2 * (wv & 3) + (lane >> 5);
+  // value-wavefront ownership: state rows i in [16 vb, 16 vb + 16)
+  const int vb = wv & 3;
+
+  float* sbase = p.pool + (static_cast<size_t>(it.slot) * p.H + h) * (kN * kN)
+                 + (16 * vb + n16) * kN + 4 * g;
+  f32x4 S[4] = {};   // S[jt][r] = S[i = 16 vb + n16][j = 16 jt + 4 g + r]
+  if (!is_key) {
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) {
+      float4 x = *reinterpret_cast<const float4*>(sbase + 16 * jt);
+      S[jt] = f32x4{x.x, x.y, x.z, x.w};
+    }
+  }
+
+  Raw nxt;
+  if (is_key) load_raw(nxt, p, it.tok0, min(kL, it.len), h, rg, jp);
+
+  // fallback flags, known to every thread: of chunk step-1 (early: its
+  // operands; gram: its Gram matrices) and of chunk step-2 (tri: its T)
+  bool early_prev = false, gram_prev = false;
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+
+  for (int step = 0; step <= nch; ++step) {
+    const int cK = step;            // chunk whose operands and Grams are built
+    const int cV = step - 1;        // chunk whose T is built and value side run
+    const bool k_on = is_key && cK < nch;
+    const bool v_on = !is_key && cV >= 0;
+    const int bK = cK & 1, bV = cV & 1;
+    _Float16* VOk = reinterpret_cast<_Float16*>(lds + kOffVO + bK * kVOBytes);
+    _Float16* LLk = reinterpret_cast<_Float16*>(lds + kOffLL + bK * kLLBytes);
+    const _Float16* VOv = reinterpret_cast<const _Float16*>(lds + kOffVO + bV * kVOBytes);
+    const _Float16* LLv = reinterpret_cast<const _Float16*>(lds + kOffLL + bV * kLLBytes);
+    const int nV = min(kL, it.len - cV * kL);
+    const int t0K = it.tok0 + cK * kL;
+    const int t0V = it.tok0 + cV * kL;
+
+    // ===== interval 0: key: prefix products of the thread's 4 rows =====
+    Raw x;
+    float w0[4], w1[4], P0[4], P1[4];
+    if (k_on) {
+      x = nxt;
+      pad_raw(x, min(kL, it.len - cK * kL), rg);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { w0[e] = bf_lo(x.w[e]); w1[e] = bf_hi(x.w[e]); }
+      P0[0] = w0[0]; P1[0] = w1[0];
+#pragma unroll
+      for (int e = 1; e < 4; ++e) { P0[e] = P0[e - 1] * w0[e]; P1[e] = P1[e - 1] * w1[e]; }
+      TOT[rg * 64 + j0] = P0[3];
+      TOT[rg * 64 + j0 + 1] = P1[3];
+    }
+    __syncthreads();                                              // B1
+
+    // ===== interval 1 =====
+    bool bad_k = false;
+    if (k_on) {
+      // key: operands of chunk cK
+      float pre0 = 1.f, pre1 = 1.f, lam0 = 1.f, lam1 = 1.f, suf0 = 1.f, suf1 = 1.f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float g0 = TOT[q * 64 + j0], g1 = TOT[q * 64 + j0 + 1];
+        lam0 *= g0; lam1 *= g1;
+        if (q < rg) { pre0 *= g0; pre1 *= g1; }
+        if (q > rg) { suf0 *= g0; suf1 *= g1; }
+      }
+      if (rg == 0) { LAMb[bK * 64 + j0] = lam0; LAMb[bK * 64 + j0 + 1] = lam1; }
+      const float inv0 = 1.f / lam0, inv1 = 1.f / lam1;
+      _Float16* Abar = VOk;
+      _Float16* Rbar = VOk + kM64;
+      _Float16* BbT = VOk + 2 * kM64;
+      _Float16* KbT = BbT + kMT;
+      _Float16* Vt = KbT + kMT;
+      // range of the raw inputs (|Abar| <= |a| etc. when every |w| <= 1)
+      uint32_t mx = 0u, mw = 0u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        mx = absmax_bits(mx, x.a[e]); mx = absmax_bits(mx, x.r[e]);
+        mx = absmax_bits(mx, x.b[e]); mx = absmax_bits(mx, x.k[e]);
+        mx = absmax_bits(mx, x.v[e]); mw = absmax_bits(mw, x.w[e]);
+      }
+      bad_k = !(lam0 >= kMinLamL) || !(lam1 >= kMinLamL) ||
+              any_half_ge(mx, 0x4700u) ||     // |x| >= 2^15 (or NaN/Inf)
+              any_half_ge(mw, 0x3f81u);       // |w| > 1 (or NaN)
+      float sfx0 = suf0, sfx1 = suf1;
+      float bt0[4], bt1[4], kt0[4], kt1[4], vt0[4], vt1[4];
+#pragma unroll
+      for (int e = 3; e >= 0; --e) {
+        const int t = 4 * rg + e;
+        const float lp0 = e == 0 ? pre0 : pre0 * P0[e - 1];
+        const float lp1 = e == 0 ? pre1 : pre1 * P1[e - 1];
+        const float lt0 = pre0 * P0[e], lt1 = pre1 * P1[e];
+        const float ab0 = bf_lo(x.a[e]) * lp0, ab1 = bf_hi(x.a[e]) * lp1;
+        const float rb0 = bf_lo(x.r[e]) * lt0, rb1 = bf_hi(x.r[e]) * lt1;
+        const float bb0 = bf_lo(x.b[e]) * sfx0, bb1 = bf_hi(x.b[e]) * sfx1;
+        const float kb0 = bf_lo(x.k[e]) * sfx0, kb1 = bf_hi(x.k[e]) * sfx1;
+        put2p(Ahat, kM64, kP64, t, j0, ab0 * inv0, ab1 * inv1);
+        put2p(Rhat, kM64, kP64, t, j0, rb0 * inv0, rb1 * inv1);
+        put2p(Bbar, kM64, kP64, t, j0, bb0, bb1);
+        put2p(Kbar, kM64, kP64, t, j0, kb0, kb1);
+        put2h(Abar, kP64, t, j0, ab0, ab1);
+        put2h(Rbar, kP64, t, j0, rb0, rb1);
+        bt0[e] = bb0; bt1[e] = bb1; kt0[e] = kb0; kt1[e] = kb1;
+        vt0[e] = bf_lo(x.v[e]); vt1[e] = bf_hi(x.v[e]);
+        sfx0 *= w0[e]; sfx1 *= w1[e];
+      }
+      put4h(BbT, kP32, j0, 4 * rg, f32x4{bt0[0], bt0[1], bt0[2], bt0[3]});
+      put4h(BbT, kP32, j0 + 1, 4 * rg, f32x4{bt1[0], bt1[1], bt1[2], bt1[3]});
+      put4h(KbT, kP32, j0, 4 * rg, f32x4{kt0[0], kt0[1], kt0[2], kt0[3]});
+      put4h(KbT, kP32, j0 + 1, 4 * rg, f32x4{kt1[0], kt1[1], kt1[2], kt1[3]});
+      put4h(Vt, kP32, j0, 4 * rg, f32x4{vt0[0], vt0[1], vt0[2], vt0[3]});
+      put4h(Vt, kP32, j0 + 1, 4 * rg, f32x4{vt1[0], vt1[1], vt1[2], vt1[3]});
+      // next chunk's inputs, in flight from here on
+      if (cK + 1 < nch)
+        load_raw(nxt, p, t0K + kL, min(kL, it.len - (cK + 1) * kL), h, rg, jp);
+    }
+    // value side, first half: X and T of chunk cV (or the whole chunk exactly)
+    bool v_exact_done = false;
+    float inv_s = 1.f;
+    f16x8 Sf0 = {}, Sf1 = {}, Vf = {}, Tf0 = {}, Tf1 = {};
+    f32x4 X[2] = {z, z};
+    if (v_on) {
+      bool exact = early_prev || gram_prev;
+      if (!exact) {
+        const _Float16* Abar = VOv;
+        const _Float16* Vt = VOv + 2 * kM64 + 2 * kMT;
+        const _Float16* Aak = LLv;
+        float m = 0.f;
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) m = abs_max4(S[jt], m);
+        const float sS = pow2_scale(wave_max(m), &inv_s);
+        Sf0 = frag8h(S[0], S[1], sS);
+        Sf1 = frag8h(S[2], S[3], sS);
+        Vf = ldh8(Vt, kP32, 16 * vb + n16, 0, g);
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          f32x4 cs = mmah(ldh8(Abar, kP64, 16 * tt + n16, 0, g), Sf0, z);
+          cs = mmah(ldh8(Abar, kP64, 16 * tt + n16, 32, g), Sf1, cs);
+          const f32x4 cv = mmah(ldh8(Aak, kP32, 16 * tt + n16, 0, g), Vf, z);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) X[tt][r] = fmaf(cs[r], inv_s, cv[r]);
+        }
+        // T = [[D_0, 0], [T_10, D_1]], D_p = (I - A_pp)^-1, T_10 = D_1 A_10 D_0
+        const _Float16* ABr = AB;
+        const _Float16* ABt = ABr + kM32;
+        const Frag D0 = inverse_unit_lower(ldh4(ABr, kP32, n16, 4 * g),
+                                           ldh4(ABt, kP32, n16, 4 * g), g, n16);
+        const Frag D1 = inverse_unit_lower(ldh4(ABr, kP32, 16 + n16, 16 + 4 * g),
+                                           ldh4(ABt, kP32, 16 + n16, 16 + 4 * g), g, n16);
+        // Y = A_10 D_0 needs row(A_10) and col(D_0) only
+        const f16x4 a10 = ldh4(ABr, kP32, 16 + n16, 4 * g);
+        Frag Y;
+        Y.fcol = mmh16(a10, D0.col, z);
+        Y.frow = mmh16(D0.col, a10, z);
+        Y.row = h4(Y.frow);
+        Y.col = h4(Y.fcol);
+        const Frag T10 = product(D1, Y);
+        float tm = abs_max4(D0.frow, 0.f);
+        tm = abs_max4(D1.frow, tm);
+        tm = abs_max4(T10.frow, tm);
+        // operand fragments of T's row tiles: k in [0,16) then [16,32)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          Tf0[r] = static_cast<_Float16>(D0.frow[r]);
+          Tf0[4 + r] = static_cast<_Float16>(0.f);
+          Tf1[r] = static_cast<_Float16>(T10.frow[r]);
+          Tf1[4 + r] = static_cast<_Float16>(D1.frow[r]);
+        }
+        exact = !(wave_max(tm) < kHalfSafe);   // T out of fp16 range
+      }
+      if (exact) {
+        // the whole chunk token by token
+        exact_chunk(p, S, t0V, nV, h, vb, g, n16);
+        v_exact_done = true;
+      }
+    }
+    const uint32_t f2 = barrier_or2(FLG, wv, lane, k_on && bad_k, false);  // B2
+    const bool early_cur = (f2 & 1u) != 0;   // chunk cK
+
+    // ===== interval 2 =====
+    float gmax = 0.f;
+    if (k_on && !early_cur) {
+      // key: Gram matrix wv, tiles (tt, st) = (0,0), (1,0), (1,1) as C[s][t]
+      const __bf16* Pm = (wv & 1) ? Kbar : Bbar;
+      const __bf16* Qm = (wv >= 2) ? Rhat : Ahat;
+      const bool strict = wv < 2;
+      f32x4 gt[3];
+      int ti = 0;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+        for (int st = 0; st <= tt; ++st) {
+          f32x4 c = z;
+#pragma unroll
+          for (int kc = 0; kc < 2; ++kc)
+            c = mm3(ldp8(Pm, kM64, kP64, 16 * st + n16, 32 * kc, g),
+                    ldp8(Qm, kM64, kP64, 16 * tt + n16, 32 * kc, g), c);
+          const int t = 16 * tt + n16;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int s = 16 * st + 4 * g + r;
+            const bool keep = strict ? (s < t) : (s <= t);
+            c[r] = keep ? c[r] : 0.f;
+          }
+          gt[ti++] = c;
+        }
+      }
+      if (wv == 0) {
+        // A_ab in fp16 as [t][s] rows and as [s][t] rows (tile ti holds
+        // C[s][t] = A_ab[t][s])
+        _Float16* ABr = AB;
+        _Float16* ABt = ABr + kM32;
+        ti = 0;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+          for (int st = 0; st <= tt; ++st, ++ti) {
+            gmax = abs_max4(gt[ti], gmax);
+            put4h(ABr, kP32, 16 * tt + n16, 16 * st + 4 * g, gt[ti]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              ABt[(16 * st + 4 * g + r) * kP32 + 16 * tt + n16] =
+                  static_cast<_Float16>(gt[ti][r]);
+          }
+        }
+      } else {
+        _Float16* dst = LLk + (wv - 1) * kM32;
+        ti = 0;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+          for (int st = 0; st <= tt; ++st, ++ti) {
+            gmax = abs_max4(gt[ti], gmax);
+            put4h(dst, kP32, 16 * tt + n16, 16 * st + 4 * g, gt[ti]);
+          }
+        }
+        put4h(dst, kP32, n16, 16 + 4 * g, z);
+      }
+    }
+    if (v_on && !v_exact_done) {
+      // value side, second half: U, O, state update of chunk cV
+      const _Float16* Rbar = VOv + kM64;
+      const _Float16* BbT = VOv + 2 * kM64;
+      const _Float16* KbT = BbT + kMT;
+      const _Float16* Mrb = LLv + kM32;
+      const _Float16* Mrk = LLv + 2 * kM32;
+      const float* lam = LAMb + bV * 64;
+      float inv_x;
+      const float sX = pow2_scale(wave_max(abs_max4(X[1], abs_max4(X[0], 0.f))), &inv_x);
+      const f16x8 Xf = frag8h(X[0], X[1], sX);
+      f32x4 U[2];
+      U[0] = mmah(Tf0, Xf, z);
+      U[1] = mmah(Tf1, Xf, z);
+      float inv_u;
+      const float sU = pow2_scale(wave_max(abs_max4(U[1], abs_max4(U[0], 0.f))), &inv_u);
+      const float inv_ux = inv_u * inv_x;
+      const f16x8 Uf = frag8h(U[0], U[1], sU);
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        f32x4 cs = mmah(Sf0, ldh8(Rbar, kP64, 16 * tt + n16, 0, g), z);
+        cs = mmah(Sf1, ldh8(Rbar, kP64, 16 * tt + n16, 32, g), cs);
+        const f32x4 cu = mmah(Uf, ldh8(Mrb, kP32, 16 * tt + n16, 0, g), z);
+        const f32x4 cv = mmah(Vf, ldh8(Mrk, kP32, 16 * tt + n16, 0, g), z);
+        const int t = 16 * tt + n16;
+        if (t < nV) {
+          float4 ov;
+          ov.x = fmaf(cs[0], inv_s, fmaf(cu[0], inv_ux, cv[0]));
+          ov.y = fmaf(cs[1], inv_s, fmaf(cu[1], inv_ux, cv[1]));
+          ov.z = fmaf(cs[2], inv_s, fmaf(cu[2], inv_ux, cv[2]));
+          ov.w = fmaf(cs[3], inv_s, fmaf(cu[3], inv_ux, cv[3]));
+          *reinterpret_cast<float4*>(p.o + static_cast<size_t>(t0V + t) * rowstride
+                                     + static_cast<size_t>(h) * kN + 16 * vb + 4 * g) = ov;
+        }
+      }
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) {
+        const f32x4 cu = mmah(ldh8(BbT, kP32, 16 * jt + n16, 0, g), Uf, z);
+        const f32x4 cv = mmah(ldh8(KbT, kP32, 16 * jt + n16, 0, g), Vf, z);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          S[jt][r] = fmaf(lam[16 * jt + 4 * g + r], S[jt][r],
+                          fmaf(cu[r], inv_ux, cv[r]));
+      }
+    }
+    const uint32_t f3 = barrier_or2(FLG + 8, wv, lane,
+                                    k_on && !early_cur && !(gmax < kHalfSafe),
+                                    false);                      // B3
+    early_prev = early_cur;
+    gram_prev = (f3 & 1u) != 0;
+  }
+
+  if (!is_key) {
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt)
+      *reinterpret_cast<float4*>(sbase + 16 * jt) =
+          make_float4(S[jt][0], S[jt][1], S[jt][2], S[jt][3]);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_chunked_p(const SeqArgs& args, hipStream_t stream) {
+  if (args.n_items <= 0) return hipSuccess;
+  const int64_t blocks = static_cast<int64_t>(args.n_items) * args.H;
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(chunk_p_kernel, dim3(static_cast<unsigned>(blocks)),
+                     dim3(512), 0, stream, args);
+  return hipGetLastError();
+}
+
+}  // namespace wkv7
