@@ -81,46 +81,69 @@ def run_decode(steps: int, warmup: int, seed: int = 1):
         stream = torch.cuda.current_stream()
         torch.cuda.synchronize()
 
+        # the batch layout is the same every step: validate it and put it
+        # on the device once, then each step only launches the kernel
+        plan = W.wkv7_plan_create(pool, ids, cu)
+
         def step(x):
-            W.wkv7_forward(pool, ids, cu, x["r"], x["w"], x["k"], x["v"],
-                           x["a"], x["b"], o, stream=stream)
+            W.wkv7_forward_plan(pool, plan, x["r"], x["w"], x["k"], x["v"],
+                                x["a"], x["b"], o, stream=stream)
 
         for i in range(warmup):
             step(xs[i])
-        ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-        ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
+        ev0.record(stream)
         for i in range(steps):
-            ev0[i].record(stream)
             step(xs[warmup + i])
-            ev1[i].record(stream)
+        ev1.record(stream)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        k_ms = [a.elapsed_time(b) for a, b in zip(ev0, ev1)]
+        # one kernel per step, back to back on the stream: the events'
+        # span over K launches is the average launch duration (with the
+        # gaps between launches, so never below the kernel's own time)
+        k_ms = ev0.elapsed_time(ev1) / steps
+
+        # the same steps through wkv7_forward (host-side validation and
+        # metadata staging on every call), for reference
+        torch.cuda.synchronize()
+        f0 = time.perf_counter()
+        for i in range(steps):
+            x = xs[warmup + i]
+            W.wkv7_forward(pool, ids, cu, x["r"], x["w"], x["k"], x["v"],
+                           x["a"], x["b"], o, stream=stream)
+        torch.cuda.synchronize()
+        f1 = time.perf_counter()
+        W.wkv7_plan_destroy(plan)
     finally:
         W.wkv7_pool_destroy(pool)
     wall = t1 - t0
-    kernel_ms = float(np.mean(k_ms))
     bytes_launch = n_active * H * decode_bytes_per_token_head(2)
     return {
         "tokens": n_active * steps, "wall_s": wall,
         "ms_per_step": wall / steps * 1e3,
-        "kernel_ms": kernel_ms, "kernel_ms_median": float(np.median(k_ms)),
+        "forward_ms_per_step": (f1 - f0) / steps * 1e3,
+        "kernel_ms": float(k_ms),
         "bytes_per_launch": bytes_launch, "n_active": n_active, "H": H,
         "n_slots": n_slots,
     }
 
 
 def chunk_mfma_flops_per_chunk_head() -> int:
-    """bf16 MFMA flops the chunked kernel issues per 64-token chunk and head
-    (each 16x16x32 instruction is 16384 flops, 16x16x16 is 8192): Gram
-    matrices 240, value side 4 x 148 and the inverse's off-diagonal blocks 9
-    16x16x32 instructions, plus 30 16x16x16 ones."""
-    return (240 + 4 * 148 + 9) * 16384 + 30 * 8192
+    """MFMA flops the bf16 chunked-prefill kernel issues per 32-token chunk
+    and head, from the instructions in its compiled loop body: each of the
+    4 key wavefronts issues 18 v_mfma_f32_16x16x32_bf16, each of the 4 value
+    wavefronts 24 v_mfma_f32_16x16x32_f16 and 21 v_mfma_f32_16x16x16_f16
+    (16384 and 8192 flops per instruction)."""
+    return 4 * 18 * 16384 + 4 * (24 * 16384 + 21 * 8192)
 
 
-def prefill_alg_flops_per_token_head(L: int = 64) -> float:
+CHUNK_L = 32        # chunk length of the bf16 chunked-prefill kernel
+
+
+def prefill_alg_flops_per_token_head(L: int = CHUNK_L) -> float:
     """Dense flop count of the chunked form per token and head:
     16 L N + 8 N^2 + (2/3) L^2 + N^2 / L."""
     return 16 * L * N + 8 * N * N + (2.0 / 3.0) * L * L + N * N / L
@@ -145,10 +168,12 @@ def run_prefill(steps: int, warmup: int, seed: int = 2):
     pool = W.wkv7_pool_create(n_seq, H, N)
     stream = torch.cuda.current_stream()
     try:
+        plan = W.wkv7_plan_create(pool, ids, cu)
+
         def step():
             W.wkv7_reset(pool, ids, stream=stream)
-            W.wkv7_forward(pool, ids, cu, x["r"], x["w"], x["k"], x["v"],
-                           x["a"], x["b"], o, stream=stream)
+            W.wkv7_forward_plan(pool, plan, x["r"], x["w"], x["k"], x["v"],
+                                x["a"], x["b"], o, stream=stream)
 
         for _ in range(warmup):
             step()
@@ -158,15 +183,16 @@ def run_prefill(steps: int, warmup: int, seed: int = 2):
         for i in range(steps):
             W.wkv7_reset(pool, ids, stream=stream)
             ev0[i].record(stream)
-            W.wkv7_forward(pool, ids, cu, x["r"], x["w"], x["k"], x["v"],
-                           x["a"], x["b"], o, stream=stream)
+            W.wkv7_forward_plan(pool, plan, x["r"], x["w"], x["k"], x["v"],
+                                x["a"], x["b"], o, stream=stream)
             ev1[i].record(stream)
         torch.cuda.synchronize()
         k_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(ev0, ev1)]))
+        W.wkv7_plan_destroy(plan)
     finally:
         W.wkv7_pool_destroy(pool)
     tokens = n_seq * T
-    chunks = n_seq * (T // 64)
+    chunks = n_seq * (T // CHUNK_L)
     bytes_alg = tokens * H * (6 * N * 2 + N * 4) + n_seq * H * 2 * 4 * N * N
     issued = chunks * H * chunk_mfma_flops_per_chunk_head()
     alg = tokens * H * prefill_alg_flops_per_token_head()
@@ -174,7 +200,7 @@ def run_prefill(steps: int, warmup: int, seed: int = 2):
     return {
         "workload": "prefill_b8_t4096_h32_bf16in_f32state",
         "tokens_per_s": tokens / sec,
-        "kernel": "chunk_kernel<bf16>",
+        "kernel": "chunk_p_kernel (bf16 inputs, chunks of 32 tokens)",
         "kernel_ms": k_ms,
         "hbm": {"achieved": bytes_alg / sec / 1e9, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": bytes_alg / sec / 1e9 / HBM_PEAK_GBS,
@@ -267,6 +293,9 @@ def main(argv=None) -> int:
             "n_slots": d["n_slots"], "active_slots": d["n_active"],
             "H": d["H"], "N": N, "input_dtype": "bf16",
             "state_dtype": "f32", "output_dtype": "f32",
+            "launch": "wkv7_forward_plan (metadata validated and uploaded "
+                      "once)",
+            "forward_api_ms_per_step": d["forward_ms_per_step"],
         },
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
@@ -274,6 +303,7 @@ def main(argv=None) -> int:
             "traffic": traffic,
             "kernel": "seq_kernel<bf16> (decode)",
             "kernel_ms": d["kernel_ms"],
+            "timing": "HIP events around the K timed launches / K",
             "bytes_per_launch": d["bytes_per_launch"],
         },
     }

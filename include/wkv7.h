@@ -153,6 +153,47 @@ wkv7_status wkv7_forward(wkv7_pool* pool, const int32_t* slot_ids,
                          const void* k, const void* v, const void* a,
                          const void* b, float* o, void* stream);
 
+/* plans — the metadata of a batch, validated once and kept on the device,
+ * for callers that run the same batch layout step after step (steady-state
+ * decode) or capture steps into a HIP graph. Page "rvLLM", section "What
+ * actually makes B=1 fast": per-step synchronous metadata uploads serialise
+ * the host against the GPU, and graphing the decode loop removes them;
+ * section "Correctness discipline": a captured graph binds a frozen
+ * metadata layout. */
+typedef struct wkv7_plan wkv7_plan;
+
+/* Validate slot_ids[n_seqs] and cu_seqlens[n_seqs+1] (host arrays) exactly
+ * as wkv7_forward does, with the same errors, split the sequences between
+ * the kernels (using the pool's PREFILL_MIN_LEN now) and copy the work list
+ * into device memory owned by the plan. The copy is synchronous, so the
+ * host arrays may be reused at once. *out receives the plan, which belongs
+ * to `pool` and must be destroyed before it. */
+wkv7_status wkv7_plan_create(wkv7_pool* pool, const int32_t* slot_ids,
+                             const int32_t* cu_seqlens, int32_t n_seqs,
+                             wkv7_plan** out);
+
+/* Token rows (T_tot = cu_seqlens[n_seqs]) a forward with this plan reads
+ * from r..b and writes to o; 0 for NULL. */
+int64_t wkv7_plan_tokens(const wkv7_plan* plan);
+
+/* forward with a plan — the same computation, with the same results bit for
+ * bit, as wkv7_forward on the plan's slot_ids and cu_seqlens. It only checks
+ * the pointers and dtype (as wkv7_forward) and enqueues the kernels on
+ * `stream`: no allocation, no host-to-device copy, no event and no host
+ * wait, so it may be captured into a HIP graph. The plan's device memory
+ * must stay alive until the stream (or every launch of a graph that
+ * captured the call) has passed it. WKV7_ERR_INVALID_ARG if the plan was
+ * made for another pool. The chunked kernel's precision is the pool's
+ * CHUNK_PRECISE at the time of the call. */
+wkv7_status wkv7_forward_plan(wkv7_pool* pool, const wkv7_plan* plan,
+                              int32_t dtype, const void* r, const void* w,
+                              const void* k, const void* v, const void* a,
+                              const void* b, float* o, void* stream);
+
+/* Wait for the plan's device to finish the work enqueued so far, then free
+ * the plan. A NULL plan is a no-op. */
+wkv7_status wkv7_plan_destroy(wkv7_plan* plan);
+
 /* snapshot — copy slot `slot` (slot_bytes) into caller-owned device memory
  * dst_device, bit-exact (page "Virtual Memory for KV Cache and Model
  * Weights": a recoverable linear-state checkpoint). */

@@ -83,6 +83,15 @@ struct wkv7_pool {
   int ring_pos = 0;
 };
 
+// Work items of one batch, validated once and kept on the pool's device.
+struct wkv7_plan {
+  const wkv7_pool* pool = nullptr;
+  int device = 0;
+  WorkItem* items = nullptr;
+  int32_t n_seq_items = 0, n_chunk_items = 0;
+  int64_t T_tot = 0;
+};
+
 namespace {
 
 size_t slot_bytes_of(const wkv7_pool* p) { return p->slot_floats * sizeof(float); }
@@ -185,6 +194,92 @@ wkv7_status check_ids(const wkv7_pool* p, const int32_t* ids, int32_t n,
 
 bool aligned16(const void* q) {
   return (reinterpret_cast<uintptr_t>(q) & 15u) == 0;
+}
+
+// A validated batch: work items with the sequential-kernel items first,
+// then the chunked ones, longest first.
+struct Batch {
+  std::vector<WorkItem> items;
+  int32_t n_seq_items = 0;
+  int64_t T_tot = 0;
+  int32_t n_chunk_items() const {
+    return static_cast<int32_t>(items.size()) - n_seq_items;
+  }
+};
+
+// Checks slot_ids / cu_seqlens exactly as wkv7_forward documents and splits
+// the sequences by length (PREFILL_MIN_LEN).
+wkv7_status build_batch(const wkv7_pool* p, const int32_t* slot_ids,
+                        const int32_t* cu_seqlens, int32_t n_seqs,
+                        const char* what, Batch* out) {
+  if (n_seqs < 0) return fail(WKV7_ERR_INVALID_ARG, "n_seqs=%d < 0", n_seqs);
+  if (n_seqs == 0) return WKV7_OK;
+  if (!cu_seqlens) return fail(WKV7_ERR_INVALID_ARG, "cu_seqlens is NULL");
+  if (cu_seqlens[0] != 0)
+    return fail(WKV7_ERR_INVALID_ARG, "cu_seqlens[0]=%d, must be 0",
+                cu_seqlens[0]);
+  for (int32_t s = 0; s < n_seqs; ++s)
+    if (cu_seqlens[s + 1] < cu_seqlens[s])
+      return fail(WKV7_ERR_INVALID_ARG,
+                  "cu_seqlens decreases at %d (%d -> %d)", s, cu_seqlens[s],
+                  cu_seqlens[s + 1]);
+  if (wkv7_status st = check_ids(p, slot_ids, n_seqs, true, what)) return st;
+  out->T_tot = cu_seqlens[n_seqs];
+  std::vector<WorkItem> chunk_items;
+  out->items.reserve(static_cast<size_t>(n_seqs));
+  for (int32_t s = 0; s < n_seqs; ++s) {
+    const int32_t len = cu_seqlens[s + 1] - cu_seqlens[s];
+    if (len == 0) continue;
+    WorkItem it{slot_ids[s], cu_seqlens[s], len, 0};
+    if (len >= p->prefill_min_len) chunk_items.push_back(it);
+    else out->items.push_back(it);
+  }
+  std::stable_sort(chunk_items.begin(), chunk_items.end(),
+                   [](const WorkItem& x, const WorkItem& y) {
+                     return x.len > y.len;
+                   });
+  out->n_seq_items = static_cast<int32_t>(out->items.size());
+  out->items.insert(out->items.end(), chunk_items.begin(), chunk_items.end());
+  return WKV7_OK;
+}
+
+wkv7_status check_forward_args(int32_t dtype, int64_t T_tot, const void* r,
+                               const void* w, const void* k, const void* v,
+                               const void* a, const void* b, const float* o) {
+  if (dtype != WKV7_F32 && dtype != WKV7_BF16)
+    return fail(WKV7_ERR_UNSUPPORTED, "dtype %d unsupported", dtype);
+  if (T_tot == 0) return WKV7_OK;
+  const void* ptrs[7] = {r, w, k, v, a, b, o};
+  const char* names[7] = {"r", "w", "k", "v", "a", "b", "o"};
+  for (int i = 0; i < 7; ++i) {
+    if (!ptrs[i]) return fail(WKV7_ERR_INVALID_ARG, "%s is NULL", names[i]);
+    if (!aligned16(ptrs[i]))
+      return fail(WKV7_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[i]);
+  }
+  return WKV7_OK;
+}
+
+// Launches the kernels of a batch whose work items are on the device
+// (n_seq sequential-kernel items, then n_chunk chunked ones).
+wkv7_status launch_batch(const wkv7_pool* p, const WorkItem* dev_items,
+                         int32_t n_seq, int32_t n_chunk, int32_t dtype,
+                         const void* r, const void* w, const void* k,
+                         const void* v, const void* a, const void* b, float* o,
+                         hipStream_t hs) {
+  wkv7::SeqArgs args{p->state, nullptr, 0, p->H, dtype, r, w, k, v, a, b, o};
+  if (n_seq > 0) {
+    args.items = dev_items;
+    args.n_items = n_seq;
+    hipError_t e = wkv7::launch_seq(args, hs);
+    if (e != hipSuccess) return fail_hip(e, "sequential kernel launch");
+  }
+  if (n_chunk > 0) {
+    args.items = dev_items + n_seq;
+    args.n_items = n_chunk;
+    hipError_t e = wkv7::launch_chunked(args, p->chunk_precise, hs);
+    if (e != hipSuccess) return fail_hip(e, "chunked kernel launch");
+  }
+  return WKV7_OK;
 }
 
 }  // namespace
@@ -331,71 +426,98 @@ wkv7_status wkv7_forward(wkv7_pool* p, const int32_t* slot_ids,
                          const void* b, float* o, void* stream) {
   g_last_error.clear();
   if (wkv7_status st = check_pool(p)) return st;
-  if (n_seqs < 0) return fail(WKV7_ERR_INVALID_ARG, "n_seqs=%d < 0", n_seqs);
-  if (dtype != WKV7_F32 && dtype != WKV7_BF16)
-    return fail(WKV7_ERR_UNSUPPORTED, "dtype %d unsupported", dtype);
-  if (n_seqs == 0) return WKV7_OK;
-  if (!cu_seqlens) return fail(WKV7_ERR_INVALID_ARG, "cu_seqlens is NULL");
-  if (cu_seqlens[0] != 0)
-    return fail(WKV7_ERR_INVALID_ARG, "cu_seqlens[0]=%d, must be 0",
-                cu_seqlens[0]);
-  for (int32_t s = 0; s < n_seqs; ++s)
-    if (cu_seqlens[s + 1] < cu_seqlens[s])
-      return fail(WKV7_ERR_INVALID_ARG,
-                  "cu_seqlens decreases at %d (%d -> %d)", s, cu_seqlens[s],
-                  cu_seqlens[s + 1]);
-  if (wkv7_status st = check_ids(p, slot_ids, n_seqs, true, "forward"))
+  Batch bt;
+  if (wkv7_status st = build_batch(p, slot_ids, cu_seqlens, n_seqs, "forward", &bt))
     return st;
-  const int64_t T_tot = cu_seqlens[n_seqs];
-  if (T_tot == 0) return WKV7_OK;
-  const void* ptrs[7] = {r, w, k, v, a, b, o};
-  const char* names[7] = {"r", "w", "k", "v", "a", "b", "o"};
-  for (int i = 0; i < 7; ++i) {
-    if (!ptrs[i]) return fail(WKV7_ERR_INVALID_ARG, "%s is NULL", names[i]);
-    if (!aligned16(ptrs[i]))
-      return fail(WKV7_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[i]);
-  }
-
-  // Split by length: short sequences take the sequential kernel, long ones
-  // the chunked kernel, longest first.
-  std::vector<WorkItem> seq_items, chunk_items;
-  for (int32_t s = 0; s < n_seqs; ++s) {
-    const int32_t len = cu_seqlens[s + 1] - cu_seqlens[s];
-    if (len == 0) continue;
-    WorkItem it{slot_ids[s], cu_seqlens[s], len, 0};
-    if (len >= p->prefill_min_len) chunk_items.push_back(it);
-    else seq_items.push_back(it);
-  }
-  std::stable_sort(chunk_items.begin(), chunk_items.end(),
-                   [](const WorkItem& x, const WorkItem& y) {
-                     return x.len > y.len;
-                   });
-  std::vector<WorkItem> all(seq_items);
-  all.insert(all.end(), chunk_items.begin(), chunk_items.end());
+  if (wkv7_status st = check_forward_args(dtype, bt.T_tot, r, w, k, v, a, b, o))
+    return st;
+  if (bt.items.empty()) return WKV7_OK;
 
   DeviceGuard guard(p->device);
   if (!guard.ok) return fail(WKV7_ERR_HIP, "cannot select the pool's device");
   hipStream_t hs = static_cast<hipStream_t>(stream);
   const int32_t* dev = nullptr;
   Stage* stage = nullptr;
-  if (wkv7_status st = stage_upload(p, reinterpret_cast<const int32_t*>(all.data()),
-                                    all.size() * 4, hs, &dev, &stage))
+  if (wkv7_status st = stage_upload(p, reinterpret_cast<const int32_t*>(bt.items.data()),
+                                    bt.items.size() * 4, hs, &dev, &stage))
     return st;
-  wkv7::SeqArgs args{p->state, nullptr, 0, p->H, dtype, r, w, k, v, a, b, o};
-  hipError_t e = hipSuccess;
-  if (!seq_items.empty()) {
-    args.items = reinterpret_cast<const WorkItem*>(dev);
-    args.n_items = static_cast<int32_t>(seq_items.size());
-    e = wkv7::launch_seq(args, hs);
-    if (e != hipSuccess) return fail_hip(e, "sequential kernel launch");
-  }
-  if (!chunk_items.empty()) {
-    args.items = reinterpret_cast<const WorkItem*>(dev) + seq_items.size();
-    args.n_items = static_cast<int32_t>(chunk_items.size());
-    e = wkv7::launch_chunked(args, p->chunk_precise, hs);
-    if (e != hipSuccess) return fail_hip(e, "chunked kernel launch");
-  }
+  if (wkv7_status st = launch_batch(p, reinterpret_cast<const WorkItem*>(dev),
+                                    bt.n_seq_items, bt.n_chunk_items(), dtype,
+                                    r, w, k, v, a, b, o, hs))
+    return st;
   return stage_commit(stage, hs);
+}
+
+wkv7_status wkv7_plan_create(wkv7_pool* p, const int32_t* slot_ids,
+                             const int32_t* cu_seqlens, int32_t n_seqs,
+                             wkv7_plan** out) {
+  g_last_error.clear();
+  if (!out) return fail(WKV7_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (wkv7_status st = check_pool(p)) return st;
+  Batch bt;
+  if (wkv7_status st = build_batch(p, slot_ids, cu_seqlens, n_seqs, "plan", &bt))
+    return st;
+  wkv7_plan* pl = new (std::nothrow) wkv7_plan();
+  if (!pl) return fail(WKV7_ERR_OOM, "host allocation failed");
+  pl->pool = p;
+  pl->device = p->device;
+  pl->T_tot = bt.T_tot;
+  pl->n_seq_items = bt.n_seq_items;
+  pl->n_chunk_items = bt.n_chunk_items();
+  if (!bt.items.empty()) {
+    DeviceGuard guard(p->device);
+    if (!guard.ok) { delete pl; return fail(WKV7_ERR_HIP, "cannot select the pool's device"); }
+    const size_t bytes = bt.items.size() * sizeof(WorkItem);
+    hipError_t e = hipMalloc(reinterpret_cast<void**>(&pl->items), bytes);
+    if (e != hipSuccess) {
+      delete pl;
+      return fail(WKV7_ERR_OOM, "hipMalloc of %zu bytes for the plan failed: %s",
+                  bytes, hipGetErrorString(e));
+    }
+    e = hipMemcpy(pl->items, bt.items.data(), bytes, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+      (void)hipFree(pl->items);
+      delete pl;
+      return fail_hip(e, "hipMemcpy(plan)");
+    }
+  }
+  *out = pl;
+  return WKV7_OK;
+}
+
+int64_t wkv7_plan_tokens(const wkv7_plan* pl) { return pl ? pl->T_tot : 0; }
+
+wkv7_status wkv7_forward_plan(wkv7_pool* p, const wkv7_plan* pl, int32_t dtype,
+                              const void* r, const void* w, const void* k,
+                              const void* v, const void* a, const void* b,
+                              float* o, void* stream) {
+  g_last_error.clear();
+  if (wkv7_status st = check_pool(p)) return st;
+  if (!pl) return fail(WKV7_ERR_INVALID_ARG, "plan is NULL");
+  if (pl->pool != p)
+    return fail(WKV7_ERR_INVALID_ARG, "the plan was made for another pool");
+  if (wkv7_status st = check_forward_args(dtype, pl->T_tot, r, w, k, v, a, b, o))
+    return st;
+  if (pl->n_seq_items + pl->n_chunk_items == 0) return WKV7_OK;
+  DeviceGuard guard(p->device);
+  if (!guard.ok) return fail(WKV7_ERR_HIP, "cannot select the pool's device");
+  return launch_batch(p, pl->items, pl->n_seq_items, pl->n_chunk_items, dtype,
+                      r, w, k, v, a, b, o, static_cast<hipStream_t>(stream));
+}
+
+wkv7_status wkv7_plan_destroy(wkv7_plan* pl) {
+  g_last_error.clear();
+  if (!pl) return WKV7_OK;
+  hipError_t e = hipSuccess;
+  if (pl->items) {
+    DeviceGuard guard(pl->device);
+    e = hipDeviceSynchronize();
+    (void)hipFree(pl->items);
+  }
+  delete pl;
+  if (e != hipSuccess) return fail_hip(e, "hipDeviceSynchronize(plan destroy)");
+  return WKV7_OK;
 }
 
 wkv7_status wkv7_snapshot(wkv7_pool* p, int32_t slot, void* dst_device,

@@ -42,7 +42,8 @@ EXPORTS = (
     "wkv7_slot_bytes", "wkv7_pool_state_ptr", "wkv7_pool_shape",
     "wkv7_pool_set_option", "wkv7_slot_alloc", "wkv7_slot_free",
     "wkv7_forward", "wkv7_snapshot", "wkv7_fork", "wkv7_reset",
-    "wkv7_hibernate", "wkv7_resume",
+    "wkv7_hibernate", "wkv7_resume", "wkv7_plan_create", "wkv7_plan_tokens",
+    "wkv7_forward_plan", "wkv7_plan_destroy",
 )
 
 
@@ -106,6 +107,15 @@ lib.wkv7_hibernate.restype = _i32
 lib.wkv7_hibernate.argtypes = [_vp, _pi32, _i32, _vp, _sz, _vp]
 lib.wkv7_resume.restype = _i32
 lib.wkv7_resume.argtypes = [_vp, _pi32, _i32, _vp, _sz, _vp]
+lib.wkv7_plan_create.restype = _i32
+lib.wkv7_plan_create.argtypes = [_vp, _pi32, _pi32, _i32, ctypes.POINTER(_vp)]
+lib.wkv7_plan_tokens.restype = _i64
+lib.wkv7_plan_tokens.argtypes = [_vp]
+lib.wkv7_forward_plan.restype = _i32
+lib.wkv7_forward_plan.argtypes = [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp,
+                                  _vp, _vp, _vp]
+lib.wkv7_plan_destroy.restype = _i32
+lib.wkv7_plan_destroy.argtypes = [_vp]
 
 
 def _check(status: int) -> None:
@@ -206,6 +216,35 @@ def wkv7_forward(pool: int, slot_ids, cu_seqlens, r, w, k, v, a, b, o,
     _check(lib.wkv7_forward(pool, _iptr(ids), _iptr(cu), ids.size, code,
                             _dptr(r), _dptr(w), _dptr(k), _dptr(v), _dptr(a),
                             _dptr(b), _dptr(o), _stream(stream)))
+
+
+def wkv7_plan_create(pool: int, slot_ids, cu_seqlens) -> int:
+    """Validate and upload a batch's metadata once; returns the plan handle."""
+    ids = _ids(slot_ids)
+    cu = _ids(cu_seqlens)
+    if cu.size != ids.size + 1:
+        raise ValueError("cu_seqlens must have len(slot_ids) + 1 entries")
+    out = _vp()
+    _check(lib.wkv7_plan_create(pool, _iptr(ids), _iptr(cu), ids.size,
+                                ctypes.byref(out)))
+    return out.value
+
+
+def wkv7_plan_tokens(plan: int) -> int:
+    return int(lib.wkv7_plan_tokens(plan))
+
+
+def wkv7_forward_plan(pool: int, plan: int, r, w, k, v, a, b, o, stream=None,
+                      dtype: Optional[int] = None) -> None:
+    """wkv7_forward over a plan's batch: kernel launches only (capturable)."""
+    code = _dtype_code(r) if dtype is None else dtype
+    _check(lib.wkv7_forward_plan(pool, plan, code, _dptr(r), _dptr(w),
+                                 _dptr(k), _dptr(v), _dptr(a), _dptr(b),
+                                 _dptr(o), _stream(stream)))
+
+
+def wkv7_plan_destroy(plan: int) -> None:
+    _check(lib.wkv7_plan_destroy(plan))
 
 
 def wkv7_snapshot(pool: int, slot: int, dst, stream=None) -> None:

@@ -63,6 +63,15 @@ def test_null_pool_everywhere():
     assert L.wkv7_slot_bytes(None) == 0
     assert L.wkv7_pool_state_ptr(None) is None
     assert L.wkv7_pool_destroy(None) == W.WKV7_OK
+    out = ctypes.c_void_p(123)
+    assert L.wkv7_plan_create(None, None, None, 0, ctypes.byref(out)) == \
+        W.WKV7_ERR_INVALID_ARG
+    assert out.value is None
+    assert L.wkv7_plan_create(None, None, None, 0, None) == W.WKV7_ERR_INVALID_ARG
+    assert L.wkv7_forward_plan(None, None, 0, *([None] * 8)) == \
+        W.WKV7_ERR_INVALID_ARG
+    assert L.wkv7_plan_tokens(None) == 0
+    assert L.wkv7_plan_destroy(None) == W.WKV7_OK
 
 
 def test_last_error_is_per_thread():
