@@ -37,10 +37,8 @@ hipError_t launch_seq(const SeqArgs& args, hipStream_t stream);
 hipError_t launch_chunked(const SeqArgs& args, bool precise,
                           hipStream_t stream);
 
-// Chunked-prefill kernels for bf16 inputs with an fp16 value side: the
-// single-stage one (64-token chunks) and the two-stage pipelined one
+// Pipelined chunked-prefill kernel for bf16 inputs with an fp16 value side
 // (32-token chunks).
-hipError_t launch_chunked_h(const SeqArgs& args, hipStream_t stream);
 hipError_t launch_chunked_p(const SeqArgs& args, hipStream_t stream);
 
 // Slot copies. `pairs` holds n (src, dst) int32 pairs on the device.
