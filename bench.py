@@ -215,6 +215,202 @@ def run_prefill(steps: int, warmup: int, seed: int = 2):
     }
 
 
+def _draw_device(gen, T: int, H: int, dtype: str, dev, chunk: int = 16384):
+    """Synthetic inputs [T, H, N] drawn on the device in token chunks (the
+    float32 temporaries of a whole large batch would be several GB)."""
+    import torch
+    import wkv7_inputs as G
+    td = torch.bfloat16 if dtype == "bf16" else torch.float32
+    out = {n: torch.empty((T, H, N), dtype=td, device=dev) for n in G.NAMES}
+    for t0 in range(0, T, chunk):
+        x = G.draw_tokens_device(gen, min(chunk, T - t0), H, N, dtype, dev)
+        for n in G.NAMES:
+            out[n][t0:t0 + x[n].shape[0]].copy_(x[n])
+    return out
+
+
+def run_decode_large(steps: int = 20, warmup: int = 3, seed: int = 4):
+    """The large-pool decode step: 1024 random slots of a 4096-slot pool,
+    H=64 (1 GiB of active state, four times the MALL), fresh bf16 inputs
+    every step, launched through a plan; one event pair over the K steps."""
+    import torch
+    import wkv7_inputs as G
+    from linear_attention_rnn_amd import wkv7 as W
+
+    dev = torch.device("cuda:0")
+    n_slots, n_active, H = 4096, 1024, 64
+    ids = np.random.default_rng(seed).permutation(n_slots)[:n_active].astype(
+        np.int32)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    pool = W.wkv7_pool_create(n_slots, H, N)
+    try:
+        init = torch.randn((n_active, H, N, N), device=dev, generator=gen) * 0.1
+        W.wkv7_resume(pool, ids, init)
+        del init
+        xs = [G.draw_tokens_device(gen, n_active, H, N, "bf16", dev)
+              for _ in range(steps + warmup)]
+        cu = np.arange(n_active + 1, dtype=np.int32)
+        o = torch.empty((n_active, H, N), dtype=torch.float32, device=dev)
+        stream = torch.cuda.current_stream()
+        plan = W.wkv7_plan_create(pool, ids, cu)
+        for i in range(warmup):
+            x = xs[i]
+            W.wkv7_forward_plan(pool, plan, x["r"], x["w"], x["k"], x["v"],
+                                x["a"], x["b"], o, stream=stream)
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for i in range(steps):
+            x = xs[warmup + i]
+            W.wkv7_forward_plan(pool, plan, x["r"], x["w"], x["k"], x["v"],
+                                x["a"], x["b"], o, stream=stream)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        k_ms = ev0.elapsed_time(ev1) / steps
+        W.wkv7_plan_destroy(plan)
+    finally:
+        W.wkv7_pool_destroy(pool)
+    bytes_launch = n_active * H * decode_bytes_per_token_head(2)
+    gbs = bytes_launch / (k_ms * 1e-3) / 1e9
+    return {
+        "workload": "decode_b1024_h64_pool4096_bf16in_f32state",
+        "tokens_per_s": n_active / (k_ms * 1e-3), "kernel_ms": k_ms,
+        "hbm": {"achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": gbs / HBM_PEAK_GBS, "bytes_per_launch": bytes_launch},
+        "steps": steps, "warmup": warmup,
+    }
+
+
+def run_prefill_ragged(steps: int = 3, warmup: int = 1, seed: int = 4):
+    """32 fresh sequences with lengths integer-uniform in [128, 8192], H=64,
+    bf16 inputs; one step = reset the 32 slots + one plan forward (timed
+    with an event pair around the forward)."""
+    import torch
+    from linear_attention_rnn_amd import wkv7 as W
+
+    dev = torch.device("cuda:0")
+    H, n_seq = 64, 32
+    lens = np.random.default_rng(seed).integers(128, 8193, size=n_seq)
+    T = int(lens.sum())
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    x = _draw_device(gen, T, H, "bf16", dev)
+    ids = np.arange(n_seq, dtype=np.int32)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    o = torch.empty((T, H, N), dtype=torch.float32, device=dev)
+    pool = W.wkv7_pool_create(n_seq, H, N)
+    stream = torch.cuda.current_stream()
+    try:
+        plan = W.wkv7_plan_create(pool, ids, cu)
+        times = []
+        for i in range(warmup + steps):
+            W.wkv7_reset(pool, ids, stream=stream)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            W.wkv7_forward_plan(pool, plan, x["r"], x["w"], x["k"], x["v"],
+                                x["a"], x["b"], o, stream=stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if i >= warmup:
+                times.append(e0.elapsed_time(e1))
+        W.wkv7_plan_destroy(plan)
+    finally:
+        W.wkv7_pool_destroy(pool)
+    k_ms = float(np.mean(times))
+    sec = k_ms * 1e-3
+    bytes_alg = T * H * (6 * N * 2 + N * 4) + n_seq * H * 2 * 4 * N * N
+    chunks = int(sum((int(n) + CHUNK_L - 1) // CHUNK_L for n in lens))
+    issued = chunks * H * chunk_mfma_flops_per_chunk_head()
+    return {
+        "workload": "prefill_32ragged_128to8192_h64_bf16in_f32state",
+        "tokens": T, "tokens_per_s": T / sec, "kernel_ms": k_ms,
+        "hbm": {"achieved": bytes_alg / sec / 1e9, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": bytes_alg / sec / 1e9 / HBM_PEAK_GBS,
+                "bytes_per_launch": bytes_alg},
+        "mfma": {"issued_tflops": issued / sec / 1e12,
+                 "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                 "util": issued / sec / 1e12 / BF16_MFMA_PEAK_TFLOPS},
+        "steps": steps, "warmup": warmup,
+    }
+
+
+def run_mixed(steps: int = 10, warmup: int = 2, seed: int = 3):
+    """The 12-layer RWKV-X-0.2B-shaped stack (H=12, one 128-slot pool per
+    layer): per layer and step 64 decode tokens plus 4 fresh prefills of
+    512, 1024, 2048 and 2048 tokens in one packed call (the prefill slots
+    are reset first); fresh inputs per layer and step; one event pair over
+    the K steps of 12 layers."""
+    import torch
+    import wkv7_inputs as G
+    from linear_attention_rnn_amd import wkv7 as W
+
+    dev = torch.device("cuda:0")
+    n_layers, n_slots, H = 12, 128, 12
+    prefill_lens = [512, 1024, 2048, 2048]
+    perm = np.random.default_rng(seed).permutation(n_slots).astype(np.int32)
+    dec_ids, pre_ids = perm[:64], perm[64:68]
+    ids = np.concatenate([dec_ids, pre_ids])
+    lens = [1] * 64 + prefill_lens
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    pools, plans = [], []
+    stream = torch.cuda.current_stream()
+    try:
+        for _ in range(n_layers):
+            pool = W.wkv7_pool_create(n_slots, H, N)
+            pools.append(pool)
+            init = torch.randn((64, H, N, N), device=dev, generator=gen) * 0.1
+            W.wkv7_resume(pool, dec_ids, init)
+            plans.append(W.wkv7_plan_create(pool, ids, cu))
+        xs = [[G.draw_tokens_device(gen, T, H, N, "bf16", dev)
+               for _ in range(n_layers)] for _ in range(steps + warmup)]
+        o = torch.empty((T, H, N), dtype=torch.float32, device=dev)
+
+        def step(i):
+            for li in range(n_layers):
+                x = xs[i][li]
+                W.wkv7_reset(pools[li], pre_ids, stream=stream)
+                W.wkv7_forward_plan(pools[li], plans[li], x["r"], x["w"],
+                                    x["k"], x["v"], x["a"], x["b"], o,
+                                    stream=stream)
+
+        for i in range(warmup):
+            step(i)
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for i in range(steps):
+            step(warmup + i)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        ms = ev0.elapsed_time(ev1) / steps
+    finally:
+        for pl in plans:
+            W.wkv7_plan_destroy(pl)
+        for pool in pools:
+            W.wkv7_pool_destroy(pool)
+    bytes_layer = (64 * H * decode_bytes_per_token_head(2)
+                   + sum(prefill_lens) * H * (6 * N * 2 + N * 4)
+                   + 4 * H * 2 * 4 * N * N)
+    return {
+        "workload": "mixed_12layers_h12_64decode_4prefill_bf16in",
+        "tokens_per_step": T, "ms_per_step": ms,
+        "tokens_per_s": T / (ms * 1e-3),
+        "layer_tokens_per_s": n_layers * T / (ms * 1e-3),
+        "hbm": {"achieved": n_layers * bytes_layer / (ms * 1e-3) / 1e9,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": n_layers * bytes_layer / (ms * 1e-3) / 1e9
+                / HBM_PEAK_GBS},
+        "steps": steps, "warmup": warmup,
+    }
+
+
 def cpu_baseline(seconds: float, seed: int = 1):
     """The float64 oracle on a bounded sample: whole decode steps of the same
     256-slot, H=32 batch, repeated until `seconds` have passed."""
@@ -248,7 +444,8 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--legs", default="decode,prefill",
+    ap.add_argument("--legs",
+                    default="decode,prefill,decode_large,prefill_ragged,mixed",
                     help="comma list of legs to run (profiling one kernel)")
     ap.add_argument("--prefill-steps", type=int, default=10)
     args = ap.parse_args(argv)
@@ -309,6 +506,12 @@ def main(argv=None) -> int:
     }
     if not args.no_prefill and "prefill" in legs:
         line["prefill"] = run_prefill(args.prefill_steps, 2)
+    if "decode_large" in legs:
+        line["decode_large"] = run_decode_large()
+    if not args.no_prefill and "prefill_ragged" in legs:
+        line["prefill_ragged"] = run_prefill_ragged()
+    if "mixed" in legs:
+        line["mixed"] = run_mixed()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(line), flush=True)
