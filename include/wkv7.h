@@ -229,6 +229,51 @@ wkv7_status wkv7_hibernate(wkv7_pool* pool, const int32_t* ids, int32_t n,
 wkv7_status wkv7_resume(wkv7_pool* pool, const int32_t* ids, int32_t n,
                         const void* src, size_t bytes, void* stream);
 
+/* live-migrate — copy n slots from pool `src` (ids src_ids, host array,
+ * repeats allowed) into pool `dst` (ids dst_ids, host array, distinct),
+ * bit-exact, on `stream` (page "wkvm: state-slot inference for RWKV, GDN
+ * and Mamba hybrids", section "The allocation unit wkvm changes": the slot
+ * verbs include live-migrate). Both pools must have the same H and N
+ * (else WKV7_ERR_UNSUPPORTED) and live on the same device (pools on two
+ * devices: WKV7_ERR_UNSUPPORTED; peer migration is not built). With
+ * src == dst this is wkv7_fork. The source slots are left as they were
+ * (freeing them is the caller's wkv7_slot_free); work on the two pools on
+ * other streams must be ordered by the caller. */
+wkv7_status wkv7_migrate(wkv7_pool* src, const int32_t* src_ids,
+                         wkv7_pool* dst, const int32_t* dst_ids, int32_t n,
+                         void* stream);
+
+/* Slot images outside a pool (hibernated to host memory, sent to another
+ * process or a later library version) are described by a versioned 64-byte
+ * header, written in front of the n_slots consecutive images it describes
+ * (the layout wkv7_hibernate writes and wkv7_resume reads). Little-endian;
+ * reserved fields are zero. */
+#define WKV7_IMAGE_MAGIC "WKV7SLOT"
+enum { WKV7_IMAGE_VERSION = 1 };
+
+typedef struct {
+  char magic[8];          /* WKV7_IMAGE_MAGIC, no terminator */
+  uint32_t version;       /* WKV7_IMAGE_VERSION */
+  uint32_t header_bytes;  /* sizeof(wkv7_image_header) = 64 */
+  uint32_t H, N;          /* heads and head size of every image */
+  uint32_t state_dtype;   /* WKV7_F32 */
+  uint32_t n_slots;       /* images that follow the header */
+  uint64_t slot_bytes;    /* H*N*N*4, bytes of one image */
+  uint64_t reserved[3];   /* zero */
+} wkv7_image_header;
+
+/* Fill *hdr for n_slots images of H heads of N x N float32 (N must be 64,
+ * else WKV7_ERR_UNSUPPORTED). Host only. */
+wkv7_status wkv7_image_header_init(wkv7_image_header* hdr, int32_t H,
+                                   int32_t N, int32_t n_slots);
+
+/* Check that *hdr describes slot images this library can resume into slots
+ * of H heads of N x N: WKV7_ERR_INVALID_ARG for a bad magic, non-zero
+ * reserved fields or an inconsistent header, WKV7_ERR_UNSUPPORTED for
+ * another version or another slot shape. Host only. */
+wkv7_status wkv7_image_header_check(const wkv7_image_header* hdr, int32_t H,
+                                    int32_t N);
+
 #ifdef __cplusplus
 }
 #endif

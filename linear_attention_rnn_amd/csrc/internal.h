@@ -41,10 +41,11 @@ hipError_t launch_chunked(const SeqArgs& args, bool precise,
 // (32-token chunks).
 hipError_t launch_chunked_p(const SeqArgs& args, hipStream_t stream);
 
-// Slot copies. `pairs` holds n (src, dst) int32 pairs on the device.
-hipError_t launch_copy_slots(float* pool, size_t slot_floats,
-                             const int32_t* pairs, int32_t n,
-                             hipStream_t stream);
+// Slot copies from src_pool to dst_pool (the same pool for a fork). `pairs`
+// holds n (src slot, dst slot) int32 pairs on the device.
+hipError_t launch_copy_slots(const float* src_pool, float* dst_pool,
+                             size_t slot_floats, const int32_t* pairs,
+                             int32_t n, hipStream_t stream);
 // Zero-fill n slots listed (device int32) in `ids`.
 hipError_t launch_zero_slots(float* pool, size_t slot_floats,
                              const int32_t* ids, int32_t n,

@@ -1,4 +1,4 @@
-// Slot-copy kernels for the fork and reset verbs (page "wkvm: state-slot
+// Slot-copy kernels for the fork, migrate and reset verbs (page "wkvm: state-slot
 // inference for RWKV, GDN and Mamba hybrids", section "The allocation unit
 // wkvm changes": a fixed-size slot can be copied and restored cheaply).
 //
@@ -15,13 +15,14 @@ namespace {
 constexpr int kThreads = 256;
 
 __global__ __launch_bounds__(kThreads)
-void copy_slots_kernel(uint4* pool, size_t slot_words, const int32_t* pairs,
-                       int32_t n, int32_t blocks_per_slot) {
+void copy_slots_kernel(const uint4* src_pool, uint4* dst_pool,
+                       size_t slot_words, const int32_t* pairs, int32_t n,
+                       int32_t blocks_per_slot) {
   const int32_t pi = blockIdx.x / blocks_per_slot;
   const int32_t part = blockIdx.x - pi * blocks_per_slot;
   if (pi >= n) return;
-  const uint4* src = pool + static_cast<size_t>(pairs[2 * pi]) * slot_words;
-  uint4* dst = pool + static_cast<size_t>(pairs[2 * pi + 1]) * slot_words;
+  const uint4* src = src_pool + static_cast<size_t>(pairs[2 * pi]) * slot_words;
+  uint4* dst = dst_pool + static_cast<size_t>(pairs[2 * pi + 1]) * slot_words;
   const size_t stride = static_cast<size_t>(blocks_per_slot) * kThreads;
   for (size_t i = static_cast<size_t>(part) * kThreads + threadIdx.x;
        i < slot_words; i += stride)
@@ -52,17 +53,18 @@ int32_t blocks_per_slot(size_t slot_words) {
 
 }  // namespace
 
-hipError_t launch_copy_slots(float* pool, size_t slot_floats,
-                             const int32_t* pairs, int32_t n,
-                             hipStream_t stream) {
+hipError_t launch_copy_slots(const float* src_pool, float* dst_pool,
+                             size_t slot_floats, const int32_t* pairs,
+                             int32_t n, hipStream_t stream) {
   if (n <= 0) return hipSuccess;
   const size_t words = slot_floats / 4;
   const int32_t bps = blocks_per_slot(words);
   const int64_t blocks = static_cast<int64_t>(n) * bps;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(copy_slots_kernel, dim3(static_cast<unsigned>(blocks)),
-                     dim3(kThreads), 0, stream, reinterpret_cast<uint4*>(pool),
-                     words, pairs, n, bps);
+                     dim3(kThreads), 0, stream,
+                     reinterpret_cast<const uint4*>(src_pool),
+                     reinterpret_cast<uint4*>(dst_pool), words, pairs, n, bps);
   return hipGetLastError();
 }
 

@@ -561,9 +561,94 @@ wkv7_status wkv7_fork(wkv7_pool* p, const int32_t* src, const int32_t* dst,
   if (wkv7_status st = stage_upload(p, pairs.data(), pairs.size(), hs, &dev,
                                     &stage))
     return st;
-  hipError_t e = wkv7::launch_copy_slots(p->state, p->slot_floats, dev, n, hs);
+  hipError_t e = wkv7::launch_copy_slots(p->state, p->state, p->slot_floats,
+                                         dev, n, hs);
   if (e != hipSuccess) return fail_hip(e, "slot copy launch");
   return stage_commit(stage, hs);
+}
+
+wkv7_status wkv7_migrate(wkv7_pool* src, const int32_t* src_ids,
+                         wkv7_pool* dst, const int32_t* dst_ids, int32_t n,
+                         void* stream) {
+  g_last_error.clear();
+  if (wkv7_status st = check_pool(src)) return st;
+  if (wkv7_status st = check_pool(dst)) return st;
+  if (src == dst) return wkv7_fork(src, src_ids, dst_ids, n, stream);
+  if (src->H != dst->H || src->N != dst->N)
+    return fail(WKV7_ERR_UNSUPPORTED,
+                "migrate: slot shapes differ (H=%d N=%d vs H=%d N=%d)", src->H,
+                src->N, dst->H, dst->N);
+  if (src->device != dst->device)
+    return fail(WKV7_ERR_UNSUPPORTED,
+                "migrate: pools on devices %d and %d (only same-device "
+                "migration is built)", src->device, dst->device);
+  if (wkv7_status st = check_ids(src, src_ids, n, false, "migrate src")) return st;
+  if (wkv7_status st = check_ids(dst, dst_ids, n, true, "migrate dst")) return st;
+  if (n == 0) return WKV7_OK;
+  std::vector<int32_t> pairs(2 * static_cast<size_t>(n));
+  for (int32_t i = 0; i < n; ++i) {
+    pairs[2 * i] = src_ids[i];
+    pairs[2 * i + 1] = dst_ids[i];
+  }
+  DeviceGuard guard(dst->device);
+  if (!guard.ok) return fail(WKV7_ERR_HIP, "cannot select the pools' device");
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const int32_t* dev = nullptr;
+  Stage* stage = nullptr;
+  if (wkv7_status st = stage_upload(dst, pairs.data(), pairs.size(), hs, &dev,
+                                    &stage))
+    return st;
+  hipError_t e = wkv7::launch_copy_slots(src->state, dst->state,
+                                         dst->slot_floats, dev, n, hs);
+  if (e != hipSuccess) return fail_hip(e, "slot migrate launch");
+  return stage_commit(stage, hs);
+}
+
+wkv7_status wkv7_image_header_init(wkv7_image_header* hdr, int32_t H,
+                                   int32_t N, int32_t n_slots) {
+  g_last_error.clear();
+  if (!hdr) return fail(WKV7_ERR_INVALID_ARG, "hdr is NULL");
+  if (H < 1 || n_slots < 0)
+    return fail(WKV7_ERR_INVALID_ARG, "H=%d must be >= 1 and n_slots=%d >= 0",
+                H, n_slots);
+  if (N != wkv7::kN)
+    return fail(WKV7_ERR_UNSUPPORTED, "head size N=%d unsupported (only %d)",
+                N, wkv7::kN);
+  std::memset(hdr, 0, sizeof(*hdr));
+  std::memcpy(hdr->magic, WKV7_IMAGE_MAGIC, 8);
+  hdr->version = WKV7_IMAGE_VERSION;
+  hdr->header_bytes = sizeof(wkv7_image_header);
+  hdr->H = static_cast<uint32_t>(H);
+  hdr->N = static_cast<uint32_t>(N);
+  hdr->state_dtype = WKV7_F32;
+  hdr->n_slots = static_cast<uint32_t>(n_slots);
+  hdr->slot_bytes = static_cast<uint64_t>(H) * N * N * sizeof(float);
+  return WKV7_OK;
+}
+
+wkv7_status wkv7_image_header_check(const wkv7_image_header* hdr, int32_t H,
+                                    int32_t N) {
+  g_last_error.clear();
+  if (!hdr) return fail(WKV7_ERR_INVALID_ARG, "hdr is NULL");
+  if (std::memcmp(hdr->magic, WKV7_IMAGE_MAGIC, 8) != 0)
+    return fail(WKV7_ERR_INVALID_ARG, "not a slot image (bad magic)");
+  if (hdr->version != WKV7_IMAGE_VERSION ||
+      hdr->header_bytes != sizeof(wkv7_image_header))
+    return fail(WKV7_ERR_UNSUPPORTED,
+                "slot image version %u (header %u bytes); this library reads "
+                "version %d (%zu bytes)", hdr->version, hdr->header_bytes,
+                WKV7_IMAGE_VERSION, sizeof(wkv7_image_header));
+  for (int i = 0; i < 3; ++i)
+    if (hdr->reserved[i] != 0)
+      return fail(WKV7_ERR_INVALID_ARG, "reserved header field %d is not 0", i);
+  if (hdr->state_dtype != WKV7_F32 ||
+      hdr->slot_bytes != static_cast<uint64_t>(hdr->H) * hdr->N * hdr->N * 4)
+    return fail(WKV7_ERR_INVALID_ARG, "inconsistent slot image header");
+  if (static_cast<int64_t>(hdr->H) != H || static_cast<int64_t>(hdr->N) != N)
+    return fail(WKV7_ERR_UNSUPPORTED,
+                "slot images of H=%u N=%u do not fit slots of H=%d N=%d",
+                hdr->H, hdr->N, H, N);
+  return WKV7_OK;
 }
 
 wkv7_status wkv7_reset(wkv7_pool* p, const int32_t* ids, int32_t n,

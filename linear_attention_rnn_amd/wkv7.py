@@ -43,8 +43,21 @@ EXPORTS = (
     "wkv7_pool_set_option", "wkv7_slot_alloc", "wkv7_slot_free",
     "wkv7_forward", "wkv7_snapshot", "wkv7_fork", "wkv7_reset",
     "wkv7_hibernate", "wkv7_resume", "wkv7_plan_create", "wkv7_plan_tokens",
-    "wkv7_forward_plan", "wkv7_plan_destroy",
+    "wkv7_forward_plan", "wkv7_plan_destroy", "wkv7_migrate",
+    "wkv7_image_header_init", "wkv7_image_header_check",
 )
+
+WKV7_IMAGE_MAGIC = b"WKV7SLOT"
+WKV7_IMAGE_VERSION = 1
+
+
+class wkv7_image_header(ctypes.Structure):
+    """The 64-byte versioned header in front of serialized slot images."""
+    _fields_ = [("magic", ctypes.c_char * 8), ("version", ctypes.c_uint32),
+                ("header_bytes", ctypes.c_uint32), ("H", ctypes.c_uint32),
+                ("N", ctypes.c_uint32), ("state_dtype", ctypes.c_uint32),
+                ("n_slots", ctypes.c_uint32), ("slot_bytes", ctypes.c_uint64),
+                ("reserved", ctypes.c_uint64 * 3)]
 
 
 class Wkv7Error(RuntimeError):
@@ -116,6 +129,14 @@ lib.wkv7_forward_plan.argtypes = [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp,
                                   _vp, _vp, _vp]
 lib.wkv7_plan_destroy.restype = _i32
 lib.wkv7_plan_destroy.argtypes = [_vp]
+lib.wkv7_migrate.restype = _i32
+lib.wkv7_migrate.argtypes = [_vp, _pi32, _vp, _pi32, _i32, _vp]
+lib.wkv7_image_header_init.restype = _i32
+lib.wkv7_image_header_init.argtypes = [ctypes.POINTER(wkv7_image_header),
+                                       _i32, _i32, _i32]
+lib.wkv7_image_header_check.restype = _i32
+lib.wkv7_image_header_check.argtypes = [ctypes.POINTER(wkv7_image_header),
+                                        _i32, _i32]
 
 
 def _check(status: int) -> None:
@@ -245,6 +266,25 @@ def wkv7_forward_plan(pool: int, plan: int, r, w, k, v, a, b, o, stream=None,
 
 def wkv7_plan_destroy(plan: int) -> None:
     _check(lib.wkv7_plan_destroy(plan))
+
+
+def wkv7_migrate(src_pool: int, src_ids, dst_pool: int, dst_ids,
+                 stream=None) -> None:
+    s, d = _ids(src_ids), _ids(dst_ids)
+    if s.size != d.size:
+        raise ValueError("migrate: src_ids and dst_ids differ in length")
+    _check(lib.wkv7_migrate(src_pool, _iptr(s), dst_pool, _iptr(d), s.size,
+                            _stream(stream)))
+
+
+def wkv7_image_header_init(H: int, N: int, n_slots: int) -> wkv7_image_header:
+    hdr = wkv7_image_header()
+    _check(lib.wkv7_image_header_init(ctypes.byref(hdr), H, N, n_slots))
+    return hdr
+
+
+def wkv7_image_header_check(hdr: wkv7_image_header, H: int, N: int) -> None:
+    _check(lib.wkv7_image_header_check(ctypes.byref(hdr), H, N))
 
 
 def wkv7_snapshot(pool: int, slot: int, dst, stream=None) -> None:

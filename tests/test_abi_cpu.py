@@ -86,3 +86,38 @@ def test_last_error_is_per_thread():
     t.join()
     assert seen["msg"] == ""
     assert "NULL" in W.wkv7_last_error()
+
+
+def test_image_header_roundtrip_and_rejections():
+    assert ctypes.sizeof(W.wkv7_image_header) == 64
+    hdr = W.wkv7_image_header_init(32, 64, 5)
+    assert bytes(hdr.magic) == W.WKV7_IMAGE_MAGIC
+    assert hdr.version == W.WKV7_IMAGE_VERSION and hdr.header_bytes == 64
+    assert (hdr.H, hdr.N, hdr.n_slots) == (32, 64, 5)
+    assert hdr.slot_bytes == 32 * 64 * 64 * 4
+    W.wkv7_image_header_check(hdr, 32, 64)
+
+    def rejected(h, H, N, code):
+        with pytest.raises(W.Wkv7Error) as e:
+            W.wkv7_image_header_check(h, H, N)
+        assert e.value.status == code
+
+    rejected(hdr, 12, 64, W.WKV7_ERR_UNSUPPORTED)          # other shape
+    bad = W.wkv7_image_header.from_buffer_copy(hdr)
+    bad.version = 2
+    rejected(bad, 32, 64, W.WKV7_ERR_UNSUPPORTED)          # other version
+    bad = W.wkv7_image_header.from_buffer_copy(hdr)
+    bad.magic = b"WKV7SLOX"
+    rejected(bad, 32, 64, W.WKV7_ERR_INVALID_ARG)
+    bad = W.wkv7_image_header.from_buffer_copy(hdr)
+    bad.reserved[1] = 7
+    rejected(bad, 32, 64, W.WKV7_ERR_INVALID_ARG)
+    bad = W.wkv7_image_header.from_buffer_copy(hdr)
+    bad.slot_bytes += 4
+    rejected(bad, 32, 64, W.WKV7_ERR_INVALID_ARG)
+    with pytest.raises(W.Wkv7Error) as e:
+        W.wkv7_image_header_init(32, 128, 1)
+    assert e.value.status == W.WKV7_ERR_UNSUPPORTED
+    assert W.lib.wkv7_image_header_check(None, 1, 64) == W.WKV7_ERR_INVALID_ARG
+    assert W.lib.wkv7_migrate(None, None, None, None, 0, None) == \
+        W.WKV7_ERR_INVALID_ARG
