@@ -5,6 +5,7 @@
 // device work, so a failed call leaves the pool and the stream untouched.
 
 #include "../../include/wkv7.h"
+#include "host.h"
 #include "internal.h"
 
 #include <algorithm>
@@ -283,6 +284,24 @@ wkv7_status launch_batch(const wkv7_pool* p, const WorkItem* dev_items,
 }
 
 }  // namespace
+
+namespace wkv7 {
+
+wkv7_status host_fail(wkv7_status code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+void host_clear_error() { g_last_error.clear(); }
+
+int pool_device(const wkv7_pool* p) { return p->device; }
+
+}  // namespace wkv7
 
 extern "C" {
 

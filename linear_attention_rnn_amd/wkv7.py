@@ -45,7 +45,31 @@ EXPORTS = (
     "wkv7_hibernate", "wkv7_resume", "wkv7_plan_create", "wkv7_plan_tokens",
     "wkv7_forward_plan", "wkv7_plan_destroy", "wkv7_migrate",
     "wkv7_image_header_init", "wkv7_image_header_check",
+    "wkv7_sessions_create", "wkv7_sessions_destroy", "wkv7_session_begin",
+    "wkv7_session_end", "wkv7_session_abort", "wkv7_session_drop_chat",
+    "wkv7_sessions_stats",
 )
+
+# session outcomes and flags (include/wkv7_session.h)
+WKV7_SESSION_HIT = 0
+WKV7_SESSION_NEW = 1
+WKV7_SESSION_RESTART_EDIT = 2
+WKV7_SESSION_RESTART_PARENT = 3
+WKV7_SESSION_RESTART_EVICTED = 4
+WKV7_SESSIONS_KEEP_PARENT = 1
+
+
+class wkv7_turn_key(ctypes.Structure):
+    _fields_ = [("model", ctypes.c_uint64), ("user", ctypes.c_uint64),
+                ("chat", ctypes.c_uint64), ("parent", ctypes.c_uint64)]
+
+
+class wkv7_session_stats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "hits", "news", "restarts_edit", "restarts_parent",
+        "restarts_evicted", "resets", "forks", "hibernates", "resumes",
+        "drops")] + [(n, ctypes.c_int32) for n in (
+            "active", "parked_device", "parked_host", "free_host_images")]
 
 WKV7_IMAGE_MAGIC = b"WKV7SLOT"
 WKV7_IMAGE_VERSION = 1
@@ -134,6 +158,23 @@ lib.wkv7_migrate.argtypes = [_vp, _pi32, _vp, _pi32, _i32, _vp]
 lib.wkv7_image_header_init.restype = _i32
 lib.wkv7_image_header_init.argtypes = [ctypes.POINTER(wkv7_image_header),
                                        _i32, _i32, _i32]
+lib.wkv7_sessions_create.restype = _i32
+lib.wkv7_sessions_create.argtypes = [_vp, _i32, _i32, _i32, ctypes.POINTER(_vp)]
+lib.wkv7_sessions_destroy.restype = _i32
+lib.wkv7_sessions_destroy.argtypes = [_vp]
+lib.wkv7_session_begin.restype = _i32
+lib.wkv7_session_begin.argtypes = [_vp, ctypes.POINTER(wkv7_turn_key), _pi32,
+                                   _i64, _vp, _pi32,
+                                   ctypes.POINTER(_i64), _pi32]
+lib.wkv7_session_end.restype = _i32
+lib.wkv7_session_end.argtypes = [_vp, _i32, ctypes.c_uint64, _pi32, _i64]
+lib.wkv7_session_abort.restype = _i32
+lib.wkv7_session_abort.argtypes = [_vp, _i32]
+lib.wkv7_session_drop_chat.restype = _i32
+lib.wkv7_session_drop_chat.argtypes = [_vp, ctypes.c_uint64, ctypes.c_uint64,
+                                       ctypes.c_uint64]
+lib.wkv7_sessions_stats.restype = _i32
+lib.wkv7_sessions_stats.argtypes = [_vp, ctypes.POINTER(wkv7_session_stats)]
 lib.wkv7_image_header_check.restype = _i32
 lib.wkv7_image_header_check.argtypes = [ctypes.POINTER(wkv7_image_header),
                                         _i32, _i32]
@@ -285,6 +326,52 @@ def wkv7_image_header_init(H: int, N: int, n_slots: int) -> wkv7_image_header:
 
 def wkv7_image_header_check(hdr: wkv7_image_header, H: int, N: int) -> None:
     _check(lib.wkv7_image_header_check(ctypes.byref(hdr), H, N))
+
+
+def wkv7_sessions_create(pool: Optional[int], dry_slots: int = 0,
+                         host_images: int = 0, flags: int = 0) -> int:
+    out = _vp()
+    _check(lib.wkv7_sessions_create(pool, dry_slots, host_images, flags,
+                                    ctypes.byref(out)))
+    return out.value
+
+
+def wkv7_sessions_destroy(s: int) -> None:
+    _check(lib.wkv7_sessions_destroy(s))
+
+
+def wkv7_session_begin(s: int, model: int, user: int, chat: int, parent: int,
+                       tokens, stream=None):
+    """Returns (slot, n_reuse, outcome)."""
+    t = _ids(tokens)
+    key = wkv7_turn_key(model, user, chat, parent)
+    slot, reuse, oc = _i32(), _i64(), _i32()
+    # NULL (the null stream) unless a stream is given: a host-only manager
+    # must not touch the GPU
+    hs = None if stream is None else _stream(stream)
+    _check(lib.wkv7_session_begin(s, ctypes.byref(key), _iptr(t), t.size, hs,
+                                  ctypes.byref(slot), ctypes.byref(reuse),
+                                  ctypes.byref(oc)))
+    return slot.value, reuse.value, oc.value
+
+
+def wkv7_session_end(s: int, slot: int, message: int, tokens) -> None:
+    t = _ids(tokens)
+    _check(lib.wkv7_session_end(s, slot, message, _iptr(t), t.size))
+
+
+def wkv7_session_abort(s: int, slot: int) -> None:
+    _check(lib.wkv7_session_abort(s, slot))
+
+
+def wkv7_session_drop_chat(s: int, model: int, user: int, chat: int) -> None:
+    _check(lib.wkv7_session_drop_chat(s, model, user, chat))
+
+
+def wkv7_sessions_stats(s: int) -> dict:
+    out = wkv7_session_stats()
+    _check(lib.wkv7_sessions_stats(s, ctypes.byref(out)))
+    return {n: getattr(out, n) for n, _ in wkv7_session_stats._fields_}
 
 
 def wkv7_snapshot(pool: int, slot: int, dst, stream=None) -> None:
