@@ -22,9 +22,8 @@ element, for one head and one timestep:
     S_t[i][j] = S_{t-1}[i][j] * w_t[j] + sa[i] * b_t[j] + v_t[i] * k_t[j]
     o_t[i]  = sum_j S_t[i][j] * r_t[j]              (uses the updated state)
 
-The state has the same size for every sequence length (same section: "fixed
-size regardless of sequence length"). Heads, sequences and slots are
-independent. Nothing is clamped: w is used exactly as given.
+The state has the same size for every sequence length (the same section
+says so). Heads, sequences and slots are independent. Nothing is clamped: w is used exactly as given.
 
 Everything is float64; inputs are the exact dtype-rounded values the device
 receives, upcast. Loops run over timesteps in Python and are vectorised over
