@@ -411,6 +411,66 @@ def run_mixed(steps: int = 10, warmup: int = 2, seed: int = 3):
     }
 
 
+INT8_MFMA_PEAK_TOPS = 5000.0
+
+
+def run_q8_proj(steps: int = 50, warmup: int = 5, seed: int = 5):
+    """The INT8 projections upstream of the recurrence in decode: the six
+    weight matrices r, w, k, v, a, b of a C=2048 layer stacked into one
+    [12288, 2048] int8 matrix (quantized once, outside the timed region);
+    a step quantizes the B input rows (bf16) and runs the INT8 product.
+    B=256 (the decode batch) and B=1 (one sequence's matrix-vector
+    product), each timed with one event pair over K steps."""
+    import torch
+    from linear_attention_rnn_amd import wkv7 as W
+
+    dev = torch.device("cuda:0")
+    C = 2048
+    O = 6 * C
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    w = (torch.randn((O, C), device=dev, generator=gen) / C ** 0.5).to(
+        torch.bfloat16)
+    wq = torch.empty((O, C), dtype=torch.int8, device=dev)
+    ws = torch.empty(O, dtype=torch.float32, device=dev)
+    W.wkv7_q8_quantize(w, wq, ws)
+    stream = torch.cuda.current_stream()
+    out = {}
+    for B in (256, 1):
+        xs = [torch.randn((B, C), device=dev, generator=gen).to(torch.bfloat16)
+              for _ in range(8)]
+        xq = torch.empty((B, C), dtype=torch.int8, device=dev)
+        xsc = torch.empty(B, dtype=torch.float32, device=dev)
+        y = torch.empty((B, O), dtype=torch.float32, device=dev)
+
+        def step(i):
+            W.wkv7_q8_quantize(xs[i % 8], xq, xsc, stream=stream)
+            W.wkv7_q8_matmul(wq, ws, xq, xsc, y, stream=stream)
+
+        for i in range(warmup):
+            step(i)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(steps):
+            step(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / steps * 1e3
+        ops = 2.0 * B * O * C
+        nbytes = O * C + 4 * O + B * C * 2 + B * C + 4 * B + 4 * B * O
+        out[f"b{B}"] = {
+            "us_per_step": us, "tops": ops / (us * 1e-6) / 1e12,
+            "mfma_frac": ops / (us * 1e-6) / 1e12 / INT8_MFMA_PEAK_TOPS,
+            "hbm_gbs": nbytes / (us * 1e-6) / 1e9,
+            "hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "bytes_per_step": nbytes,
+        }
+    return {"workload": "q8_proj_c2048_stacked6_bf16in", "peak_int8_tops":
+            INT8_MFMA_PEAK_TOPS, **out, "steps": steps, "warmup": warmup}
+
+
 def cpu_baseline(seconds: float, seed: int = 1):
     """The float64 oracle on a bounded sample: whole decode steps of the same
     256-slot, H=32 batch, repeated until `seconds` have passed."""
@@ -445,7 +505,8 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--legs",
-                    default="decode,prefill,decode_large,prefill_ragged,mixed",
+                    default="decode,prefill,decode_large,prefill_ragged,mixed,"
+                            "q8_proj",
                     help="comma list of legs to run (profiling one kernel)")
     ap.add_argument("--prefill-steps", type=int, default=10)
     args = ap.parse_args(argv)
@@ -468,6 +529,9 @@ def main(argv=None) -> int:
     if legs == {"prefill"}:
         print(json.dumps({"prefill": run_prefill(args.prefill_steps, 2)}),
               flush=True)
+        return 0
+    if legs == {"q8_proj"}:
+        print(json.dumps({"q8_proj": run_q8_proj()}), flush=True)
         return 0
     d = run_decode(args.steps, args.warmup)
     achieved = d["bytes_per_launch"] / (d["kernel_ms"] * 1e-3) / 1e9
@@ -512,6 +576,8 @@ def main(argv=None) -> int:
         line["prefill_ragged"] = run_prefill_ragged()
     if "mixed" in legs:
         line["mixed"] = run_mixed()
+    if "q8_proj" in legs:
+        line["q8_proj"] = run_q8_proj()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(line), flush=True)

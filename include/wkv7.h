@@ -274,6 +274,38 @@ wkv7_status wkv7_image_header_init(wkv7_image_header* hdr, int32_t H,
 wkv7_status wkv7_image_header_check(const wkv7_image_header* hdr, int32_t H,
                                     int32_t N);
 
+/* INT8 projections — the step upstream of the recurrence in decode (page
+ * "RWKV-X Architecture", section "INT8 Quantization"): each row of a linear
+ * projection's weights [out][in] is quantized symmetrically with its own
+ * scale, the input is quantized once, and every output is an integer dot
+ * product times the two scales.
+ *
+ * quantize — per-row symmetric INT8 codes of x [rows][cols] (device, dtype
+ * WKV7_F32 or WKV7_BF16, row-major): scale[r] = max_c |x[r][c]| / 127 and
+ * q[r][c] = round(x[r][c] / scale[r]), both in IEEE float32 with C roundf
+ * rounding (halves away from zero), so the codes are reproducible bit for
+ * bit; a row of zeros gets scale 0 and codes 0. q (int8 [rows][cols]) and
+ * scale (float32 [rows]) are device arrays owned by the caller. Inputs must
+ * be finite (other values give unspecified codes). Used for weight rows
+ * once and for the input rows (one per token) of every call. */
+wkv7_status wkv7_q8_quantize(const void* x, int32_t dtype, int64_t rows,
+                             int64_t cols, int8_t* q, float* scale,
+                             void* stream);
+
+/* matmul — y[b][o] = (sum_i wq[o][i] * xq[b][i]) * w_scale[o] * x_scale[b]
+ * for B input rows (tokens) and `out` output rows: wq int8 [out][in] and
+ * w_scale float32 [out] from wkv7_q8_quantize of the weights, xq int8
+ * [B][in] and x_scale float32 [B] from wkv7_q8_quantize of the inputs, y
+ * float32 [B][out]; all device memory owned by the caller, wq, w_scale, xq
+ * and y 16-byte aligned. The integer sums are exact (int32). in must be a
+ * multiple of 64 and out of 16 (else WKV7_ERR_UNSUPPORTED). Stacking the
+ * weights of several projections (r, w, k, v, a, b) into one [6C][C] matrix
+ * runs them in one call. */
+wkv7_status wkv7_q8_matmul(const int8_t* wq, const float* w_scale,
+                           int64_t out, int64_t in, const int8_t* xq,
+                           const float* x_scale, int64_t B, float* y,
+                           void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,6 +28,20 @@ struct SeqArgs {
   float* o;                    // [T_tot][H][N]
 };
 
+// Workgroup barrier that orders LDS only. __syncthreads() also waits for the
+// wavefront's outstanding global loads and stores (s_waitcnt vmcnt(0)),
+// which would stall loads prefetched just before the barrier; here only this
+// wavefront's LDS operations must be complete (lgkmcnt(0); the vmcnt and
+// expcnt fields of the s_waitcnt immediate are left at their maxima). The
+// empty asm statements keep the compiler from moving memory accesses across
+// the barrier. Only for kernels whose waves share data through LDS alone.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Sequential kernel: one wavefront per (sequence, head), state in registers.
 hipError_t launch_seq(const SeqArgs& args, hipStream_t stream);
 
@@ -46,6 +60,16 @@ hipError_t launch_chunked_p(const SeqArgs& args, hipStream_t stream);
 hipError_t launch_copy_slots(const float* src_pool, float* dst_pool,
                              size_t slot_floats, const int32_t* pairs,
                              int32_t n, hipStream_t stream);
+// INT8 per-row quantization of x [rows][cols] (fp32 or bf16) into codes q
+// and float32 scales, and the INT8 product y[B][O] of codes wq [O][I] with
+// codes xq [B][I] (I % 64 == 0, O % 16 == 0).
+hipError_t launch_q8_quantize(const void* x, int dtype, int64_t rows,
+                              int64_t cols, int8_t* q, float* scale,
+                              hipStream_t stream);
+hipError_t launch_q8_matmul(const int8_t* wq, const float* ws, int64_t O,
+                            int64_t I, const int8_t* xq, const float* xs,
+                            int64_t B, float* y, hipStream_t stream);
+
 // Zero-fill n slots listed (device int32) in `ids`.
 hipError_t launch_zero_slots(float* pool, size_t slot_floats,
                              const int32_t* ids, int32_t n,

@@ -1,0 +1,305 @@
+// INT8 per-row symmetric quantization and the INT8 matrix product of the
+// projections that feed the recurrence (page "RWKV-X Architecture",
+// section "INT8 Quantization": each weight row gets the scale max|row|/127
+// and codes round(w / scale); the input is quantized once and every output
+// row is an integer dot product, rescaled).
+//
+// Quantization decides integers in float32 exactly as single-precision C
+// would (IEEE division, roundf: halves away from zero; an all-zero row has
+// scale 0 and codes 0), so codes and scales are reproducible bit for bit.
+//
+// The product y[b][o] = (sum_i wq[o][i] xq[b][i]) * ws[o] * xs[b] runs on
+// v_mfma_i32_16x16x64_i8 with exact int32 accumulation. A workgroup of four
+// wavefronts owns 64 output rows and up to 128 tokens. k advances in
+// super-chunks of 256: the tokens' codes go through two LDS buffers (shared
+// by the four wavefronts), each wavefront holds its 16 weight rows'
+// fragments in registers and reuses each for 8 token tiles, and the next
+// super-chunk's codes and weights are loaded while the current one is
+// multiplied (one barrier per super-chunk). Weight codes are read from HBM
+// once per token block.
+//
+// MFMA operands: lane 16 g + n supplies row n of its operand with 16 bytes
+// for k = kb + 16 g .. kb + 16 g + 15 (the same k assignment for both
+// operands, so the sum is over every k once); the result lane holds
+// C[4 g + r][n].
+
+#include "internal.h"
+#include "../../include/wkv7.h"
+
+namespace wkv7 {
+namespace {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------- quantization: one wavefront per row ----------------
+
+template <int DT> struct Elem;
+template <> struct Elem<WKV7_F32> {
+  typedef float T;
+  __device__ static float get(const T* p, int64_t i) { return p[i]; }
+  // 8 consecutive values (32 bytes)
+  __device__ static void get8(const T* p, float v[8]) {
+    const float4 a = reinterpret_cast<const float4*>(p)[0];
+    const float4 b = reinterpret_cast<const float4*>(p)[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+};
+template <> struct Elem<WKV7_BF16> {
+  typedef uint16_t T;
+  __device__ static float get(const T* p, int64_t i) {
+    return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
+  }
+  // 8 consecutive values (16 bytes)
+  __device__ static void get8(const T* p, float v[8]) {
+    const uint4 a = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+};
+
+__device__ __forceinline__ float wave_max_abs(float m) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  return m;
+}
+
+__device__ __forceinline__ uint32_t code(float x, float s) {
+  const float v = s > 0.f ? roundf(x / s) : 0.f;   // IEEE divide, roundf
+  return static_cast<uint32_t>(static_cast<int>(v)) & 0xffu;
+}
+
+// One wavefront per row. Rows whose length is a multiple of 8 with 16-byte
+// aligned starts (VEC) move 8 values per lane and load; rows of at most
+// 4096 such values are read once, all loads issued together, and quantized
+// from registers. Other rows take two passes, one value at a time.
+constexpr int kMaxCh = 8;        // 8 x 512 = 4096 values per row in registers
+
+template <int DT>
+__device__ __forceinline__ void quantize_row_regs(
+    const typename Elem<DT>::T* xr, int64_t cols, int8_t* qr, float* srow,
+    int lane) {
+  using E = Elem<DT>;
+  const int nch = static_cast<int>((cols + 511) / 512);
+  float v[kMaxCh][8];
+  float m = 0.f;
+#pragma unroll
+  for (int c = 0; c < kMaxCh; ++c) {
+    const int64_t i = 512 * c + 8 * lane;
+    if (c < nch && i < cols) {
+      E::get8(xr + i, v[c]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[c][e] = 0.f;
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < kMaxCh; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[c][e]));
+  m = wave_max_abs(m);
+  const float s = m / 127.0f;                 // IEEE float32 division
+  if (lane == 0) *srow = s;
+#pragma unroll
+  for (int c = 0; c < kMaxCh; ++c) {
+    const int64_t i = 512 * c + 8 * lane;
+    if (c < nch && i < cols) {
+      uint2 packed;
+      packed.x = code(v[c][0], s) | code(v[c][1], s) << 8 |
+                 code(v[c][2], s) << 16 | code(v[c][3], s) << 24;
+      packed.y = code(v[c][4], s) | code(v[c][5], s) << 8 |
+                 code(v[c][6], s) << 16 | code(v[c][7], s) << 24;
+      *reinterpret_cast<uint2*>(qr + i) = packed;
+    }
+  }
+}
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(256)
+void quantize_rows_kernel(const typename Elem<DT>::T* __restrict__ x,
+                          int64_t rows, int64_t cols, int8_t* __restrict__ q,
+                          float* __restrict__ scale) {
+  using E = Elem<DT>;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const typename E::T* xr = x + row * cols;
+  int8_t* qr = q + row * cols;
+  if (VEC) {
+    quantize_row_regs<DT>(xr, cols, qr, scale + row, lane);
+    return;
+  }
+  float m = 0.f;
+  for (int64_t i = lane; i < cols; i += 64) m = fmaxf(m, fabsf(E::get(xr, i)));
+  m = wave_max_abs(m);
+  const float s = m / 127.0f;                 // IEEE float32 division
+  if (lane == 0) scale[row] = s;
+  for (int64_t i = lane; i < cols; i += 64)
+    qr[i] = static_cast<int8_t>(code(E::get(xr, i), s));
+}
+
+// ---------------- INT8 product on MFMA ----------------
+
+constexpr int kRowsWG = 64;      // output rows per workgroup (16 per wave)
+constexpr int kTokWG = 128;      // tokens per workgroup (8 tiles of 16)
+constexpr int kKS = 256;         // k per super-chunk (4 MFMA k-steps)
+constexpr int kPitch = kKS + 16; // LDS bytes per token row (padded)
+
+__global__ __launch_bounds__(256)
+void q8_matmul_kernel(const int8_t* __restrict__ wq,
+                      const float* __restrict__ ws, int64_t O, int64_t I,
+                      const int8_t* __restrict__ xq,
+                      const float* __restrict__ xs, int64_t B,
+                      float* __restrict__ y) {
+  __shared__ __attribute__((aligned(16))) int8_t xl[2][kTokWG * kPitch];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int g = lane >> 4;
+  const int n = lane & 15;
+  const int64_t o0 = static_cast<int64_t>(blockIdx.x) * kRowsWG + 16 * wv;
+  const int64_t b0 = static_cast<int64_t>(blockIdx.y) * kTokWG;
+  const bool rows_ok = o0 < O;             // O % 16 == 0: all 16 rows or none
+  // Loads go through buffer resources sized to the arrays: a token past B or
+  // a row past O reads as zeros, with no branch. Within the last (partial)
+  // super-chunk, k-steps past I are zeroed on the weight side, so whatever
+  // the token side reads there contributes 0.
+  const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int8_t*>(xq), 0, static_cast<int>(B * I), 0x00020000);
+  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int8_t*>(wq), 0, static_cast<int>(O * I), 0x00020000);
+  // staging: thread t copies 128 bytes (8 x 16) of token t / 2's super-chunk
+  const int st_tok = tid >> 1;
+  const int st_off = 128 * (tid & 1);
+  const int xoff = static_cast<int>((b0 + st_tok) * I) + st_off;
+  // weight fragment of k-step j in a super-chunk: bytes kb + 64 j + 16 g
+  const int woff = static_cast<int>((o0 + n) * I) + 16 * g;
+  const int64_t n_sc = (I + kKS - 1) / kKS;    // I % 64 == 0
+  auto steps_of = [&](int64_t sc) {
+    return static_cast<int>(min<int64_t>(4, (I - sc * kKS) / 64));
+  };
+
+  i32x4 acc[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) acc[t] = i32x4{0, 0, 0, 0};
+
+  i32x4 xr[8], wcur[4], wnxt[4];
+  auto load_x = [&](int64_t kb) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      xr[e] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(
+          xres, xoff + static_cast<int>(kb) + 16 * e, 0, 0));
+  };
+  auto load_w = [&](i32x4* w, int64_t kb, int steps) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const i32x4 v = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(
+          wres, woff + static_cast<int>(kb) + 64 * j, 0, 0));
+      w[j] = j < steps ? v : i32x4{0, 0, 0, 0};
+    }
+  };
+  auto store_x = [&](int buf) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      *reinterpret_cast<i32x4*>(&xl[buf][st_tok * kPitch + st_off + 16 * e]) =
+          xr[e];
+  };
+
+  // prologue: super-chunk 0 staged, super-chunk 1 in flight
+  load_x(0);
+  load_w(wcur, 0, steps_of(0));
+  store_x(0);
+  if (n_sc > 1) {
+    load_x(kKS);
+    load_w(wnxt, kKS, steps_of(1));
+  }
+  lds_barrier();
+  for (int64_t sc = 0; sc < n_sc; ++sc) {
+    const int buf = static_cast<int>(sc & 1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const i32x4 xf = *reinterpret_cast<const i32x4*>(
+            &xl[buf][(16 * t + n) * kPitch + 64 * j + 16 * g]);
+        acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wcur[j], xf, acc[t],
+                                                       0, 0, 0);
+        // keeps each accumulator in its own AGPRs across the loop (without
+        // it the compiler rotates all 32 accumulator registers every pass)
+        asm volatile("" : "+a"(acc[t]));
+      }
+    }
+    if (sc + 1 < n_sc) {
+      store_x(buf ^ 1);                    // buffer read two steps ago
+#pragma unroll
+      for (int j = 0; j < 4; ++j) wcur[j] = wnxt[j];
+      if (sc + 2 < n_sc) {
+        load_x((sc + 2) * kKS);
+        load_w(wnxt, (sc + 2) * kKS, steps_of(sc + 2));
+      }
+    }
+    lds_barrier();                         // loads for sc + 2 stay in flight
+  }
+  if (!rows_ok) return;
+  // lane (g, n) of tile t: rows o0 + 4 g + r, token b0 + 16 t + n
+  const float4 wsc = *reinterpret_cast<const float4*>(ws + o0 + 4 * g);
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int64_t b = b0 + 16 * t + n;
+    if (b >= B) continue;
+    const float sx = xs[b];
+    float4 out;
+    out.x = static_cast<float>(acc[t][0]) * (wsc.x * sx);
+    out.y = static_cast<float>(acc[t][1]) * (wsc.y * sx);
+    out.z = static_cast<float>(acc[t][2]) * (wsc.z * sx);
+    out.w = static_cast<float>(acc[t][3]) * (wsc.w * sx);
+    *reinterpret_cast<float4*>(y + b * O + o0 + 4 * g) = out;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_q8_quantize(const void* x, int dtype, int64_t rows,
+                              int64_t cols, int8_t* q, float* scale,
+                              hipStream_t stream) {
+  if (rows <= 0) return hipSuccess;
+  const int64_t blocks = (rows + 3) / 4;
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  dim3 grid(static_cast<unsigned>(blocks)), block(256);
+  // 8 values per lane, the whole row in registers: whole 16-byte groups on
+  // every row and at most 4096 values
+  const size_t esz = dtype == WKV7_BF16 ? 2 : 4;
+  const bool vec = cols % 8 == 0 && cols <= 512 * kMaxCh &&
+                   reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(q) % 8 == 0 &&
+                   (cols * esz) % 16 == 0;
+  if (dtype == WKV7_BF16) {
+    const uint16_t* xb = static_cast<const uint16_t*>(x);
+    if (vec) hipLaunchKernelGGL((quantize_rows_kernel<WKV7_BF16, true>), grid, block, 0, stream, xb, rows, cols, q, scale);
+    else hipLaunchKernelGGL((quantize_rows_kernel<WKV7_BF16, false>), grid, block, 0, stream, xb, rows, cols, q, scale);
+  } else {
+    const float* xf = static_cast<const float*>(x);
+    if (vec) hipLaunchKernelGGL((quantize_rows_kernel<WKV7_F32, true>), grid, block, 0, stream, xf, rows, cols, q, scale);
+    else hipLaunchKernelGGL((quantize_rows_kernel<WKV7_F32, false>), grid, block, 0, stream, xf, rows, cols, q, scale);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_q8_matmul(const int8_t* wq, const float* ws, int64_t O,
+                            int64_t I, const int8_t* xq, const float* xs,
+                            int64_t B, float* y, hipStream_t stream) {
+  if (O <= 0 || B <= 0) return hipSuccess;
+  const int64_t gx = (O + kRowsWG - 1) / kRowsWG;
+  const int64_t gy = (B + kTokWG - 1) / kTokWG;
+  if (gx > 0x7fffffff || gy > 65535) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(q8_matmul_kernel,
+                     dim3(static_cast<unsigned>(gx), static_cast<unsigned>(gy)),
+                     dim3(256), 0, stream, wq, ws, O, I, xq, xs, B, y);
+  return hipGetLastError();
+}
+
+}  // namespace wkv7

@@ -623,6 +623,55 @@ wkv7_status wkv7_migrate(wkv7_pool* src, const int32_t* src_ids,
   return stage_commit(stage, hs);
 }
 
+wkv7_status wkv7_q8_quantize(const void* x, int32_t dtype, int64_t rows,
+                             int64_t cols, int8_t* q, float* scale,
+                             void* stream) {
+  g_last_error.clear();
+  if (dtype != WKV7_F32 && dtype != WKV7_BF16)
+    return fail(WKV7_ERR_UNSUPPORTED, "dtype %d unsupported", dtype);
+  if (rows < 0 || cols < 1)
+    return fail(WKV7_ERR_INVALID_ARG, "rows=%lld must be >= 0 and cols=%lld >= 1",
+                static_cast<long long>(rows), static_cast<long long>(cols));
+  if (rows == 0) return WKV7_OK;
+  if (!x || !q || !scale)
+    return fail(WKV7_ERR_INVALID_ARG, "x, q and scale must not be NULL");
+  hipError_t e = wkv7::launch_q8_quantize(x, dtype, rows, cols, q, scale,
+                                          static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail_hip(e, "quantize launch");
+  return WKV7_OK;
+}
+
+wkv7_status wkv7_q8_matmul(const int8_t* wq, const float* w_scale,
+                           int64_t out, int64_t in, const int8_t* xq,
+                           const float* x_scale, int64_t B, float* y,
+                           void* stream) {
+  g_last_error.clear();
+  if (out < 0 || in < 1 || B < 0)
+    return fail(WKV7_ERR_INVALID_ARG, "out=%lld, in=%lld, B=%lld",
+                static_cast<long long>(out), static_cast<long long>(in),
+                static_cast<long long>(B));
+  if (in % 64 != 0 || out % 16 != 0)
+    return fail(WKV7_ERR_UNSUPPORTED,
+                "q8 product needs in %% 64 == 0 and out %% 16 == 0 "
+                "(in=%lld, out=%lld)", static_cast<long long>(in),
+                static_cast<long long>(out));
+  if (out == 0 || B == 0) return WKV7_OK;
+  if (out * in >= (int64_t(1) << 31) || B * in >= (int64_t(1) << 31))
+    return fail(WKV7_ERR_UNSUPPORTED,
+                "q8 product operands must each be under 2 GiB of codes");
+  const void* ptrs[5] = {wq, w_scale, xq, x_scale, y};
+  const char* names[5] = {"wq", "w_scale", "xq", "x_scale", "y"};
+  for (int i = 0; i < 5; ++i) {
+    if (!ptrs[i]) return fail(WKV7_ERR_INVALID_ARG, "%s is NULL", names[i]);
+    if (i != 3 && !aligned16(ptrs[i]))
+      return fail(WKV7_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[i]);
+  }
+  hipError_t e = wkv7::launch_q8_matmul(wq, w_scale, out, in, xq, x_scale, B,
+                                        y, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail_hip(e, "q8 product launch");
+  return WKV7_OK;
+}
+
 wkv7_status wkv7_image_header_init(wkv7_image_header* hdr, int32_t H,
                                    int32_t N, int32_t n_slots) {
   g_last_error.clear();

@@ -47,7 +47,7 @@ EXPORTS = (
     "wkv7_image_header_init", "wkv7_image_header_check",
     "wkv7_sessions_create", "wkv7_sessions_destroy", "wkv7_session_begin",
     "wkv7_session_end", "wkv7_session_abort", "wkv7_session_drop_chat",
-    "wkv7_sessions_stats",
+    "wkv7_sessions_stats", "wkv7_q8_quantize", "wkv7_q8_matmul",
 )
 
 # session outcomes and flags (include/wkv7_session.h)
@@ -175,6 +175,10 @@ lib.wkv7_session_drop_chat.argtypes = [_vp, ctypes.c_uint64, ctypes.c_uint64,
                                        ctypes.c_uint64]
 lib.wkv7_sessions_stats.restype = _i32
 lib.wkv7_sessions_stats.argtypes = [_vp, ctypes.POINTER(wkv7_session_stats)]
+lib.wkv7_q8_quantize.restype = _i32
+lib.wkv7_q8_quantize.argtypes = [_vp, _i32, _i64, _i64, _vp, _vp, _vp]
+lib.wkv7_q8_matmul.restype = _i32
+lib.wkv7_q8_matmul.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp]
 lib.wkv7_image_header_check.restype = _i32
 lib.wkv7_image_header_check.argtypes = [ctypes.POINTER(wkv7_image_header),
                                         _i32, _i32]
@@ -372,6 +376,23 @@ def wkv7_sessions_stats(s: int) -> dict:
     out = wkv7_session_stats()
     _check(lib.wkv7_sessions_stats(s, ctypes.byref(out)))
     return {n: getattr(out, n) for n, _ in wkv7_session_stats._fields_}
+
+
+def wkv7_q8_quantize(x, q, scale, stream=None, dtype: Optional[int] = None):
+    """Per-row INT8 codes of the 2-D device tensor x into q (int8, same
+    shape) and scale (float32 [rows])."""
+    rows, cols = x.shape
+    code = _dtype_code(x) if dtype is None else dtype
+    _check(lib.wkv7_q8_quantize(_dptr(x), code, rows, cols, _dptr(q),
+                                _dptr(scale), _stream(stream)))
+
+
+def wkv7_q8_matmul(wq, w_scale, xq, x_scale, y, stream=None) -> None:
+    """y[B, out] = INT8 product of codes wq [out, in] and xq [B, in]."""
+    out, inn = wq.shape
+    B = xq.shape[0]
+    _check(lib.wkv7_q8_matmul(_dptr(wq), _dptr(w_scale), out, inn, _dptr(xq),
+                              _dptr(x_scale), B, _dptr(y), _stream(stream)))
 
 
 def wkv7_snapshot(pool: int, slot: int, dst, stream=None) -> None:

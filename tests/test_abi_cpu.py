@@ -20,7 +20,7 @@ def declared_symbols():
         with open(os.path.join(inc, fn)) as f:
             src = f.read()
         src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-        names |= set(re.findall(r"\b(wkv7_[a-z_]+)\s*\(", src))
+        names |= set(re.findall(r"\b(wkv7_[a-z0-9_]+)\s*\(", src))
     return sorted(names)
 
 
@@ -126,4 +126,18 @@ def test_image_header_roundtrip_and_rejections():
     assert e.value.status == W.WKV7_ERR_UNSUPPORTED
     assert W.lib.wkv7_image_header_check(None, 1, 64) == W.WKV7_ERR_INVALID_ARG
     assert W.lib.wkv7_migrate(None, None, None, None, 0, None) == \
+        W.WKV7_ERR_INVALID_ARG
+
+
+def test_q8_rejects_before_device():
+    L = W.lib
+    assert L.wkv7_q8_quantize(None, 0, 2, 4, None, None, None) == \
+        W.WKV7_ERR_INVALID_ARG
+    assert L.wkv7_q8_quantize(None, 9, 2, 4, None, None, None) == \
+        W.WKV7_ERR_UNSUPPORTED
+    assert L.wkv7_q8_quantize(None, 0, -1, 4, None, None, None) == \
+        W.WKV7_ERR_INVALID_ARG
+    assert L.wkv7_q8_matmul(None, None, 16, 100, None, None, 1, None, None) == \
+        W.WKV7_ERR_UNSUPPORTED
+    assert L.wkv7_q8_matmul(None, None, 16, 64, None, None, 1, None, None) == \
         W.WKV7_ERR_INVALID_ARG

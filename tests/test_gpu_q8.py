@@ -1,0 +1,125 @@
+"""INT8 projections on the GPU against the oracle: codes and scales bit for
+bit, products to float32 rounding of the exact integer sums (GPU)."""
+import numpy as np
+import pytest
+import torch
+
+from linear_attention_rnn_amd import wkv7 as W
+from oracle import quantize_rows, q8_matmul
+from tests.gpu_util import DEV, say
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-6      # fp32 conversion of the int32 sums and of the scale product
+
+
+def _rel(got, ref):
+    ref = np.asarray(ref, np.float64)
+    return float(np.max(np.abs(np.asarray(got, np.float64) - ref))
+                 / np.sqrt(np.mean(ref ** 2)))
+
+
+def _quantize_dev(x):
+    q = torch.empty(x.shape, dtype=torch.int8, device=DEV)
+    s = torch.empty(x.shape[0], dtype=torch.float32, device=DEV)
+    W.wkv7_q8_quantize(x, q, s)
+    torch.cuda.synchronize()
+    return q, s
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_quantize_bitexact(dtype):
+    rng = np.random.default_rng(61)
+    x = (rng.standard_normal((37, 193)) *
+         10.0 ** rng.integers(-4, 4, (37, 1))).astype(np.float32)
+    x[3] = 0.0                                   # zero row
+    x[5] = 0.0
+    x[5, 7] = -2.0                               # single entry
+    x[6, :5] = [127.0, 2.5, -2.5, 0.5, -0.5]     # exact halves at scale 1
+    x[6, 5:] = 0.0
+    xt = torch.from_numpy(x).to(dtype)
+    x_in = xt.float().numpy()                    # the values the GPU sees
+    q, s = _quantize_dev(xt.to(DEV))
+    q_ref, s_ref = quantize_rows(x_in)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+    assert list(q_ref[6, :5]) == [127, 3, -3, 1, -1]
+
+
+@pytest.mark.parametrize("O,I,B", [(48, 128, 1), (64, 256, 17), (208, 640, 130),
+                                   (16, 64, 300)])
+def test_matmul_matches_oracle(O, I, B):
+    rng = np.random.default_rng(O + I + B)
+    w = rng.standard_normal((O, I)).astype(np.float32)
+    x = rng.standard_normal((B, I)).astype(np.float32)
+    wq, ws = _quantize_dev(torch.from_numpy(w).to(DEV))
+    xq, xs = _quantize_dev(torch.from_numpy(x).to(DEV))
+    y = torch.full((B, O), float("nan"), dtype=torch.float32, device=DEV)
+    W.wkv7_q8_matmul(wq, ws, xq, xs, y)
+    torch.cuda.synchronize()
+    ref = q8_matmul(wq.cpu().numpy(), ws.cpu().numpy(), xq.cpu().numpy(),
+                    xs.cpu().numpy())
+    e = _rel(y.cpu().numpy(), ref)
+    say(f"q8 matmul O={O} I={I} B={B}: rel err {e:.2e}")
+    assert np.all(np.isfinite(y.cpu().numpy()))
+    assert e < TOL
+
+
+def test_full_size_stacked_projection_sampled():
+    """r,w,k,v,a,b weights of a C=2048 layer stacked into [12288, 2048],
+    bf16, 256 decode tokens: 512 sampled outputs against exact integer dot
+    products; the quantized result stays within 5% rms of the float64
+    product of the unquantized operands."""
+    C, B = 2048, 256
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(62)
+    w = (torch.randn((6 * C, C), device=DEV, generator=gen) / C ** 0.5
+         ).to(torch.bfloat16)
+    x = torch.randn((B, C), device=DEV, generator=gen).to(torch.bfloat16)
+    wq, ws = _quantize_dev(w)
+    xq, xs = _quantize_dev(x)
+    y = torch.empty((B, 6 * C), dtype=torch.float32, device=DEV)
+    W.wkv7_q8_matmul(wq, ws, xq, xs, y)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(63)
+    bs, os_ = rng.integers(0, B, 512), rng.integers(0, 6 * C, 512)
+    wqn, xqn = wq.cpu().numpy(), xq.cpu().numpy()
+    wsn, xsn = ws.cpu().numpy(), xs.cpu().numpy()
+    yn = y.cpu().numpy()
+    ref = np.array([int(np.dot(wqn[o].astype(np.int64), xqn[b].astype(np.int64)))
+                    * float(wsn[o]) * float(xsn[b]) for b, o in zip(bs, os_)])
+    got = yn[bs, os_]
+    e = float(np.max(np.abs(got - ref)) / np.sqrt(np.mean(ref ** 2)))
+    say(f"full-size q8 projection, sampled: rel err {e:.2e}")
+    assert e < TOL
+    wf = w.float().cpu().numpy().astype(np.float64)
+    xf = x.float().cpu().numpy().astype(np.float64)
+    exact = np.array([np.dot(wf[o], xf[b]) for b, o in zip(bs, os_)])
+    qe = float(np.max(np.abs(got - exact)) / np.sqrt(np.mean(exact ** 2)))
+    say(f"  quantization error against the float64 product: {qe:.2e}")
+    assert qe < 0.05
+
+
+def test_q8_errors():
+    q = torch.zeros((16, 64), dtype=torch.int8, device=DEV)
+    s = torch.ones(16, dtype=torch.float32, device=DEV)
+    y = torch.zeros((4, 16), dtype=torch.float32, device=DEV)
+    xq = torch.zeros((4, 64), dtype=torch.int8, device=DEV)
+    xs = torch.ones(4, dtype=torch.float32, device=DEV)
+    L = W.lib
+    assert L.wkv7_q8_matmul(q.data_ptr(), s.data_ptr(), 16, 96, xq.data_ptr(),
+                            xs.data_ptr(), 4, y.data_ptr(), None) == \
+        W.WKV7_ERR_UNSUPPORTED                       # in % 64 != 0
+    assert L.wkv7_q8_matmul(q.data_ptr(), s.data_ptr(), 8, 64, xq.data_ptr(),
+                            xs.data_ptr(), 4, y.data_ptr(), None) == \
+        W.WKV7_ERR_UNSUPPORTED                       # out % 16 != 0
+    assert L.wkv7_q8_matmul(q.data_ptr() + 1, s.data_ptr(), 16, 64,
+                            xq.data_ptr(), xs.data_ptr(), 4, y.data_ptr(),
+                            None) == W.WKV7_ERR_INVALID_ARG   # misaligned
+    assert L.wkv7_q8_matmul(None, s.data_ptr(), 16, 64, xq.data_ptr(),
+                            xs.data_ptr(), 4, y.data_ptr(), None) == \
+        W.WKV7_ERR_INVALID_ARG
+    assert L.wkv7_q8_matmul(None, None, 16, 64, None, None, 0, None, None) == \
+        W.WKV7_OK                                    # B = 0: nothing to do
+    assert L.wkv7_q8_quantize(q.data_ptr(), 5, 1, 1, q.data_ptr(), s.data_ptr(),
+                              None) == W.WKV7_ERR_UNSUPPORTED
+    assert L.wkv7_q8_quantize(None, 0, 0, 4, None, None, None) == W.WKV7_OK
