@@ -283,7 +283,7 @@ def run_decode_large(steps: int = 20, warmup: int = 3, seed: int = 4):
     }
 
 
-def run_prefill_ragged(steps: int = 3, warmup: int = 1, seed: int = 4):
+def run_prefill_ragged(steps: int = 3, warmup: int = 3, seed: int = 4):
     """32 fresh sequences with lengths integer-uniform in [128, 8192], H=64,
     bf16 inputs; one step = reset the 32 slots + one plan forward (timed
     with an event pair around the forward)."""
@@ -527,7 +527,7 @@ def main(argv=None) -> int:
 
     legs = set(args.legs.split(","))
     if legs == {"prefill"}:
-        print(json.dumps({"prefill": run_prefill(args.prefill_steps, 2)}),
+        print(json.dumps({"prefill": run_prefill(args.prefill_steps, 20)}),
               flush=True)
         return 0
     if legs == {"q8_proj"}:
@@ -569,7 +569,7 @@ def main(argv=None) -> int:
         },
     }
     if not args.no_prefill and "prefill" in legs:
-        line["prefill"] = run_prefill(args.prefill_steps, 2)
+        line["prefill"] = run_prefill(args.prefill_steps, 20)
     if "decode_large" in legs:
         line["decode_large"] = run_decode_large()
     if not args.no_prefill and "prefill_ragged" in legs:

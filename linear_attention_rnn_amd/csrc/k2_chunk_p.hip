@@ -332,14 +332,12 @@ __device__ __forceinline__ f16x4 ldh4(const _Float16* m, int pitch, int row,
 
 // Workgroup OR of two flag bits with one barrier: lane 0 of every wave
 // posts its wave's bits; all threads read the eight posts after the barrier.
-// The barrier orders LDS only, so the next chunk's input loads and this
-// chunk's output stores stay in flight across it.
 __device__ __forceinline__ uint32_t barrier_or2(uint32_t* slot, int wv,
                                                 int lane, bool b0, bool b1) {
   const uint32_t m0 = __builtin_amdgcn_ballot_w64(b0) != 0 ? 1u : 0u;
   const uint32_t m1 = __builtin_amdgcn_ballot_w64(b1) != 0 ? 2u : 0u;
   if (lane == 0) slot[wv] = m0 | m1;
-  lds_barrier();
+  __syncthreads();
   uint32_t r = 0;
 #pragma unroll
   for (int w = 0; w < 8; ++w) r |= slot[w];
@@ -476,7 +474,7 @@ void chunk_p_kernel(SeqArgs p) {
       TOT[rg * 64 + j0] = P0[3];
       TOT[rg * 64 + j0 + 1] = P1[3];
     }
-    lds_barrier();                                                // B1
+    __syncthreads();                                              // B1
 
     // ===== interval 1 =====
     bool bad_k = false;
