@@ -147,9 +147,10 @@ void quantize_rows_kernel(const typename Elem<DT>::T* __restrict__ x,
 constexpr int kRowsWG = 64;      // output rows per workgroup (16 per wave)
 constexpr int kTokWG = 128;      // tokens per workgroup (8 tiles of 16)
 constexpr int kKS = 256;         // k per super-chunk (4 MFMA k-steps)
+constexpr int kSCM = 8;          // super-chunks per macro-chunk (2048 k)
 constexpr int kPitch = kKS + 16; // LDS bytes per token row (padded)
 
-__global__ __launch_bounds__(256)
+__global__ __launch_bounds__(256, 2)
 void q8_matmul_kernel(const int8_t* __restrict__ wq,
                       const float* __restrict__ ws, int64_t O, int64_t I,
                       const int8_t* __restrict__ xq,
@@ -165,9 +166,8 @@ void q8_matmul_kernel(const int8_t* __restrict__ wq,
   const int64_t b0 = static_cast<int64_t>(blockIdx.y) * kTokWG;
   const bool rows_ok = o0 < O;             // O % 16 == 0: all 16 rows or none
   // Loads go through buffer resources sized to the arrays: a token past B or
-  // a row past O reads as zeros, with no branch. Within the last (partial)
-  // super-chunk, k-steps past I are zeroed on the weight side, so whatever
-  // the token side reads there contributes 0.
+  // a row past O reads as zeros, with no branch. k-steps past I are zeroed
+  // on the weight side, so whatever the token side reads there adds 0.
   const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<int8_t*>(xq), 0, static_cast<int>(B * I), 0x00020000);
   const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
@@ -176,31 +176,20 @@ void q8_matmul_kernel(const int8_t* __restrict__ wq,
   const int st_tok = tid >> 1;
   const int st_off = 128 * (tid & 1);
   const int xoff = static_cast<int>((b0 + st_tok) * I) + st_off;
-  // weight fragment of k-step j in a super-chunk: bytes kb + 64 j + 16 g
+  // weight fragment of k-step j: bytes kb + 64 j + 16 g of row o0 + n
   const int woff = static_cast<int>((o0 + n) * I) + 16 * g;
   const int64_t n_sc = (I + kKS - 1) / kKS;    // I % 64 == 0
-  auto steps_of = [&](int64_t sc) {
-    return static_cast<int>(min<int64_t>(4, (I - sc * kKS) / 64));
-  };
 
   i32x4 acc[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) acc[t] = i32x4{0, 0, 0, 0};
 
-  i32x4 xr[8], wcur[4], wnxt[4];
+  i32x4 xr[8];
   auto load_x = [&](int64_t kb) {
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       xr[e] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(
           xres, xoff + static_cast<int>(kb) + 16 * e, 0, 0));
-  };
-  auto load_w = [&](i32x4* w, int64_t kb, int steps) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const i32x4 v = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(
-          wres, woff + static_cast<int>(kb) + 64 * j, 0, 0));
-      w[j] = j < steps ? v : i32x4{0, 0, 0, 0};
-    }
   };
   auto store_x = [&](int buf) {
 #pragma unroll
@@ -209,40 +198,46 @@ void q8_matmul_kernel(const int8_t* __restrict__ wq,
           xr[e];
   };
 
-  // prologue: super-chunk 0 staged, super-chunk 1 in flight
   load_x(0);
-  load_w(wcur, 0, steps_of(0));
   store_x(0);
-  if (n_sc > 1) {
-    load_x(kKS);
-    load_w(wnxt, kKS, steps_of(1));
-  }
-  lds_barrier();
-  for (int64_t sc = 0; sc < n_sc; ++sc) {
-    const int buf = static_cast<int>(sc & 1);
+  if (n_sc > 1) load_x(kKS);
+  // macro-chunks of 2048 k: the wavefront's whole weight strip for the
+  // macro-chunk is loaded at once (all 32 fragments in flight together)
+  for (int64_t m0 = 0; m0 < n_sc; m0 += kSCM) {
+    i32x4 wall[kSCM * 4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int f = 0; f < kSCM * 4; ++f) {
+      const int64_t k = (m0 * 4 + f) * 64;     // first k of this k-step
+      const i32x4 v = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(
+          wres, woff + static_cast<int>(k), 0, 0));
+      wall[f] = k < I ? v : i32x4{0, 0, 0, 0};
+    }
+    lds_barrier();                          // super-chunk m0 staged
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const i32x4 xf = *reinterpret_cast<const i32x4*>(
-            &xl[buf][(16 * t + n) * kPitch + 64 * j + 16 * g]);
-        acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wcur[j], xf, acc[t],
-                                                       0, 0, 0);
-        // keeps each accumulator in its own AGPRs across the loop (without
-        // it the compiler rotates all 32 accumulator registers every pass)
-        asm volatile("" : "+a"(acc[t]));
+    for (int q = 0; q < kSCM; ++q) {
+      const int64_t sc = m0 + q;
+      if (sc < n_sc) {
+        const int buf = static_cast<int>(sc & 1);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const i32x4 xf = *reinterpret_cast<const i32x4*>(
+                &xl[buf][(16 * t + n) * kPitch + 64 * j + 16 * g]);
+            acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wall[4 * q + j], xf,
+                                                           acc[t], 0, 0, 0);
+            // keeps each accumulator in its own AGPRs (without it the
+            // compiler rotates all 32 accumulator registers every pass)
+            asm volatile("" : "+a"(acc[t]));
+          }
+        }
+        if (sc + 1 < n_sc) {
+          store_x(buf ^ 1);                 // buffer read two steps ago
+          if (sc + 2 < n_sc) load_x((sc + 2) * kKS);
+          if (q + 1 < kSCM) lds_barrier();  // loads stay in flight
+        }
       }
     }
-    if (sc + 1 < n_sc) {
-      store_x(buf ^ 1);                    // buffer read two steps ago
-#pragma unroll
-      for (int j = 0; j < 4; ++j) wcur[j] = wnxt[j];
-      if (sc + 2 < n_sc) {
-        load_x((sc + 2) * kKS);
-        load_w(wnxt, (sc + 2) * kKS, steps_of(sc + 2));
-      }
-    }
-    lds_barrier();                         // loads for sc + 2 stay in flight
   }
   if (!rows_ok) return;
   // lane (g, n) of tile t: rows o0 + 4 g + r, token b0 + 16 t + n
