@@ -188,3 +188,44 @@ def test_forward_errors_leave_pool_untouched():
                            init.view(torch.int32))
     finally:
         W.wkv7_pool_destroy(pool)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_streams_large_state_nontemporally(dtype):
+    """300 slots x H=64 is 300 MiB of active state, above the 256 MB
+    Infinity Cache: the decode kernel takes its non-temporal variant. Two
+    steps (the second also short sequences of 3 tokens) against the oracle
+    on 24 sampled slots, every head."""
+    n, H = 300, 64
+    rng = np.random.default_rng(71)
+    ids = rng.permutation(320)[:n].astype(np.int32)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(71)
+    init = torch.randn((n, H, 64, 64), device=DEV, generator=gen) * 0.1
+    pool = _pool(320, H)
+    try:
+        W.wkv7_resume(pool, ids, init)
+        torch.cuda.synchronize()
+        samp = rng.choice(n, 24, replace=False)
+        S = init[samp].double().cpu().numpy()
+        for lens in ([1] * n, [3] * n):
+            b = G.make_batch(np.random.default_rng(len(lens) + lens[0]), ids,
+                             lens, H, 64, dtype)
+            o = run_forward(pool, b)
+            x = b.inputs64()
+            cu = b.cu_seqlens
+            err = 0.0
+            for s_i, n_i in enumerate(samp):
+                sl = slice(cu[n_i], cu[n_i + 1])
+                st = {0: S[s_i]}
+                o_ref, st = oracle_forward(st, np.array([0], np.int32),
+                                           np.array([0, lens[n_i]], np.int32),
+                                           {k: x[k][sl] for k in G.NAMES}, H, 64)
+                S[s_i] = st[0]
+                err = max(err, rel_err(o[sl], o_ref))
+            Sg = get_states(pool, ids[samp])
+            err = max(err, rel_err(Sg, S))
+            say(f"large-state decode {dtype} lens {lens[0]}: err {err:.3e}")
+            assert err < tol_for(dtype)
+    finally:
+        W.wkv7_pool_destroy(pool)
