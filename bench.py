@@ -337,12 +337,14 @@ def run_prefill_ragged(steps: int = 3, warmup: int = 3, seed: int = 4):
     }
 
 
-def run_mixed(steps: int = 10, warmup: int = 2, seed: int = 3):
+def run_mixed(steps: int = 10, warmup: int = 2, seed: int = 3,
+              segment_len: int = 0):
     """The 12-layer RWKV-X-0.2B-shaped stack (H=12, one 128-slot pool per
     layer): per layer and step 64 decode tokens plus 4 fresh prefills of
     512, 1024, 2048 and 2048 tokens in one packed call (the prefill slots
     are reset first); fresh inputs per layer and step; one event pair over
-    the K steps of 12 layers."""
+    the K steps of 12 layers. segment_len > 0 turns on segment-parallel
+    prefill with segments of that many tokens."""
     import torch
     import wkv7_inputs as G
     from linear_attention_rnn_amd import wkv7 as W
@@ -364,6 +366,7 @@ def run_mixed(steps: int = 10, warmup: int = 2, seed: int = 3):
         for _ in range(n_layers):
             pool = W.wkv7_pool_create(n_slots, H, N)
             pools.append(pool)
+            W.wkv7_pool_set_option(pool, W.WKV7_OPT_SEGMENT_LEN, segment_len)
             init = torch.randn((64, H, N, N), device=dev, generator=gen) * 0.1
             W.wkv7_resume(pool, dec_ids, init)
             plans.append(W.wkv7_plan_create(pool, ids, cu))
@@ -400,6 +403,7 @@ def run_mixed(steps: int = 10, warmup: int = 2, seed: int = 3):
                    + 4 * H * 2 * 4 * N * N)
     return {
         "workload": "mixed_12layers_h12_64decode_4prefill_bf16in",
+        "segment_len": segment_len,
         "tokens_per_step": T, "ms_per_step": ms,
         "tokens_per_s": T / (ms * 1e-3),
         "layer_tokens_per_s": n_layers * T / (ms * 1e-3),
@@ -409,6 +413,50 @@ def run_mixed(steps: int = 10, warmup: int = 2, seed: int = 3):
                 / HBM_PEAK_GBS},
         "steps": steps, "warmup": warmup,
     }
+
+
+def run_prefill_long(T: int = 32768, H: int = 32, steps: int = 3,
+                     warmup: int = 2, seed: int = 6, segment_len: int = 2048):
+    """One fresh sequence of T tokens at H=32 (the time to prefill one long
+    prompt): H chains only, so most CUs would idle; timed unsplit and with
+    segment-parallel prefill (segments of segment_len tokens), each step a
+    reset + one plan forward timed with an event pair."""
+    import torch
+    from linear_attention_rnn_amd import wkv7 as W
+
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    x = _draw_device(gen, T, H, "bf16", dev)
+    o = torch.empty((T, H, N), dtype=torch.float32, device=dev)
+    ids = np.zeros(1, dtype=np.int32)
+    cu = np.array([0, T], dtype=np.int32)
+    stream = torch.cuda.current_stream()
+    out = {"workload": f"prefill_1x{T}_h{H}_bf16in_f32state",
+           "segment_len": segment_len}
+    for name, seg in (("unsplit", 0), ("segmented", segment_len)):
+        pool = W.wkv7_pool_create(1, H, N)
+        try:
+            W.wkv7_pool_set_option(pool, W.WKV7_OPT_SEGMENT_LEN, seg)
+            plan = W.wkv7_plan_create(pool, ids, cu)
+            times = []
+            for i in range(warmup + steps):
+                W.wkv7_reset(pool, ids, stream=stream)
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                W.wkv7_forward_plan(pool, plan, x["r"], x["w"], x["k"],
+                                    x["v"], x["a"], x["b"], o, stream=stream)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                if i >= warmup:
+                    times.append(e0.elapsed_time(e1))
+            W.wkv7_plan_destroy(plan)
+        finally:
+            W.wkv7_pool_destroy(pool)
+        ms = float(np.mean(times))
+        out[name] = {"ms": ms, "tokens_per_s": T / (ms * 1e-3)}
+    return out
 
 
 INT8_MFMA_PEAK_TOPS = 5000.0
@@ -506,7 +554,7 @@ def main(argv=None) -> int:
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--legs",
                     default="decode,prefill,decode_large,prefill_ragged,mixed,"
-                            "q8_proj",
+                            "prefill_long,q8_proj",
                     help="comma list of legs to run (profiling one kernel)")
     ap.add_argument("--prefill-steps", type=int, default=10)
     args = ap.parse_args(argv)
@@ -532,6 +580,15 @@ def main(argv=None) -> int:
         return 0
     if legs == {"q8_proj"}:
         print(json.dumps({"q8_proj": run_q8_proj()}), flush=True)
+        return 0
+    if legs <= {"mixed", "prefill_long"}:
+        out = {}
+        if "mixed" in legs:
+            out["mixed"] = run_mixed()
+            out["mixed_segmented"] = run_mixed(segment_len=256)
+        if "prefill_long" in legs:
+            out["prefill_long"] = run_prefill_long()
+        print(json.dumps(out), flush=True)
         return 0
     d = run_decode(args.steps, args.warmup)
     achieved = d["bytes_per_launch"] / (d["kernel_ms"] * 1e-3) / 1e9
@@ -576,6 +633,9 @@ def main(argv=None) -> int:
         line["prefill_ragged"] = run_prefill_ragged()
     if "mixed" in legs:
         line["mixed"] = run_mixed()
+        line["mixed_segmented"] = run_mixed(segment_len=256)
+    if not args.no_prefill and "prefill_long" in legs:
+        line["prefill_long"] = run_prefill_long()
     if "q8_proj" in legs:
         line["q8_proj"] = run_q8_proj()
     if not args.no_cpu_baseline:

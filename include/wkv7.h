@@ -85,7 +85,20 @@ enum {
    * scaled by powers of two), about 3e-3 of max|err|/rms(o) on the
    * workloads' inputs. 1: every product uses split bf16 operands, about
    * 1e-4, roughly twice the work. fp32 inputs always use 1. */
-  WKV7_OPT_CHUNK_PRECISE = 2
+  WKV7_OPT_CHUNK_PRECISE = 2,
+  /* Segment-parallel prefill, for batches with few long sequences (the
+   * chunked kernel runs one workgroup per (sequence, head), so a handful of
+   * sequences leaves most of the GPU idle). 0 (default): off. s > 0 (a
+   * multiple of 32, at least 64): on the bf16 fast chunked path, every
+   * sequence of at least 2 s tokens is cut into segments of s tokens that
+   * run in parallel: each segment's transition and zero-start state, a
+   * short scan chaining the segments' states (the recurrence is affine in
+   * the state), then every segment again from its true initial state. About
+   * three times the arithmetic, so it pays only while the (sequence, head)
+   * count is well below the CU count. The split depends on the sequence's
+   * own length only; results agree with the unsplit run to rounding, not
+   * bit for bit. Other chunked paths ignore it. */
+  WKV7_OPT_SEGMENT_LEN = 3
 };
 
 typedef struct wkv7_pool wkv7_pool;

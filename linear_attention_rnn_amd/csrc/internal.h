@@ -17,6 +17,43 @@ struct WorkItem {
   int32_t pad;
 };
 
+// One segment of a sequence split by the segment-parallel prefill (32
+// bytes): its own initial and final state buffers instead of a pool slot.
+struct SegItem {
+  const float* s_in;   // initial state of head 0 (head h at + h*N*N); NULL: 0
+  float* s_out;        // final state of head 0; NULL: not stored
+  int32_t tok0;        // first token row in r..b / o
+  int32_t len;         // number of tokens (>= 1)
+  int32_t flags;       // kSeg* below
+  int32_t pad;
+};
+constexpr int32_t kSegIdentity = 1;   // initial state I (s_in ignored)
+constexpr int32_t kSegZeroV = 2;      // v taken as 0
+constexpr int32_t kSegNoOut = 4;      // o not written
+
+// The carry scan of one split sequence: its segments' blocks follow each
+// other, segment j at base + j * 3 * H*N*N floats, each block holding the
+// segment's transition P, zero-start final state Hs and initial state Sin
+// ([3][H][N][N]). Sin_0 = S0 and Sin_{j+1} = Sin_j P_j + Hs_j (32 bytes).
+struct ScanItem {
+  const float* s0;     // the sequence's initial state, head 0 (a pool slot)
+  float* base;         // block of segment 0
+  int32_t n_seg;
+  int32_t pad[3];
+};
+
+// Where one launch's work description lives on the device: sequential
+// items, all chunked items, and for segment-parallel prefill the segment
+// items of its two kernel phases (the first also runs the chunked sequences
+// that are not split) and the scan items.
+struct Launch {
+  const WorkItem* seq = nullptr;           int32_t n_seq = 0;
+  const WorkItem* chunk_all = nullptr;     int32_t n_chunk_all = 0;
+  const SegItem* phase1 = nullptr;         int32_t n_phase1 = 0;
+  const SegItem* phase3 = nullptr;         int32_t n_phase3 = 0;
+  const ScanItem* scan = nullptr;          int32_t n_scan = 0;
+};
+
 struct SeqArgs {
   float* pool;                 // [n_slots][H][N][N]
   const WorkItem* items;       // device array
@@ -52,8 +89,14 @@ hipError_t launch_chunked(const SeqArgs& args, bool precise,
                           hipStream_t stream);
 
 // Pipelined chunked-prefill kernel for bf16 inputs with an fp16 value side
-// (32-token chunks).
+// (32-token chunks), over pool slots (args.items) or over segments
+// (launch_chunked_p_seg: `segs`, n_items of them; args.items unused).
 hipError_t launch_chunked_p(const SeqArgs& args, hipStream_t stream);
+hipError_t launch_chunked_p_seg(const SeqArgs& args, const SegItem* segs,
+                                hipStream_t stream);
+// Carry scan of split sequences: one workgroup per (sequence, head).
+hipError_t launch_seg_scan(const ScanItem* items, int32_t n_items, int32_t H,
+                           hipStream_t stream);
 
 // Slot copies from src_pool to dst_pool (the same pool for a fork). `pairs`
 // holds n (src slot, dst slot) int32 pairs on the device.

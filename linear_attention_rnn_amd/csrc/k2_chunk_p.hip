@@ -348,7 +348,7 @@ __device__ __forceinline__ uint32_t barrier_or2(uint32_t* slot, int wv,
 // i = 16 vb + n16 of the state, held as S[jt][r] = S[i][16 jt + 4 g + r]).
 __device__ __forceinline__ void exact_chunk(const SeqArgs& p, f32x4* S, int t0,
                                          int n, int h, int vb, int g,
-                                         int n16) {
+                                         int n16, bool zero_v, bool no_out) {
   const uint16_t* R = static_cast<const uint16_t*>(p.r);
   const uint16_t* Wp = static_cast<const uint16_t*>(p.w);
   const uint16_t* K = static_cast<const uint16_t*>(p.k);
@@ -371,7 +371,8 @@ __device__ __forceinline__ void exact_chunk(const SeqArgs& p, f32x4* S, int t0,
         bb[4 * jt + r] = __uint_as_float(static_cast<uint32_t>(B[o]) << 16);
       }
     }
-    const float vi = __uint_as_float(static_cast<uint32_t>(V[base + i]) << 16);
+    const float vi = zero_v ? 0.f
+                            : __uint_as_float(static_cast<uint32_t>(V[base + i]) << 16);
     float sa = 0.f;
 #pragma unroll
     for (int jt = 0; jt < 4; ++jt)
@@ -390,12 +391,15 @@ __device__ __forceinline__ void exact_chunk(const SeqArgs& p, f32x4* S, int t0,
       }
     o += __shfl_xor(o, 16);
     o += __shfl_xor(o, 32);
-    if (g == 0) p.o[base + i] = o;
+    if (g == 0 && !no_out) p.o[base + i] = o;
   }
 }
 
+// SEG = false: items are pool slots (p.items); true: segments (segs) with
+// their own state buffers and flags.
+template <bool SEG>
 __global__ __launch_bounds__(512, 1)
-void chunk_p_kernel(SeqArgs p) {
+void chunk_p_kernel(SeqArgs p, const SegItem* segs) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
   __bf16* GR = reinterpret_cast<__bf16*>(lds + kOffGR);
   __bf16* Ahat = GR;                       // pair [t][j]
@@ -416,8 +420,26 @@ void chunk_p_kernel(SeqArgs p) {
   const int item = blockIdx.x / p.H;
   const int h = blockIdx.x - item * p.H;
   if (item >= p.n_items) return;
-  const WorkItem it = p.items[item];
-  const int nch = (it.len + kL - 1) / kL;
+  int32_t tok0, len, flags = 0;
+  const float* s_in;
+  float* s_out;
+  if (SEG) {
+    const SegItem it = segs[item];
+    tok0 = it.tok0;
+    len = it.len;
+    flags = it.flags;
+    s_in = it.s_in ? it.s_in + static_cast<size_t>(h) * (kN * kN) : nullptr;
+    s_out = it.s_out ? it.s_out + static_cast<size_t>(h) * (kN * kN) : nullptr;
+  } else {
+    const WorkItem it = p.items[item];
+    tok0 = it.tok0;
+    len = it.len;
+    s_out = p.pool + (static_cast<size_t>(it.slot) * p.H + h) * (kN * kN);
+    s_in = s_out;
+  }
+  const bool zero_v = (flags & kSegZeroV) != 0;
+  const bool no_out = (flags & kSegNoOut) != 0;
+  const int nch = (len + kL - 1) / kL;
   const size_t rowstride = static_cast<size_t>(p.H) * kN;
 
   // key-thread ownership: channel pair jp, rows 4 rg .. 4 rg + 3
@@ -427,19 +449,26 @@ void chunk_p_kernel(SeqArgs p) {
   // value-wavefront ownership: state rows i in [16 vb, 16 vb + 16)
   const int vb = wv & 3;
 
-  float* sbase = p.pool + (static_cast<size_t>(it.slot) * p.H + h) * (kN * kN)
-                 + (16 * vb + n16) * kN + 4 * g;
+  const size_t soff = static_cast<size_t>(16 * vb + n16) * kN + 4 * g;
   f32x4 S[4] = {};   // S[jt][r] = S[i = 16 vb + n16][j = 16 jt + 4 g + r]
   if (!is_key) {
+    if (flags & kSegIdentity) {
 #pragma unroll
-    for (int jt = 0; jt < 4; ++jt) {
-      float4 x = *reinterpret_cast<const float4*>(sbase + 16 * jt);
-      S[jt] = f32x4{x.x, x.y, x.z, x.w};
+      for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          S[jt][r] = (16 * vb + n16 == 16 * jt + 4 * g + r) ? 1.f : 0.f;
+    } else if (s_in) {
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) {
+        float4 x = *reinterpret_cast<const float4*>(s_in + soff + 16 * jt);
+        S[jt] = f32x4{x.x, x.y, x.z, x.w};
+      }
     }
   }
 
   Raw nxt;
-  if (is_key) load_raw(nxt, p, it.tok0, min(kL, it.len), h, rg, jp);
+  if (is_key) load_raw(nxt, p, tok0, min(kL, len), h, rg, jp);
 
   // fallback flags, known to every thread: of chunk step-1 (early: its
   // operands; gram: its Gram matrices) and of chunk step-2 (tri: its T)
@@ -456,16 +485,20 @@ void chunk_p_kernel(SeqArgs p) {
     _Float16* LLk = reinterpret_cast<_Float16*>(lds + kOffLL + bK * kLLBytes);
     const _Float16* VOv = reinterpret_cast<const _Float16*>(lds + kOffVO + bV * kVOBytes);
     const _Float16* LLv = reinterpret_cast<const _Float16*>(lds + kOffLL + bV * kLLBytes);
-    const int nV = min(kL, it.len - cV * kL);
-    const int t0K = it.tok0 + cK * kL;
-    const int t0V = it.tok0 + cV * kL;
+    const int nV = min(kL, len - cV * kL);
+    const int t0K = tok0 + cK * kL;
+    const int t0V = tok0 + cV * kL;
 
     // ===== interval 0: key: prefix products of the thread's 4 rows =====
     Raw x;
     float w0[4], w1[4], P0[4], P1[4];
     if (k_on) {
       x = nxt;
-      pad_raw(x, min(kL, it.len - cK * kL), rg);
+      pad_raw(x, min(kL, len - cK * kL), rg);
+      if (zero_v) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x.v[e] = 0u;
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) { w0[e] = bf_lo(x.w[e]); w1[e] = bf_hi(x.w[e]); }
       P0[0] = w0[0]; P1[0] = w1[0];
@@ -536,7 +569,7 @@ void chunk_p_kernel(SeqArgs p) {
       put4h(Vt, kP32, j0 + 1, 4 * rg, f32x4{vt1[0], vt1[1], vt1[2], vt1[3]});
       // next chunk's inputs, in flight from here on
       if (cK + 1 < nch)
-        load_raw(nxt, p, t0K + kL, min(kL, it.len - (cK + 1) * kL), h, rg, jp);
+        load_raw(nxt, p, t0K + kL, min(kL, len - (cK + 1) * kL), h, rg, jp);
     }
     // value side, first half: X and T of chunk cV (or the whole chunk exactly)
     bool v_exact_done = false;
@@ -594,7 +627,7 @@ void chunk_p_kernel(SeqArgs p) {
       }
       if (exact) {
         // the whole chunk token by token
-        exact_chunk(p, S, t0V, nV, h, vb, g, n16);
+        exact_chunk(p, S, t0V, nV, h, vb, g, n16, zero_v, no_out);
         v_exact_done = true;
       }
     }
@@ -686,7 +719,7 @@ void chunk_p_kernel(SeqArgs p) {
         const f32x4 cu = mmah(Uf, ldh8(Mrb, kP32, 16 * tt + n16, 0, g), z);
         const f32x4 cv = mmah(Vf, ldh8(Mrk, kP32, 16 * tt + n16, 0, g), z);
         const int t = 16 * tt + n16;
-        if (t < nV) {
+        if (t < nV && !no_out) {
           float4 ov;
           ov.x = fmaf(cs[0], inv_s, fmaf(cu[0], inv_ux, cv[0]));
           ov.y = fmaf(cs[1], inv_s, fmaf(cu[1], inv_ux, cv[1]));
@@ -713,10 +746,10 @@ void chunk_p_kernel(SeqArgs p) {
     gram_prev = (f3 & 1u) != 0;
   }
 
-  if (!is_key) {
+  if (!is_key && s_out) {
 #pragma unroll
     for (int jt = 0; jt < 4; ++jt)
-      *reinterpret_cast<float4*>(sbase + 16 * jt) =
+      *reinterpret_cast<float4*>(s_out + soff + 16 * jt) =
           make_float4(S[jt][0], S[jt][1], S[jt][2], S[jt][3]);
   }
 }
@@ -727,8 +760,18 @@ hipError_t launch_chunked_p(const SeqArgs& args, hipStream_t stream) {
   if (args.n_items <= 0) return hipSuccess;
   const int64_t blocks = static_cast<int64_t>(args.n_items) * args.H;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(chunk_p_kernel, dim3(static_cast<unsigned>(blocks)),
-                     dim3(512), 0, stream, args);
+  hipLaunchKernelGGL(chunk_p_kernel<false>, dim3(static_cast<unsigned>(blocks)),
+                     dim3(512), 0, stream, args, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_chunked_p_seg(const SeqArgs& args, const SegItem* segs,
+                                hipStream_t stream) {
+  if (args.n_items <= 0) return hipSuccess;
+  const int64_t blocks = static_cast<int64_t>(args.n_items) * args.H;
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(chunk_p_kernel<true>, dim3(static_cast<unsigned>(blocks)),
+                     dim3(512), 0, stream, args, segs);
   return hipGetLastError();
 }
 

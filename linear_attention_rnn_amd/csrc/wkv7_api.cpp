@@ -15,6 +15,7 @@
 #include <cstring>
 #include <new>
 #include <string>
+#include <type_traits>
 #include <vector>
 
 using wkv7::WorkItem;
@@ -78,6 +79,9 @@ struct wkv7_pool {
   size_t slot_floats = 0;
   int64_t prefill_min_len = 64;
   bool chunk_precise = false;
+  int64_t segment_len = 0;           // 0: segment-parallel prefill off
+  float* seg_scratch = nullptr;      // wkv7_forward's segment buffers
+  size_t seg_scratch_floats = 0;
   std::vector<int32_t> free_ids;     // stack; top = back
   std::vector<uint8_t> allocated;
   Stage ring[kRing];
@@ -88,8 +92,9 @@ struct wkv7_pool {
 struct wkv7_plan {
   const wkv7_pool* pool = nullptr;
   int device = 0;
-  WorkItem* items = nullptr;
-  int32_t n_seq_items = 0, n_chunk_items = 0;
+  void* dev = nullptr;               // serialized work description
+  float* scratch = nullptr;          // segment buffers (segment prefill)
+  wkv7::Launch launch;               // pointers into dev
   int64_t T_tot = 0;
 };
 
@@ -200,9 +205,13 @@ bool aligned16(const void* q) {
 // A validated batch: work items with the sequential-kernel items first,
 // then the chunked ones, longest first.
 struct Batch {
-  std::vector<WorkItem> items;
+  std::vector<WorkItem> items;       // sequential items, then all chunked
   int32_t n_seq_items = 0;
   int64_t T_tot = 0;
+  // with segment-parallel prefill on: chunked items run whole (unsplit) and
+  // those split into segments of `seg_len` tokens
+  std::vector<WorkItem> unsplit, split;
+  int64_t seg_len = 0, n_segments = 0;
   int32_t n_chunk_items() const {
     return static_cast<int32_t>(items.size()) - n_seq_items;
   }
@@ -241,7 +250,108 @@ wkv7_status build_batch(const wkv7_pool* p, const int32_t* slot_ids,
                    });
   out->n_seq_items = static_cast<int32_t>(out->items.size());
   out->items.insert(out->items.end(), chunk_items.begin(), chunk_items.end());
+  // segment-parallel prefill: a sequence of at least two segments is split
+  // (the rule looks at the sequence's own length only)
+  out->seg_len = p->segment_len;
+  if (p->segment_len > 0) {
+    for (const WorkItem& it : chunk_items) {
+      if (it.len >= 2 * p->segment_len) {
+        out->split.push_back(it);
+        out->n_segments += (it.len + p->segment_len - 1) / p->segment_len;
+      } else {
+        out->unsplit.push_back(it);
+      }
+    }
+    if (out->split.empty()) out->unsplit.clear();
+  }
   return WKV7_OK;
+}
+
+// Floats of segment buffers a batch needs: P, Hs and Sin per segment-head.
+size_t seg_scratch_floats(const wkv7_pool* p, const Batch& bt) {
+  return static_cast<size_t>(bt.n_segments) * 3 * p->H * wkv7::kN * wkv7::kN;
+}
+
+// Serializes a batch's work for the device: work items, segment items and
+// scan items with their device addresses (pool slots and `scratch`), each
+// section 16-byte aligned. `lay` receives section offsets (bytes, in
+// Launch's pointer fields) and counts.
+std::vector<int32_t> serialize(const wkv7_pool* p, const Batch& bt,
+                               float* scratch, wkv7::Launch* lay) {
+  using wkv7::SegItem;
+  using wkv7::ScanItem;
+  std::vector<int32_t> out;
+  auto put = [&](const void* src, size_t bytes) -> size_t {
+    const size_t off = out.size() * 4;
+    const size_t words = bytes / 4;
+    out.resize(out.size() + words);
+    std::memcpy(out.data() + off / 4, src, bytes);
+    return off;
+  };
+  auto at = [](size_t off) { return reinterpret_cast<const void*>(off); };
+  *lay = wkv7::Launch{};
+  lay->n_seq = bt.n_seq_items;
+  lay->n_chunk_all = bt.n_chunk_items();
+  lay->seq = static_cast<const WorkItem*>(at(put(bt.items.data(),
+                                                 bt.items.size() * sizeof(WorkItem))));
+  lay->chunk_all = lay->seq + bt.n_seq_items;
+  if (bt.split.empty()) return out;
+  const size_t nn = static_cast<size_t>(wkv7::kN) * wkv7::kN;
+  const size_t blk = static_cast<size_t>(p->H) * nn;      // one of P/Hs/Sin
+  std::vector<SegItem> ph1, ph3;
+  std::vector<ScanItem> scan;
+  // chunked sequences that are not split run whole in the first phase's
+  // launch, from and back into their slots (longest first, ahead of the
+  // segments, which are at most seg_len tokens)
+  for (const WorkItem& it : bt.unsplit) {
+    float* slot_state = p->state + static_cast<size_t>(it.slot) * p->slot_floats;
+    ph1.push_back(SegItem{slot_state, slot_state, it.tok0, it.len, 0, 0});
+  }
+  int64_t seg0 = 0;
+  for (const WorkItem& it : bt.split) {
+    const int64_t n_seg = (it.len + bt.seg_len - 1) / bt.seg_len;
+    float* slot_state = p->state + static_cast<size_t>(it.slot) * p->slot_floats;
+    float* base = scratch + static_cast<size_t>(seg0) * 3 * blk;
+    for (int64_t j = 0; j < n_seg; ++j) {
+      float* b = base + static_cast<size_t>(j) * 3 * blk;
+      const int32_t tok0 = it.tok0 + static_cast<int32_t>(j * bt.seg_len);
+      const int32_t len = static_cast<int32_t>(
+          std::min<int64_t>(bt.seg_len, it.len - j * bt.seg_len));
+      if (j + 1 < n_seg) {
+        ph1.push_back(SegItem{nullptr, b + blk, tok0, len, wkv7::kSegNoOut, 0});
+        ph1.push_back(SegItem{nullptr, b, tok0, len,
+                              wkv7::kSegIdentity | wkv7::kSegZeroV |
+                                  wkv7::kSegNoOut, 0});
+      }
+      ph3.push_back(SegItem{b + 2 * blk, j + 1 == n_seg ? slot_state : nullptr,
+                            tok0, len, 0, 0});
+    }
+    scan.push_back(ScanItem{slot_state, base, static_cast<int32_t>(n_seg), {0, 0, 0}});
+    seg0 += n_seg;
+  }
+  lay->n_phase1 = static_cast<int32_t>(ph1.size());
+  lay->n_phase3 = static_cast<int32_t>(ph3.size());
+  lay->n_scan = static_cast<int32_t>(scan.size());
+  lay->phase1 = static_cast<const SegItem*>(at(put(ph1.data(), ph1.size() * sizeof(SegItem))));
+  lay->phase3 = static_cast<const SegItem*>(at(put(ph3.data(), ph3.size() * sizeof(SegItem))));
+  lay->scan = static_cast<const ScanItem*>(at(put(scan.data(), scan.size() * sizeof(ScanItem))));
+  return out;
+}
+
+// Turns the section offsets of `lay` into addresses within `dev`.
+void relocate(wkv7::Launch* lay, const void* dev) {
+  auto fix = [&](auto*& ptr) {
+    using T = std::remove_reference_t<decltype(ptr)>;
+    ptr = reinterpret_cast<T>(static_cast<const char*>(dev) +
+                              reinterpret_cast<uintptr_t>(ptr));
+  };
+  fix(lay->seq);
+  lay->chunk_all = lay->seq + lay->n_seq;
+  if (lay->n_phase3 > 0) {
+    fix(lay->phase1);
+    fix(lay->phase3);
+    fix(lay->scan);
+  }
 }
 
 wkv7_status check_forward_args(int32_t dtype, int64_t T_tot, const void* r,
@@ -260,26 +370,55 @@ wkv7_status check_forward_args(int32_t dtype, int64_t T_tot, const void* r,
   return WKV7_OK;
 }
 
-// Launches the kernels of a batch whose work items are on the device
-// (n_seq sequential-kernel items, then n_chunk chunked ones).
-wkv7_status launch_batch(const wkv7_pool* p, const WorkItem* dev_items,
-                         int32_t n_seq, int32_t n_chunk, int32_t dtype,
-                         const void* r, const void* w, const void* k,
-                         const void* v, const void* a, const void* b, float* o,
-                         hipStream_t hs) {
+// Launches the kernels of a batch whose work description is on the device.
+// Split sequences run segment-parallel on the bf16 fast path (three
+// launches: segment transitions and zero-start states together with the
+// unsplit chunked sequences, the carry scan, the segments' outputs); on the
+// other chunked paths every chunked sequence runs whole.
+wkv7_status launch_batch(const wkv7_pool* p, const wkv7::Launch& L,
+                         int32_t dtype, const void* r, const void* w,
+                         const void* k, const void* v, const void* a,
+                         const void* b, float* o, hipStream_t hs) {
   wkv7::SeqArgs args{p->state, nullptr, 0, p->H, dtype, r, w, k, v, a, b, o};
-  if (n_seq > 0) {
-    args.items = dev_items;
-    args.n_items = n_seq;
+  if (L.n_seq > 0) {
+    args.items = L.seq;
+    args.n_items = L.n_seq;
     hipError_t e = wkv7::launch_seq(args, hs);
     if (e != hipSuccess) return fail_hip(e, "sequential kernel launch");
   }
-  if (n_chunk > 0) {
-    args.items = dev_items + n_seq;
-    args.n_items = n_chunk;
-    hipError_t e = wkv7::launch_chunked(args, p->chunk_precise, hs);
-    if (e != hipSuccess) return fail_hip(e, "chunked kernel launch");
+  const bool segmented = L.n_phase3 > 0 && dtype == WKV7_BF16 &&
+                         !p->chunk_precise;
+  if (!segmented) {
+    if (L.n_chunk_all > 0) {
+      args.items = L.chunk_all;
+      args.n_items = L.n_chunk_all;
+      hipError_t e = wkv7::launch_chunked(args, p->chunk_precise, hs);
+      if (e != hipSuccess) return fail_hip(e, "chunked kernel launch");
+    }
+    return WKV7_OK;
   }
+  args.items = nullptr;
+  args.n_items = L.n_phase1;
+  hipError_t e = wkv7::launch_chunked_p_seg(args, L.phase1, hs);
+  if (e != hipSuccess) return fail_hip(e, "segment transition launch");
+  e = wkv7::launch_seg_scan(L.scan, L.n_scan, p->H, hs);
+  if (e != hipSuccess) return fail_hip(e, "segment scan launch");
+  args.n_items = L.n_phase3;
+  e = wkv7::launch_chunked_p_seg(args, L.phase3, hs);
+  if (e != hipSuccess) return fail_hip(e, "segment prefill launch");
+  return WKV7_OK;
+}
+
+// Makes the pool's segment buffers hold at least `floats` (grow only; the
+// free waits for the device, so earlier work still using them finishes).
+wkv7_status ensure_seg_scratch(wkv7_pool* p, size_t floats) {
+  if (floats <= p->seg_scratch_floats) return WKV7_OK;
+  if (p->seg_scratch) (void)hipFree(p->seg_scratch);
+  p->seg_scratch = nullptr;
+  p->seg_scratch_floats = 0;
+  if (hipMalloc(reinterpret_cast<void**>(&p->seg_scratch), floats * 4) != hipSuccess)
+    return fail(WKV7_ERR_OOM, "segment buffers of %zu bytes", floats * 4);
+  p->seg_scratch_floats = floats;
   return WKV7_OK;
 }
 
@@ -367,6 +506,7 @@ wkv7_status wkv7_pool_destroy(wkv7_pool* p) {
     if (s.ev) (void)hipEventDestroy(s.ev);
   }
   if (p->state) (void)hipFree(p->state);
+  if (p->seg_scratch) (void)hipFree(p->seg_scratch);
   delete p;
   if (e != hipSuccess) return fail_hip(e, "hipDeviceSynchronize(destroy)");
   return WKV7_OK;
@@ -401,6 +541,14 @@ wkv7_status wkv7_pool_set_option(wkv7_pool* p, int32_t opt, int64_t val) {
       return fail(WKV7_ERR_INVALID_ARG, "CHUNK_PRECISE=%lld must be 0 or 1",
                   static_cast<long long>(val));
     p->chunk_precise = val != 0;
+    return WKV7_OK;
+  }
+  if (opt == WKV7_OPT_SEGMENT_LEN) {
+    if (val != 0 && (val < 64 || val % 32 != 0 || val > (int64_t(1) << 30)))
+      return fail(WKV7_ERR_INVALID_ARG,
+                  "SEGMENT_LEN=%lld must be 0 or a multiple of 32, >= 64",
+                  static_cast<long long>(val));
+    p->segment_len = val;
     return WKV7_OK;
   }
   return fail(WKV7_ERR_UNSUPPORTED, "unknown option %d", opt);
@@ -455,14 +603,15 @@ wkv7_status wkv7_forward(wkv7_pool* p, const int32_t* slot_ids,
   DeviceGuard guard(p->device);
   if (!guard.ok) return fail(WKV7_ERR_HIP, "cannot select the pool's device");
   hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (wkv7_status st = ensure_seg_scratch(p, seg_scratch_floats(p, bt))) return st;
+  wkv7::Launch L;
+  const std::vector<int32_t> words = serialize(p, bt, p->seg_scratch, &L);
   const int32_t* dev = nullptr;
   Stage* stage = nullptr;
-  if (wkv7_status st = stage_upload(p, reinterpret_cast<const int32_t*>(bt.items.data()),
-                                    bt.items.size() * 4, hs, &dev, &stage))
+  if (wkv7_status st = stage_upload(p, words.data(), words.size(), hs, &dev, &stage))
     return st;
-  if (wkv7_status st = launch_batch(p, reinterpret_cast<const WorkItem*>(dev),
-                                    bt.n_seq_items, bt.n_chunk_items(), dtype,
-                                    r, w, k, v, a, b, o, hs))
+  relocate(&L, dev);
+  if (wkv7_status st = launch_batch(p, L, dtype, r, w, k, v, a, b, o, hs))
     return st;
   return stage_commit(stage, hs);
 }
@@ -482,24 +631,32 @@ wkv7_status wkv7_plan_create(wkv7_pool* p, const int32_t* slot_ids,
   pl->pool = p;
   pl->device = p->device;
   pl->T_tot = bt.T_tot;
-  pl->n_seq_items = bt.n_seq_items;
-  pl->n_chunk_items = bt.n_chunk_items();
   if (!bt.items.empty()) {
     DeviceGuard guard(p->device);
     if (!guard.ok) { delete pl; return fail(WKV7_ERR_HIP, "cannot select the pool's device"); }
-    const size_t bytes = bt.items.size() * sizeof(WorkItem);
-    hipError_t e = hipMalloc(reinterpret_cast<void**>(&pl->items), bytes);
+    const size_t sf = seg_scratch_floats(p, bt);
+    if (sf > 0 &&
+        hipMalloc(reinterpret_cast<void**>(&pl->scratch), sf * 4) != hipSuccess) {
+      delete pl;
+      return fail(WKV7_ERR_OOM, "segment buffers of %zu bytes for the plan", sf * 4);
+    }
+    const std::vector<int32_t> words = serialize(p, bt, pl->scratch, &pl->launch);
+    const size_t bytes = words.size() * 4;
+    hipError_t e = hipMalloc(&pl->dev, bytes);
     if (e != hipSuccess) {
+      if (pl->scratch) (void)hipFree(pl->scratch);
       delete pl;
       return fail(WKV7_ERR_OOM, "hipMalloc of %zu bytes for the plan failed: %s",
                   bytes, hipGetErrorString(e));
     }
-    e = hipMemcpy(pl->items, bt.items.data(), bytes, hipMemcpyHostToDevice);
+    e = hipMemcpy(pl->dev, words.data(), bytes, hipMemcpyHostToDevice);
     if (e != hipSuccess) {
-      (void)hipFree(pl->items);
+      (void)hipFree(pl->dev);
+      if (pl->scratch) (void)hipFree(pl->scratch);
       delete pl;
       return fail_hip(e, "hipMemcpy(plan)");
     }
+    relocate(&pl->launch, pl->dev);
   }
   *out = pl;
   return WKV7_OK;
@@ -518,21 +675,22 @@ wkv7_status wkv7_forward_plan(wkv7_pool* p, const wkv7_plan* pl, int32_t dtype,
     return fail(WKV7_ERR_INVALID_ARG, "the plan was made for another pool");
   if (wkv7_status st = check_forward_args(dtype, pl->T_tot, r, w, k, v, a, b, o))
     return st;
-  if (pl->n_seq_items + pl->n_chunk_items == 0) return WKV7_OK;
+  if (!pl->dev) return WKV7_OK;
   DeviceGuard guard(p->device);
   if (!guard.ok) return fail(WKV7_ERR_HIP, "cannot select the pool's device");
-  return launch_batch(p, pl->items, pl->n_seq_items, pl->n_chunk_items, dtype,
-                      r, w, k, v, a, b, o, static_cast<hipStream_t>(stream));
+  return launch_batch(p, pl->launch, dtype, r, w, k, v, a, b, o,
+                      static_cast<hipStream_t>(stream));
 }
 
 wkv7_status wkv7_plan_destroy(wkv7_plan* pl) {
   g_last_error.clear();
   if (!pl) return WKV7_OK;
   hipError_t e = hipSuccess;
-  if (pl->items) {
+  if (pl->dev) {
     DeviceGuard guard(pl->device);
     e = hipDeviceSynchronize();
-    (void)hipFree(pl->items);
+    (void)hipFree(pl->dev);
+    if (pl->scratch) (void)hipFree(pl->scratch);
   }
   delete pl;
   if (e != hipSuccess) return fail_hip(e, "hipDeviceSynchronize(plan destroy)");

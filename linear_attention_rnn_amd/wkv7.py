@@ -35,6 +35,7 @@ WKV7_BF16 = 1
 
 WKV7_OPT_PREFILL_MIN_LEN = 1
 WKV7_OPT_CHUNK_PRECISE = 2
+WKV7_OPT_SEGMENT_LEN = 3
 
 # Every symbol include/wkv7.h declares.
 EXPORTS = (

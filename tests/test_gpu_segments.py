@@ -1,0 +1,179 @@
+"""Segment-parallel prefill (GPU): long sequences cut into segments whose
+carries are chained by a scan. Against the oracle, against the unsplit run,
+batch invariance, plans and graph capture."""
+import numpy as np
+import pytest
+import torch
+
+import wkv7_inputs as G
+from linear_attention_rnn_amd import wkv7 as W
+from oracle import wkv7_forward as oracle_forward
+from tests.gpu_util import (DEV, say, set_states, get_states, run_forward,
+                            to_dev, rel_err)
+
+pytestmark = pytest.mark.gpu
+H = 3
+SEG = 256
+GUARD = 1e-2
+
+
+def _bits_equal(a, b):
+    return torch.equal(a.contiguous().view(torch.int32),
+                       b.contiguous().view(torch.int32))
+
+
+def _pool(n, seg=SEG, dtype_precise=0):
+    p = W.wkv7_pool_create(n, H, 64)
+    W.wkv7_pool_set_option(p, W.WKV7_OPT_SEGMENT_LEN, seg)
+    W.wkv7_pool_set_option(p, W.WKV7_OPT_CHUNK_PRECISE, dtype_precise)
+    return p
+
+
+def _run(lens, seg=SEG, seed=0, dtype=G.BF16, precise=0, **draw):
+    ids = np.arange(len(lens), dtype=np.int32)[::-1].copy()
+    init = G.draw_states(np.random.default_rng(seed + 100), len(ids), H, 64)
+    b = G.make_batch(np.random.default_rng(seed), ids, lens, H, 64, dtype,
+                     **draw)
+    pool = _pool(len(ids), seg, precise)
+    try:
+        set_states(pool, ids, init)
+        o = run_forward(pool, b)
+        S = get_states(pool, ids)
+    finally:
+        W.wkv7_pool_destroy(pool)
+    st = {int(i): G.as_f64(init[n]) for n, i in enumerate(ids)}
+    o_ref, S_ref = oracle_forward(st, b.slot_ids, b.cu_seqlens, b.inputs64(),
+                                  H, 64)
+    e = max(rel_err(o, o_ref),
+            max(rel_err(S[n], S_ref[int(i)]) for n, i in enumerate(ids)))
+    return e, o, S
+
+
+@pytest.mark.parametrize("lens", [[600], [1, 600, 1024, 130, 2065, 3],
+                                  [512, 513, 767, 768, 769]])
+def test_segments_match_oracle(lens):
+    e, o, S = _run(lens)
+    say(f"segments of {SEG}, lens {lens}: err {e:.3e}")
+    assert np.all(np.isfinite(o.numpy())) and np.all(np.isfinite(S.numpy()))
+    assert e < GUARD
+
+
+@pytest.mark.parametrize("w", [0.995, 0.9999])
+def test_segments_carry_slowly_decaying_state(w):
+    """With the recipe's decay (w about 0.55 per token) a segment forgets
+    its initial state within a few dozen tokens, so the carries hardly
+    matter; with w close to 1 (Lambda over 256 tokens 0.28 and 0.97) the
+    chained carries decide the result."""
+    lens = [1, 1100, 70, 2048]
+    e, o1, S1 = _run(lens, seed=15, w_override=w)
+    say(f"segments, w={w}: err vs oracle {e:.3e}")
+    assert e < GUARD
+    _, o2, S2 = _run(lens, seg=0, seed=15, w_override=w)
+    d = max(rel_err(o1, o2.double().numpy()), rel_err(S1, S2.double().numpy()))
+    say(f"  split vs unsplit: {d:.3e}")
+    assert 0 < d < GUARD
+
+
+def test_segments_agree_with_unsplit_run():
+    lens = [1, 1100, 70, 2048]
+    _, o1, S1 = _run(lens, seg=SEG, seed=5)
+    _, o2, S2 = _run(lens, seg=0, seed=5)
+    e = max(rel_err(o1, o2.double().numpy()), rel_err(S1, S2.double().numpy()))
+    say(f"split vs unsplit: {e:.3e}")
+    assert e < GUARD
+
+
+def test_segment_split_is_batch_invariant():
+    """The split depends on a sequence's own length: the same sequence,
+    alone or among others in another order, gives the same bits."""
+    lens_a, lens_b = [1500], [1, 700, 1500, 64]
+    rng = np.random.default_rng(7)
+    one = G.make_batch(rng, np.array([0], np.int32), lens_a, H, 64, G.BF16)
+    init = G.draw_states(np.random.default_rng(8), 1, H, 64)
+    pa = _pool(1)
+    try:
+        set_states(pa, [0], init)
+        oa = run_forward(pa, one)
+        Sa = get_states(pa, [0])
+    finally:
+        W.wkv7_pool_destroy(pa)
+    ids = np.array([3, 1, 0, 2], np.int32)
+    other = G.make_batch(np.random.default_rng(9), ids, lens_b, H, 64, G.BF16)
+    inputs = {}
+    for n in G.NAMES:       # put the same 1500 tokens at sequence 2's rows
+        t = other.inputs[n].clone()
+        lo = int(other.cu_seqlens[2])
+        t[lo:lo + 1500] = one.inputs[n]
+        inputs[n] = t
+    big = G.Batch(G.BF16, H, 64, ids, other.cu_seqlens, inputs)
+    pb = _pool(4)
+    try:
+        set_states(pb, [0], init)
+        ob = run_forward(pb, big)
+        Sb = get_states(pb, [0])
+    finally:
+        W.wkv7_pool_destroy(pb)
+    lo = int(other.cu_seqlens[2])
+    assert _bits_equal(oa, ob[lo:lo + 1500])
+    assert _bits_equal(Sa, Sb)
+
+
+def test_segment_plan_and_graph_equal_forward():
+    lens = [1, 900, 70, 1300]
+    ids = np.array([2, 0, 3, 1], np.int32)
+    init = G.draw_states(np.random.default_rng(11), 4, H, 64)
+    b = G.make_batch(np.random.default_rng(12), ids, lens, H, 64, G.BF16)
+    x = to_dev(b)
+    pf, pp, pg = _pool(4), _pool(4), _pool(4)
+    plan_p = plan_g = None
+    try:
+        for p in (pf, pp, pg):
+            set_states(p, ids, init)
+        plan_p = W.wkv7_plan_create(pp, ids, b.cu_seqlens)
+        plan_g = W.wkv7_plan_create(pg, ids, b.cu_seqlens)
+        outs = [torch.empty((b.T_tot, H, 64), dtype=torch.float32, device=DEV)
+                for _ in range(3)]
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            W.wkv7_forward_plan(pg, plan_g, x["r"], x["w"], x["k"], x["v"],
+                                x["a"], x["b"], outs[2])
+        torch.cuda.synchronize()
+        for step in range(2):
+            W.wkv7_forward(pf, ids, b.cu_seqlens, x["r"], x["w"], x["k"],
+                           x["v"], x["a"], x["b"], outs[0])
+            W.wkv7_forward_plan(pp, plan_p, x["r"], x["w"], x["k"], x["v"],
+                                x["a"], x["b"], outs[1])
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            assert _bits_equal(outs[0], outs[1]), step
+            assert _bits_equal(outs[0], outs[2]), step
+            Sf = get_states(pf, ids)
+            assert _bits_equal(Sf, get_states(pp, ids)), step
+            assert _bits_equal(Sf, get_states(pg, ids)), step
+        say("segment prefill: forward, plan and graph replays agree bit for bit")
+        del graph
+    finally:
+        for pl in (plan_p, plan_g):
+            if pl:
+                W.wkv7_plan_destroy(pl)
+        for p in (pf, pp, pg):
+            W.wkv7_pool_destroy(p)
+
+
+def test_segment_option_on_other_paths_and_validation():
+    # fp32 inputs and the precise mode take the whole-sequence kernels
+    e, _, _ = _run([700, 1], dtype=G.F32, seed=13)
+    assert e < 1e-3
+    e, _, _ = _run([700, 1], precise=1, seed=14)
+    assert e < 5e-4
+    pool = W.wkv7_pool_create(1, H, 64)
+    try:
+        for bad in (32, 100, -64, 1 << 31):
+            with pytest.raises(W.Wkv7Error) as ex:
+                W.wkv7_pool_set_option(pool, W.WKV7_OPT_SEGMENT_LEN, bad)
+            assert ex.value.status == W.WKV7_ERR_INVALID_ARG
+        W.wkv7_pool_set_option(pool, W.WKV7_OPT_SEGMENT_LEN, 0)
+        W.wkv7_pool_set_option(pool, W.WKV7_OPT_SEGMENT_LEN, 96)
+    finally:
+        W.wkv7_pool_destroy(pool)
