@@ -416,7 +416,7 @@ def run_mixed(steps: int = 10, warmup: int = 2, seed: int = 3,
 
 
 def run_prefill_long(T: int = 32768, H: int = 32, steps: int = 3,
-                     warmup: int = 2, seed: int = 6, segment_len: int = 2048):
+                     warmup: int = 2, seed: int = 6, segment_len: int = 4096):
     """One fresh sequence of T tokens at H=32 (the time to prefill one long
     prompt): H chains only, so most CUs would idle; timed unsplit and with
     segment-parallel prefill (segments of segment_len tokens), each step a
@@ -539,8 +539,20 @@ def cpu_baseline(seconds: float, seed: int = 1):
         "value": len(wl.batch.slot_ids) * n_steps / t_used,
         "unit": "tokens/s", "cores": 1, "kind": "oracle",
         "sample": (f"{n_steps} decode step(s) of the 256-slot H=32 batch "
-                   f"({t_used:.1f} s of CPU time, numpy float64, one thread)"),
+                   f"({t_used:.1f} s of CPU time, numpy float64, one thread"
+                   f" of {_cpu_model()})"),
     }
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
 
 
 def main(argv=None) -> int:
@@ -585,7 +597,7 @@ def main(argv=None) -> int:
         out = {}
         if "mixed" in legs:
             out["mixed"] = run_mixed()
-            out["mixed_segmented"] = run_mixed(segment_len=256)
+            out["mixed_segmented"] = run_mixed(segment_len=512)
         if "prefill_long" in legs:
             out["prefill_long"] = run_prefill_long()
         print(json.dumps(out), flush=True)
@@ -633,7 +645,7 @@ def main(argv=None) -> int:
         line["prefill_ragged"] = run_prefill_ragged()
     if "mixed" in legs:
         line["mixed"] = run_mixed()
-        line["mixed_segmented"] = run_mixed(segment_len=256)
+        line["mixed_segmented"] = run_mixed(segment_len=512)
     if not args.no_prefill and "prefill_long" in legs:
         line["prefill_long"] = run_prefill_long()
     if "q8_proj" in legs:
