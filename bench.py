@@ -229,6 +229,67 @@ def _draw_device(gen, T: int, H: int, dtype: str, dev, chunk: int = 16384):
     return out
 
 
+def run_decode_cold(steps: int = 20, warmup: int = 3, seed: int = 1):
+    """The headline decode batch shape with a new random 256-slot subset of
+    the 1024-slot pool every step (the pool's 512 MiB is twice the MALL, so
+    a step's slots are mostly not cached from the step before). One plan per
+    step, built before timing; one event pair over the K launches."""
+    import torch
+    import wkv7_inputs as G
+    from linear_attention_rnn_amd import wkv7 as W
+
+    dev = torch.device("cuda:0")
+    n_slots, n_active, H = 1024, 256, 32
+    rng = np.random.default_rng(seed + 100)
+    total = steps + warmup
+    id_sets = [rng.permutation(n_slots)[:n_active].astype(np.int32)
+               for _ in range(total)]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed + 100)
+    pool = W.wkv7_pool_create(n_slots, H, N)
+    plans = []
+    try:
+        init = torch.randn((n_slots, H, N, N), device=dev, generator=gen) * 0.1
+        W.wkv7_resume(pool, np.arange(n_slots, dtype=np.int32), init)
+        del init
+        xs = [G.draw_tokens_device(gen, n_active, H, N, "bf16", dev)
+              for _ in range(total)]
+        cu = np.arange(n_active + 1, dtype=np.int32)
+        o = torch.empty((n_active, H, N), dtype=torch.float32, device=dev)
+        stream = torch.cuda.current_stream()
+        plans = [W.wkv7_plan_create(pool, ids, cu) for ids in id_sets]
+
+        def step(i):
+            x = xs[i]
+            W.wkv7_forward_plan(pool, plans[i], x["r"], x["w"], x["k"], x["v"],
+                                x["a"], x["b"], o, stream=stream)
+
+        for i in range(warmup):
+            step(i)
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for i in range(steps):
+            step(warmup + i)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        k_ms = ev0.elapsed_time(ev1) / steps
+    finally:
+        for pl in plans:
+            W.wkv7_plan_destroy(pl)
+        W.wkv7_pool_destroy(pool)
+    bytes_launch = n_active * H * decode_bytes_per_token_head(2)
+    gbs = bytes_launch / (k_ms * 1e-3) / 1e9
+    return {
+        "workload": "decode_b256_h32_pool1024_bf16in_f32state_new_subset_each_step",
+        "tokens_per_s": n_active / (k_ms * 1e-3), "kernel_ms": k_ms,
+        "hbm": {"achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": gbs / HBM_PEAK_GBS, "bytes_per_launch": bytes_launch},
+        "steps": steps, "warmup": warmup,
+    }
+
+
 def run_decode_large(steps: int = 20, warmup: int = 3, seed: int = 4):
     """The large-pool decode step: 1024 random slots of a 4096-slot pool,
     H=64 (1 GiB of active state, four times the MALL), fresh bf16 inputs
@@ -270,11 +331,38 @@ def run_decode_large(steps: int = 20, warmup: int = 3, seed: int = 4):
         torch.cuda.synchronize()
         k_ms = ev0.elapsed_time(ev1) / steps
         W.wkv7_plan_destroy(plan)
+        # hibernate 256 of the touched slots into pinned host memory and
+        # resume them (1 MiB per slot; DMA over PCIe)
+        hib_ids = ids[:256]
+        host = torch.empty((256, H, N, N), dtype=torch.float32,
+                           pin_memory=True)
+        hib_bytes = host.numel() * 4
+        t_h, t_r = [], []
+        for _ in range(3):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e2 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            W.wkv7_hibernate(pool, hib_ids, host, stream=stream)
+            e1.record(stream)
+            W.wkv7_resume(pool, hib_ids, host, stream=stream)
+            e2.record(stream)
+            torch.cuda.synchronize()
+            t_h.append(e0.elapsed_time(e1))
+            t_r.append(e1.elapsed_time(e2))
+        del host
     finally:
         W.wkv7_pool_destroy(pool)
     bytes_launch = n_active * H * decode_bytes_per_token_head(2)
     gbs = bytes_launch / (k_ms * 1e-3) / 1e9
+    hib = {"slots": 256, "bytes": hib_bytes,
+           "hibernate_GBps": hib_bytes / (min(t_h) * 1e-3) / 1e9,
+           "resume_GBps": hib_bytes / (min(t_r) * 1e-3) / 1e9,
+           "hibernate_ms": min(t_h), "resume_ms": min(t_r),
+           "note": "pinned host memory, best of 3"}
     return {
+        "hibernate_resume": hib,
         "workload": "decode_b1024_h64_pool4096_bf16in_f32state",
         "tokens_per_s": n_active / (k_ms * 1e-3), "kernel_ms": k_ms,
         "hbm": {"achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -519,28 +607,166 @@ def run_q8_proj(steps: int = 50, warmup: int = 5, seed: int = 5):
             INT8_MFMA_PEAK_TOPS, **out, "steps": steps, "warmup": warmup}
 
 
-def cpu_baseline(seconds: float, seed: int = 1):
-    """The float64 oracle on a bounded sample: whole decode steps of the same
-    256-slot, H=32 batch, repeated until `seconds` have passed."""
+def run_ceilings(reps: int = 10):
+    """What the chip sustains, measured with the probe library: uint4
+    streaming copies over the decode legs' state sizes (in place, as the
+    decode kernel reads and rewrites its slots; the large one also with
+    non-temporal loads and stores, and source to destination) and matrix-core
+    loops. Copy rates count bytes read plus bytes written; each figure is
+    the best over a few launch shapes, timed with one event pair around
+    `reps` back-to-back launches after a warm-up."""
+    import torch
+    from linear_attention_rnn_amd import hw_probe as P
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, n=reps):
+        fn()
+        fn()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e-3
+
+    def copy_gbs(src, dst, nbytes, nt):
+        best = 0.0
+        for blocks in (1024, 2048, 4096, 8192):
+            t = timed(lambda: P.hwprobe_copy(src, dst, nbytes, nt, blocks,
+                                             stream))
+            best = max(best, 2 * nbytes / t / 1e9)
+        return best
+
+    out = {"unit_copy": "GB/s (read + written)", "unit_mfma": "TFLOP/s"}
+    small = 128 << 20           # the headline decode's active state
+    big = 1 << 30               # the large-pool decode's active state
+    a = torch.empty(big // 4, dtype=torch.float32, device=dev).normal_()
+    out["copy_inplace_128MiB"] = copy_gbs(a, a, small, False)
+    out["copy_inplace_1GiB"] = copy_gbs(a, a, big, False)
+    out["copy_inplace_1GiB_nt"] = copy_gbs(a, a, big, True)
+    # 128 MiB windows of a 512 MiB buffer, a different window each launch:
+    # no reuse between launches. The cold decode leg reads a random quarter
+    # of its 512 MiB pool per step, which overlaps the previous step's slots
+    # by a quarter on average, so it can exceed this figure; it is reported
+    # against the published peak only.
+    win = [a[i * (small // 4):(i + 1) * (small // 4)] for i in range(4)]
+    best = 0.0
+    for blocks in (2048, 8192):
+        k = {"i": 0}
+
+        def rot():
+            w = win[k["i"] % 4]
+            k["i"] += 1
+            P.hwprobe_copy(w, w, small, False, blocks, stream)
+        best = max(best, 2 * small / timed(rot, 12) / 1e9)
+    out["copy_inplace_128MiB_rotating_512MiB"] = best
+    b = torch.empty_like(a)
+    out["copy_1GiB_nt"] = copy_gbs(a, b, big, True)
+    out["torch_copy_1GiB"] = 2 * big / timed(lambda: b.copy_(a)) / 1e9
+    del b
+    # PCIe: one contiguous 256 MiB DMA each way with pinned host memory
+    host = torch.empty(64 << 20, dtype=torch.float32, pin_memory=True)
+    dsub = a[:64 << 20]
+    out["pcie_d2h_256MiB"] = (256 << 20) / timed(
+        lambda: host.copy_(dsub, non_blocking=True), 3) / 1e9
+    out["pcie_h2d_256MiB"] = (256 << 20) / timed(
+        lambda: dsub.copy_(host, non_blocking=True), 3) / 1e9
+    out["unit_pcie"] = "GB/s (one direction)"
+    del a, host, dsub
+    blocks = 1024               # four workgroups of four wavefronts per CU
+    res = torch.empty(blocks * P.WAVES_PER_BLOCK, dtype=torch.float32,
+                      device=dev)
+    for kind, key, iters in ((P.MFMA_BF16, "mfma_bf16_16x16x32", 20000),
+                             (P.MFMA_I8, "mfma_i8_16x16x64", 20000)):
+        ops = {}
+
+        def run():
+            ops["n"] = P.hwprobe_mfma(kind, blocks, iters, res, stream)
+        t = timed(run, 3)
+        out[key] = ops["n"] / t / 1e12
+    out["hbm_ceiling_decode"] = out["copy_inplace_128MiB"]
+    out["hbm_ceiling_decode_large"] = max(out["copy_inplace_1GiB"],
+                                          out["copy_inplace_1GiB_nt"])
+    return out
+
+
+def _with_ceiling(obj: dict, achieved: float, ceiling: float) -> dict:
+    obj["measured_ceiling"] = ceiling
+    obj["frac_of_measured"] = achieved / ceiling
+    return obj
+
+
+def _oracle_decode_slice(lo: int, hi: int, seed: int, seconds: float,
+                         barrier=None, queue=None):
+    """Whole decode steps of slots lo..hi of the 256-slot H=32 batch through
+    the float64 oracle, one BLAS thread, until `seconds` of compute have
+    passed (input generation is not timed). Returns (tokens, seconds)."""
+    from threadpoolctl import threadpool_limits
     import wkv7_inputs as G
     from oracle import wkv7_decode_batch
 
-    wl = G.cfg_decode(seed=seed)
-    S = G.as_f64(wl.init_states)
-    n_steps, t_used = 0, 0.0
-    while t_used < seconds:
-        b = G.decode_step_inputs(seed, n_steps, wl.batch.slot_ids, wl.H, wl.N)
-        x = b.inputs64()
-        t0 = time.perf_counter()
-        _, S = wkv7_decode_batch(S, x)
-        t_used += time.perf_counter() - t0
-        n_steps += 1
+    with threadpool_limits(1):
+        wl = G.cfg_decode(seed=seed)
+        S = G.as_f64(wl.init_states[lo:hi])
+        ids = wl.batch.slot_ids
+        if barrier is not None:
+            barrier.wait()
+        n_steps, t_used = 0, 0.0
+        while t_used < seconds:
+            b = G.decode_step_inputs(seed, n_steps, ids, wl.H, wl.N)
+            x = {k: v[lo:hi] for k, v in b.inputs64().items()}
+            t0 = time.perf_counter()
+            _, S = wkv7_decode_batch(S, x)
+            t_used += time.perf_counter() - t0
+            n_steps += 1
+    res = ((hi - lo) * n_steps, t_used)
+    if queue is not None:
+        queue.put(res)
+    return res
+
+
+def cpu_baseline(seconds: float, seed: int = 1, max_workers: int = 16):
+    """The float64 oracle on a bounded sample of the headline workload:
+    whole decode steps of the 256-slot, H=32 batch. First on one core; then
+    the batch's slots are split over worker processes (one per core of this
+    process's CPU set, at most `max_workers`), all running at once, and the
+    rate is the sum of the workers' rates."""
+    import multiprocessing as mp
+
+    tok1, t1 = _oracle_decode_slice(0, 256, seed, seconds)
+    single = tok1 / t1
+    cores = max(1, min(max_workers, len(os.sched_getaffinity(0))))
+    value, used, sample_par = single, 1, ""
+    if cores > 1:
+        ctx = mp.get_context("spawn")
+        barrier, queue = ctx.Barrier(cores), ctx.Queue()
+        bounds = np.linspace(0, 256, cores + 1).astype(int)
+        procs = [ctx.Process(target=_oracle_decode_slice,
+                             args=(int(bounds[i]), int(bounds[i + 1]), seed,
+                                   seconds * 0.5, barrier, queue))
+                 for i in range(cores)]
+        for p in procs:
+            p.start()
+        res = [queue.get(timeout=600) for _ in procs]
+        for p in procs:
+            p.join(timeout=60)
+        if all(p.exitcode == 0 for p in procs):
+            value, used = sum(t / s for t, s in res), cores
+            sample_par = (f"; all cores: the 256 slots split over {cores} "
+                          f"worker processes running at once, "
+                          f"{seconds * 0.5:.0f} s of compute each")
     return {
-        "value": len(wl.batch.slot_ids) * n_steps / t_used,
-        "unit": "tokens/s", "cores": 1, "kind": "oracle",
-        "sample": (f"{n_steps} decode step(s) of the 256-slot H=32 batch "
-                   f"({t_used:.1f} s of CPU time, numpy float64, one thread"
-                   f" of {_cpu_model()})"),
+        "value": value, "unit": "tokens/s", "cores": used, "kind": "oracle",
+        "single_core_value": single,
+        "sample": (f"whole decode steps of the 256-slot H=32 batch, numpy "
+                   f"float64, one BLAS thread per process, on "
+                   f"{_cpu_model()}; one core: {tok1 // 256} steps in "
+                   f"{t1:.1f} s{sample_par}"),
     }
 
 
@@ -565,8 +791,9 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--legs",
-                    default="decode,prefill,decode_large,prefill_ragged,mixed,"
-                            "prefill_long,q8_proj",
+                    default="decode,prefill,decode_cold,decode_large,"
+                            "prefill_ragged,mixed,prefill_long,q8_proj,"
+                            "ceilings",
                     help="comma list of legs to run (profiling one kernel)")
     ap.add_argument("--prefill-steps", type=int, default=10)
     args = ap.parse_args(argv)
@@ -641,6 +868,8 @@ def main(argv=None) -> int:
         line["prefill"] = run_prefill(args.prefill_steps, 20)
     if "decode_large" in legs:
         line["decode_large"] = run_decode_large()
+    if "decode_cold" in legs:
+        line["decode_cold"] = run_decode_cold()
     if not args.no_prefill and "prefill_ragged" in legs:
         line["prefill_ragged"] = run_prefill_ragged()
     if "mixed" in legs:
@@ -650,6 +879,26 @@ def main(argv=None) -> int:
         line["prefill_long"] = run_prefill_long()
     if "q8_proj" in legs:
         line["q8_proj"] = run_q8_proj()
+    if "ceilings" in legs:
+        c = run_ceilings()
+        line["ceilings"] = c
+        _with_ceiling(line["roofline"], achieved, c["hbm_ceiling_decode"])
+        if "prefill" in line:
+            m = line["prefill"]["mfma"]
+            _with_ceiling(m, m["issued_tflops"], c["mfma_bf16_16x16x32"])
+        if "decode_large" in line:
+            h = line["decode_large"]["hbm"]
+            _with_ceiling(h, h["achieved"], c["hbm_ceiling_decode_large"])
+        if "q8_proj" in line:
+            q = line["q8_proj"]
+            q["measured_int8_tops"] = c["mfma_i8_16x16x64"]
+            for k, v in q.items():
+                if isinstance(v, dict) and "tops" in v:
+                    v["mfma_frac_of_measured"] = v["tops"] / c["mfma_i8_16x16x64"]
+        if "decode_large" in line:
+            hr = line["decode_large"]["hibernate_resume"]
+            hr["pcie_d2h_contiguous_GBps"] = c["pcie_d2h_256MiB"]
+            hr["pcie_h2d_contiguous_GBps"] = c["pcie_h2d_256MiB"]
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -3,7 +3,9 @@
     python -m linear_attention_rnn_amd.build
 
 Compiles every source under csrc/ to an object in _build/ (in parallel) and
-links linear_attention_rnn_amd/libwkv7.so. Always rebuilds.
+links linear_attention_rnn_amd/libwkv7.so; links the hardware-ceiling probes
+under probe/ into libwkv7_probe.so, a library of their own that only
+measurement code loads. Always rebuilds.
 """
 from __future__ import annotations
 
@@ -18,6 +20,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libwkv7.so")
+PROBE_SRC = os.path.join(PKG, "probe")
+PROBE_LIB = os.path.join(PKG, "libwkv7_probe.so")
 ARCH = "gfx950"
 
 
@@ -50,13 +54,13 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
+def _sources(d: str) -> list:
+    return sorted(os.path.join(d, f) for f in os.listdir(d)
                   if f.endswith((".hip", ".cpp")))
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+
+
+def _link(objs: list, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}",
            "-mcode-object-version=5", *objs,
            "-o", tmp]
@@ -64,9 +68,20 @@ def build(verbose: bool = False) -> str:
     if res.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stdout}\n"
                            f"{res.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = _sources(CSRC)
+    probe_srcs = _sources(PROBE_SRC)
+    with cf.ThreadPoolExecutor(max_workers=8) as ex:
+        objs = list(ex.map(_compile, srcs + probe_srcs))
+    _link(objs[:len(srcs)], LIB)
+    _link(objs[len(srcs):], PROBE_LIB)
     if verbose:
         print(f"built {LIB}")
+        print(f"built {PROBE_LIB}")
     return LIB
 
 
