@@ -231,14 +231,23 @@ wkv7_status wkv7_reset(wkv7_pool* pool, const int32_t* ids, int32_t n,
  * must stay alive and untouched until the stream has passed the call (page
  * "Virtual Memory for KV Cache and Model Weights": blocks stay retained
  * until their transfers finish). bytes >= n*slot_bytes, else
- * WKV7_ERR_INVALID_ARG. The slots stay valid on the device. */
+ * WKV7_ERR_INVALID_ARG. The slots stay valid on the device.
+ * Ids that form at least four runs of consecutive slots go through a
+ * device staging buffer of the pool (at most 64 MiB, allocated on first
+ * use, kept until the pool is destroyed; WKV7_ERR_OOM if that fails): a
+ * kernel gathers up to 64 MiB of slots and one DMA moves them, so
+ * scattered slots cross PCIe at the rate of one large copy. Fewer runs
+ * take one DMA per run. */
 wkv7_status wkv7_hibernate(wkv7_pool* pool, const int32_t* ids, int32_t n,
                            void* host_dst, size_t bytes, void* stream);
 
 /* resume — copy n consecutive slot images from src (pinned host memory or
  * device memory, e.g. a snapshot) into slots ids[0..n) (distinct),
  * bit-exact. bytes >= n*slot_bytes, else WKV7_ERR_INVALID_ARG. src must
- * stay alive until the stream has passed the call. */
+ * stay alive until the stream has passed the call. Scattered ids (at
+ * least four runs) take the staging path described under hibernate; a
+ * 16-byte-aligned src in device memory of the pool's device is instead
+ * scattered into the slots by one kernel, without staging. */
 wkv7_status wkv7_resume(wkv7_pool* pool, const int32_t* ids, int32_t n,
                         const void* src, size_t bytes, void* stream);
 

@@ -82,6 +82,8 @@ struct wkv7_pool {
   int64_t segment_len = 0;           // 0: segment-parallel prefill off
   float* seg_scratch = nullptr;      // wkv7_forward's segment buffers
   size_t seg_scratch_floats = 0;
+  float* xfer_stage = nullptr;       // staging of scattered hibernate/resume
+  size_t xfer_stage_bytes = 0;
   std::vector<int32_t> free_ids;     // stack; top = back
   std::vector<uint8_t> allocated;
   Stage ring[kRing];
@@ -507,6 +509,7 @@ wkv7_status wkv7_pool_destroy(wkv7_pool* p) {
   }
   if (p->state) (void)hipFree(p->state);
   if (p->seg_scratch) (void)hipFree(p->seg_scratch);
+  if (p->xfer_stage) (void)hipFree(p->xfer_stage);
   delete p;
   if (e != hipSuccess) return fail_hip(e, "hipDeviceSynchronize(destroy)");
   return WKV7_OK;
@@ -921,6 +924,100 @@ wkv7_status copy_runs(wkv7_pool* p, const int32_t* ids, int32_t n, char* buf,
   return WKV7_OK;
 }
 
+// Scattered slots cross PCIe through a device staging buffer: a kernel
+// gathers (or scatters) up to kXferStageBytes of slot images and one DMA
+// moves the contiguous block, instead of one DMA per run of consecutive
+// ids (each DMA has a set-up cost, so many 1 MiB copies reach about two
+// thirds of the rate of one large copy). With few runs the per-run DMA is
+// kept: it needs no staging and no kernel.
+constexpr size_t kXferStageBytes = static_cast<size_t>(64) << 20;
+constexpr int32_t kXferMinRuns = 4;
+
+int32_t count_runs(const int32_t* ids, int32_t n) {
+  int32_t runs = n > 0 ? 1 : 0;
+  for (int32_t i = 1; i < n; ++i) runs += ids[i] != ids[i - 1] + 1;
+  return runs;
+}
+
+// Grow-only, like the segment buffers (the free waits for the device).
+wkv7_status ensure_xfer_stage(wkv7_pool* p, size_t bytes) {
+  if (bytes <= p->xfer_stage_bytes) return WKV7_OK;
+  if (p->xfer_stage) (void)hipFree(p->xfer_stage);
+  p->xfer_stage = nullptr;
+  p->xfer_stage_bytes = 0;
+  if (hipMalloc(reinterpret_cast<void**>(&p->xfer_stage), bytes) != hipSuccess)
+    return fail(WKV7_ERR_OOM, "transfer staging of %zu bytes", bytes);
+  p->xfer_stage_bytes = bytes;
+  return WKV7_OK;
+}
+
+// True if ptr is device memory of the pool's device, 16-byte aligned (a
+// snapshot buffer): resume then scatters straight from it with one kernel.
+bool is_pool_device_buffer(const wkv7_pool* p, const void* ptr) {
+  if (reinterpret_cast<uintptr_t>(ptr) % 16 != 0) return false;
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, ptr) != hipSuccess) {
+    (void)hipGetLastError();          // unregistered host memory: not ours
+    return false;
+  }
+  return attr.type == hipMemoryTypeDevice && attr.device == p->device;
+}
+
+wkv7_status copy_slots_staged(wkv7_pool* p, const int32_t* ids, int32_t n,
+                              char* buf, bool to_pool, bool device_src,
+                              hipStream_t hs) {
+  const size_t sb = slot_bytes_of(p);
+  // slots per group; a device source is one group read in place
+  const int32_t g = device_src
+      ? n : static_cast<int32_t>(std::max<size_t>(1, kXferStageBytes / sb));
+  if (!device_src)
+    if (wkv7_status st = ensure_xfer_stage(p, static_cast<size_t>(std::min(g, n)) * sb))
+      return st;
+  // (source slot, destination slot) per image; the stage and a device
+  // source are indexed like pools, from the start of the group
+  std::vector<int32_t> pairs(2 * static_cast<size_t>(n));
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t local = i % g;
+    pairs[2 * i] = to_pool ? local : ids[i];
+    pairs[2 * i + 1] = to_pool ? ids[i] : local;
+  }
+  const int32_t* dev = nullptr;
+  Stage* stage = nullptr;
+  if (wkv7_status st = stage_upload(p, pairs.data(), pairs.size(), hs, &dev, &stage))
+    return st;
+  for (int32_t g0 = 0; g0 < n; g0 += g) {
+    const int32_t m = std::min(g, n - g0);
+    const size_t bytes = static_cast<size_t>(m) * sb;
+    char* img = buf + static_cast<size_t>(g0) * sb;
+    hipError_t e = hipSuccess;
+    if (device_src) {
+      e = wkv7::launch_copy_slots(reinterpret_cast<const float*>(img), p->state,
+                                  p->slot_floats, dev + 2 * g0, m, hs);
+      if (e != hipSuccess) return fail_hip(e, "slot scatter launch");
+    } else if (to_pool) {
+      e = hipMemcpyAsync(p->xfer_stage, img, bytes, hipMemcpyDefault, hs);
+      if (e != hipSuccess) return fail_hip(e, "hipMemcpyAsync(resume)");
+      e = wkv7::launch_copy_slots(p->xfer_stage, p->state, p->slot_floats,
+                                  dev + 2 * g0, m, hs);
+      if (e != hipSuccess) return fail_hip(e, "slot scatter launch");
+    } else {
+      e = wkv7::launch_copy_slots(p->state, p->xfer_stage, p->slot_floats,
+                                  dev + 2 * g0, m, hs);
+      if (e != hipSuccess) return fail_hip(e, "slot gather launch");
+      e = hipMemcpyAsync(img, p->xfer_stage, bytes, hipMemcpyDefault, hs);
+      if (e != hipSuccess) return fail_hip(e, "hipMemcpyAsync(hibernate)");
+    }
+  }
+  return stage_commit(stage, hs);
+}
+
+wkv7_status copy_slot_images(wkv7_pool* p, const int32_t* ids, int32_t n,
+                             char* buf, bool to_pool, hipStream_t hs) {
+  if (count_runs(ids, n) < kXferMinRuns) return copy_runs(p, ids, n, buf, to_pool, hs);
+  const bool device_src = to_pool && is_pool_device_buffer(p, buf);
+  return copy_slots_staged(p, ids, n, buf, to_pool, device_src, hs);
+}
+
 }  // namespace
 
 wkv7_status wkv7_hibernate(wkv7_pool* p, const int32_t* ids, int32_t n,
@@ -936,8 +1033,8 @@ wkv7_status wkv7_hibernate(wkv7_pool* p, const int32_t* ids, int32_t n,
                 static_cast<size_t>(n) * slot_bytes_of(p), n);
   DeviceGuard guard(p->device);
   if (!guard.ok) return fail(WKV7_ERR_HIP, "cannot select the pool's device");
-  return copy_runs(p, ids, n, static_cast<char*>(host_dst), false,
-                   static_cast<hipStream_t>(stream));
+  return copy_slot_images(p, ids, n, static_cast<char*>(host_dst), false,
+                          static_cast<hipStream_t>(stream));
 }
 
 wkv7_status wkv7_resume(wkv7_pool* p, const int32_t* ids, int32_t n,
@@ -953,8 +1050,9 @@ wkv7_status wkv7_resume(wkv7_pool* p, const int32_t* ids, int32_t n,
                 static_cast<size_t>(n) * slot_bytes_of(p), n);
   DeviceGuard guard(p->device);
   if (!guard.ok) return fail(WKV7_ERR_HIP, "cannot select the pool's device");
-  return copy_runs(p, ids, n, const_cast<char*>(static_cast<const char*>(src)),
-                   true, static_cast<hipStream_t>(stream));
+  return copy_slot_images(p, ids, n,
+                          const_cast<char*>(static_cast<const char*>(src)), true,
+                          static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"
