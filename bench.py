@@ -229,6 +229,56 @@ def _draw_device(gen, T: int, H: int, dtype: str, dev, chunk: int = 16384):
     return out
 
 
+def run_small(calls: int = 200, warmup: int = 20, seed: int = 0):
+    """The small case: one sequence of 64 tokens, H=2, fp32 inputs, from a
+    zeroed slot (64 tokens take the chunked kernel). Launch-bound: reported
+    as microseconds per call, through wkv7_forward (host validation and
+    metadata staging each call) and through a plan, with no roofline."""
+    import torch
+    import wkv7_inputs as G
+    from linear_attention_rnn_amd import wkv7 as W
+
+    dev = torch.device("cuda:0")
+    H, T = 2, 64
+    b = G.make_batch(np.random.default_rng(seed), [0], [T], H, N, G.F32)
+    x = {n: b.inputs[n].to(dev) for n in G.NAMES}
+    o = torch.empty((T, H, N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    pool = W.wkv7_pool_create(1, H, N)
+    out = {"workload": "small_h2_t64_f32in_zero_state"}
+    try:
+        plan = W.wkv7_plan_create(pool, b.slot_ids, b.cu_seqlens)
+
+        def fwd():
+            W.wkv7_forward(pool, b.slot_ids, b.cu_seqlens, x["r"], x["w"],
+                           x["k"], x["v"], x["a"], x["b"], o, stream=stream)
+
+        def fwd_plan():
+            W.wkv7_forward_plan(pool, plan, x["r"], x["w"], x["k"], x["v"],
+                                x["a"], x["b"], o, stream=stream)
+
+        for name, fn in (("forward", fwd), ("plan", fwd_plan)):
+            for _ in range(warmup):
+                fn()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            e0.record(stream)
+            for _ in range(calls):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
+            out[f"{name}_us_per_call_wall"] = (t1 - t0) / calls * 1e6
+            out[f"{name}_us_per_call_gpu"] = e0.elapsed_time(e1) / calls * 1e3
+        W.wkv7_plan_destroy(plan)
+    finally:
+        W.wkv7_pool_destroy(pool)
+    out["calls"] = calls
+    return out
+
+
 def run_decode_cold(steps: int = 20, warmup: int = 3, seed: int = 1):
     """The headline decode batch shape with a new random 256-slot subset of
     the 1024-slot pool every step (the pool's 512 MiB is twice the MALL, so
@@ -793,7 +843,7 @@ def main(argv=None) -> int:
     ap.add_argument("--legs",
                     default="decode,prefill,decode_cold,decode_large,"
                             "prefill_ragged,mixed,prefill_long,q8_proj,"
-                            "ceilings",
+                            "small,ceilings",
                     help="comma list of legs to run (profiling one kernel)")
     ap.add_argument("--prefill-steps", type=int, default=10)
     args = ap.parse_args(argv)
@@ -870,6 +920,8 @@ def main(argv=None) -> int:
         line["decode_large"] = run_decode_large()
     if "decode_cold" in legs:
         line["decode_cold"] = run_decode_cold()
+    if "small" in legs:
+        line["small"] = run_small()
     if not args.no_prefill and "prefill_ragged" in legs:
         line["prefill_ragged"] = run_prefill_ragged()
     if "mixed" in legs:
