@@ -155,12 +155,31 @@ __device__ __forceinline__ f16x8 frag8h(f32x4 t0, f32x4 t1, float s) {
 __device__ __forceinline__ float bf_lo(uint32_t x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
 
+// Products of the per-group decay totals g[q] of row groups q < 2 W and
+// q > 2 W + 1 (two channels), for the key wavefront W.
+template <int W>
+__device__ __forceinline__ void outer_products(const float (&g0)[8], const float (&g1)[8],
+                                               float& lo0, float& lo1, float& hi0,
+                                               float& hi1) {
+  lo0 = lo1 = hi0 = hi1 = 1.f;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    if (q < 2 * W) { lo0 *= g0[q]; lo1 *= g1[q]; }
+    if (q > 2 * W + 1) { hi0 *= g0[q]; hi1 *= g1[q]; }
+  }
+}
+
+// Two channels at once: one packed conversion for the high parts, the
+// residuals from the packed bits (exact), one packed conversion for them.
+// The same values as split() per channel.
 __device__ __forceinline__ void put2p(__bf16* pair, int mat, int pitch,
                                       int row, int col, float x0, float x1) {
-  __bf16 h0, l0, h1, l1;
-  split(x0, h0, l0);
-  split(x1, h1, l1);
-  bf16x2 h = {h0, h1}, l = {l0, l1};
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 h = __builtin_convertvector(f32x2{x0, x1}, bf16x2);
+  const uint32_t hb = __builtin_bit_cast(uint32_t, h);
+  const float h0 = __uint_as_float(hb << 16);
+  const float h1 = __uint_as_float(hb & 0xffff0000u);
+  const bf16x2 l = __builtin_convertvector(f32x2{x0 - h0, x1 - h1}, bf16x2);
   *reinterpret_cast<bf16x2*>(pair + row * pitch + col) = h;
   *reinterpret_cast<bf16x2*>(pair + mat + row * pitch + col) = l;
 }
@@ -512,17 +531,31 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs) {
     // ===== interval 1 =====
     bool bad_k = false;
     if (k_on) {
-      // key: operands of chunk cK
-      float pre0 = 1.f, pre1 = 1.f, lam0 = 1.f, lam1 = 1.f, suf0 = 1.f, suf1 = 1.f;
+      // key: operands of chunk cK. Decay over the row groups before the
+      // thread's group (pre), after it (suf) and over the whole chunk (lam).
+      // The wavefront's two groups are 2 (wv & 3) and the one after, so the
+      // products outside them have wavefront-uniform bounds.
+      float g0[8], g1[8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const float g0 = TOT[q * 64 + j0], g1 = TOT[q * 64 + j0 + 1];
-        lam0 *= g0; lam1 *= g1;
-        if (q < rg) { pre0 *= g0; pre1 *= g1; }
-        if (q > rg) { suf0 *= g0; suf1 *= g1; }
+      for (int q = 0; q < 8; ++q) { g0[q] = TOT[q * 64 + j0]; g1[q] = TOT[q * 64 + j0 + 1]; }
+      float lo0, lo1, hi0, hi1;      // products below and above the pair
+      switch (wv & 3) {
+        case 0: outer_products<0>(g0, g1, lo0, lo1, hi0, hi1); break;
+        case 1: outer_products<1>(g0, g1, lo0, lo1, hi0, hi1); break;
+        case 2: outer_products<2>(g0, g1, lo0, lo1, hi0, hi1); break;
+        default: outer_products<3>(g0, g1, lo0, lo1, hi0, hi1); break;
       }
+      const int wq = 2 * (wv & 3);
+      const bool second = (lane >> 5) != 0;   // group wq + 1
+      const float ga0 = g0[wq], ga1 = g1[wq], gb0 = g0[wq + 1], gb1 = g1[wq + 1];
+      const float pre0 = second ? lo0 * ga0 : lo0, pre1 = second ? lo1 * ga1 : lo1;
+      const float suf0 = second ? hi0 : gb0 * hi0, suf1 = second ? hi1 : gb1 * hi1;
+      const float lam0 = (lo0 * ga0) * (gb0 * hi0), lam1 = (lo1 * ga1) * (gb1 * hi1);
       if (rg == 0) { LAMb[bK * 64 + j0] = lam0; LAMb[bK * 64 + j0 + 1] = lam1; }
-      const float inv0 = 1.f / lam0, inv1 = 1.f / lam1;
+      // hardware reciprocal (1 ulp): the scaled Gram operands are split into
+      // bf16 pairs, far coarser; a lam below the fast path's range takes the
+      // token-by-token path, which does not use these operands
+      const float inv0 = __builtin_amdgcn_rcpf(lam0), inv1 = __builtin_amdgcn_rcpf(lam1);
       _Float16* Abar = VOk;
       _Float16* Rbar = VOk + kM64;
       _Float16* BbT = VOk + 2 * kM64;
