@@ -206,12 +206,16 @@ __device__ __forceinline__ uint32_t dpp_umax16(uint32_t x) {
   x = umax(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x140, 0xF, 0xF, false)));
   return x;
 }
-// max over the wavefront of x >= 0 (or NaN): rows of 16 by DPP, then across rows
+// max over the wavefront of x >= 0 (or NaN): rows of 16 by DPP (every lane
+// of a row then holds the row's maximum), then the four rows through scalar
+// registers (no LDS round trip). The result is wavefront-uniform.
 __device__ __forceinline__ float wave_max(float x) {
-  uint32_t u = dpp_umax16(__float_as_uint(x));
-  u = umax(u, static_cast<uint32_t>(__shfl_xor(static_cast<int>(u), 16)));
-  u = umax(u, static_cast<uint32_t>(__shfl_xor(static_cast<int>(u), 32)));
-  return __uint_as_float(u);
+  const uint32_t u = dpp_umax16(__float_as_uint(x));
+  const uint32_t r0 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(u), 0));
+  const uint32_t r1 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(u), 16));
+  const uint32_t r2 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(u), 32));
+  const uint32_t r3 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(u), 48));
+  return __uint_as_float(umax(umax(r0, r1), umax(r2, r3)));
 }
 // power of two s with max|x s| < 2^14 for max|x| = m (1 if m is 0 or not
 // finite); 1/s in *inv
