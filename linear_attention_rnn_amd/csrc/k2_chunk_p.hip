@@ -490,8 +490,34 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs) {
     }
   }
 
-  Raw nxt;
-  if (is_key) load_raw(nxt, p, tok0, min(kL, len), h, rg, jp);
+  // Key side: a chunk's raw inputs are loaded two steps before its operands
+  // are built (nxt) and prepared one step before (x: padded; running
+  // products of w over the thread's 4 rows in P0/P1; the rows' totals in
+  // TOT), in the previous step's second interval, where the key wavefronts
+  // wait on the value side anyway. The third barrier then orders the TOT
+  // writes before their reads, and no barrier precedes the operand build.
+  Raw nxt, x;
+  float w0[4], w1[4], P0[4], P1[4];
+  auto prep = [&](int c) {
+    x = nxt;
+    pad_raw(x, min(kL, len - c * kL), rg);
+    if (zero_v) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x.v[e] = 0u;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { w0[e] = bf_lo(x.w[e]); w1[e] = bf_hi(x.w[e]); }
+    P0[0] = w0[0]; P1[0] = w1[0];
+#pragma unroll
+    for (int e = 1; e < 4; ++e) { P0[e] = P0[e - 1] * w0[e]; P1[e] = P1[e - 1] * w1[e]; }
+    TOT[rg * 64 + j0] = P0[3];
+    TOT[rg * 64 + j0 + 1] = P1[3];
+  };
+  if (is_key) {
+    load_raw(nxt, p, tok0, min(kL, len), h, rg, jp);
+    if (nch > 0) prep(0);
+  }
+  __syncthreads();                                                // TOT of chunk 0
 
   // fallback flags, known to every thread: of chunk step-1 (early: its
   // operands; gram: its Gram matrices) and of chunk step-2 (tri: its T)
@@ -511,26 +537,6 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs) {
     const int nV = min(kL, len - cV * kL);
     const int t0K = tok0 + cK * kL;
     const int t0V = tok0 + cV * kL;
-
-    // ===== interval 0: key: prefix products of the thread's 4 rows =====
-    Raw x;
-    float w0[4], w1[4], P0[4], P1[4];
-    if (k_on) {
-      x = nxt;
-      pad_raw(x, min(kL, len - cK * kL), rg);
-      if (zero_v) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x.v[e] = 0u;
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) { w0[e] = bf_lo(x.w[e]); w1[e] = bf_hi(x.w[e]); }
-      P0[0] = w0[0]; P1[0] = w1[0];
-#pragma unroll
-      for (int e = 1; e < 4; ++e) { P0[e] = P0[e - 1] * w0[e]; P1[e] = P1[e - 1] * w1[e]; }
-      TOT[rg * 64 + j0] = P0[3];
-      TOT[rg * 64 + j0 + 1] = P1[3];
-    }
-    __syncthreads();                                              // B1
 
     // ===== interval 1 =====
     bool bad_k = false;
@@ -731,6 +737,7 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs) {
         put4h(dst, kP32, n16, 16 + 4 * g, z);
       }
     }
+    if (is_key && cK + 1 < nch) prep(cK + 1);   // key: prepare the next chunk
     if (v_on && !v_exact_done) {
       // value side, second half: U, O, state update of chunk cV
       const _Float16* Rbar = VOv + kM64;
