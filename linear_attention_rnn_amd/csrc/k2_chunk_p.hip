@@ -18,18 +18,18 @@
 //
 // Organisation: one 512-thread workgroup (8 wavefronts, two per SIMD) per
 // (sequence, head), as a pipeline over chunks. In step c:
-//   * key wavefronts 0-3 build chunk c: running-product decays, the scaled
-//     operands (into one of two LDS buffers), then the four Gram matrices
-//     (wavefront w computes matrix w);
-//   * key wavefront 0 also builds T for chunk c - 1 (diagonal 16x16 blocks by
-//     forward substitution, the off-diagonal block by two MFMA products),
-//     its latency hidden behind the element-wise work;
+//   * key wavefronts 0-3 build chunk c's scaled operands (into one of two
+//     LDS buffers) from its decay products, then the four Gram matrices
+//     (wavefront w computes matrix w), then prepare chunk c + 1 (its
+//     running-product decays and per-row-group totals), which fills the
+//     time they would otherwise wait for the value side;
 //   * value wavefronts 4-7 consume chunk c - 1: wavefront 4 + w owns state
 //     rows i in [16 w, 16 w + 16), kept in registers as MFMA accumulator
-//     tiles of S^T, and computes X, then U, O (written to HBM) and the state
-//     update.
-// Three workgroup barriers per step; fallback flags travel with the second
-// and third (a ballot per wavefront, posted to LDS).
+//     tiles of S^T, and computes X and T (in registers, fp16 MFMA products),
+//     then U, O (written to HBM) and the state update.
+// Two workgroup barriers per step, after the operands and at the end; the
+// fallback flags of chunk c travel with the second (a ballot per
+// wavefront, posted to LDS).
 //
 // Precision: Gram products use split bf16 (hi + lo) operands, three MFMAs
 // with fp32 accumulation; the diagonal blocks of T are fp32; every
@@ -519,8 +519,9 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs) {
   }
   __syncthreads();                                                // TOT of chunk 0
 
-  // fallback flags, known to every thread: of chunk step-1 (early: its
-  // operands; gram: its Gram matrices) and of chunk step-2 (tri: its T)
+  // fallback flags of chunk step - 1, known to every thread from the end
+  // of the step before: early (its inputs or decays out of the fast path's
+  // range) and gram (its Gram matrices out of the fp16 range)
   bool early_prev = false, gram_prev = false;
   const f32x4 z = {0.f, 0.f, 0.f, 0.f};
 
@@ -674,12 +675,14 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs) {
         v_exact_done = true;
       }
     }
-    const uint32_t f2 = barrier_or2(FLG, wv, lane, k_on && bad_k, false);  // B2
-    const bool early_cur = (f2 & 1u) != 0;   // chunk cK
+    // B2. The key side's range flags for chunk cK travel with B3: its Grams
+    // are built either way, and the value side reads them only if no flag
+    // was raised.
+    __syncthreads();                                              // B2
 
     // ===== interval 2 =====
     float gmax = 0.f;
-    if (k_on && !early_cur) {
+    if (k_on) {
       // key: Gram matrix wv, tiles (tt, st) = (0,0), (1,0), (1,1) as C[s][t]
       const __bf16* Pm = (wv & 1) ? Kbar : Bbar;
       const __bf16* Qm = (wv >= 2) ? Rhat : Ahat;
@@ -783,11 +786,10 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs) {
                           fmaf(cu[r], inv_ux, cv[r]));
       }
     }
-    const uint32_t f3 = barrier_or2(FLG + 8, wv, lane,
-                                    k_on && !early_cur && !(gmax < kHalfSafe),
-                                    false);                      // B3
-    early_prev = early_cur;
-    gram_prev = (f3 & 1u) != 0;
+    const uint32_t f3 = barrier_or2(FLG + 8, wv, lane, k_on && bad_k,
+                                    k_on && !(gmax < kHalfSafe));  // B3
+    early_prev = (f3 & 1u) != 0;
+    gram_prev = (f3 & 2u) != 0;
   }
 
   if (!is_key && s_out) {
