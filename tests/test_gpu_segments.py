@@ -177,3 +177,60 @@ def test_segment_option_on_other_paths_and_validation():
         W.wkv7_pool_set_option(pool, W.WKV7_OPT_SEGMENT_LEN, 96)
     finally:
         W.wkv7_pool_destroy(pool)
+
+
+@pytest.mark.parametrize("w", [None, 0.9995])
+def test_long_prompt_full_size_sampled(w):
+    """One prompt of 32,768 tokens at H=32, bf16, zero state, with segments
+    of 4096: the benchmark's long-prompt configuration (8 segments, phases
+    of 448 and 256 workgroups). Outputs and final state of sampled heads
+    against the oracle, one head at a time. With w = 0.9995 a segment keeps
+    e^-2 of its initial state, so the chained carries decide the result."""
+    from oracle import wkv7_sequence
+    T, Hl, seg = 32768, 32, 4096
+    draw = {} if w is None else {"w_override": w}
+    b = G.make_batch(np.random.default_rng(12), [0], [T], Hl, 64, G.BF16,
+                     **draw)
+    say(f"long prompt {T} x H={Hl}, segments of {seg}, w={w}")
+    pool = W.wkv7_pool_create(1, Hl, 64)
+    try:
+        W.wkv7_pool_set_option(pool, W.WKV7_OPT_SEGMENT_LEN, seg)
+        o = run_forward(pool, b)
+        S = get_states(pool, [0])
+    finally:
+        W.wkv7_pool_destroy(pool)
+    assert np.all(np.isfinite(o.numpy())) and np.all(np.isfinite(S.numpy()))
+    worst = 0.0
+    for hh in (0, 13, 31):
+        x = {n: G.as_f64(b.inputs[n][:, hh]) for n in G.NAMES}
+        o_ref, S_ref = wkv7_sequence(np.zeros((64, 64)), **x)
+        e = max(rel_err(o[:, hh], o_ref), rel_err(S[0, hh], S_ref))
+        say(f"  head {hh}: err {e:.3e}")
+        worst = max(worst, e)
+    assert worst < GUARD
+
+
+def test_mixed_layer_full_size_with_segments():
+    """One layer of the 12-layer mixed stack (H=12: 64 decode tokens from
+    resident states and prefills of 512, 1024, 2048 and 2048 tokens from
+    zero) with segments of 512, as the benchmark runs it: every output and
+    final state against the oracle."""
+    lay = G.cfg_mixed_layers(seed=3)[0]
+    b = lay.batch
+    Hm = 12
+    pool = W.wkv7_pool_create(128, Hm, 64)
+    try:
+        W.wkv7_pool_set_option(pool, W.WKV7_OPT_SEGMENT_LEN, 512)
+        set_states(pool, lay.decode_ids, lay.init_states)
+        o = run_forward(pool, b)
+        S = get_states(pool, b.slot_ids)
+    finally:
+        W.wkv7_pool_destroy(pool)
+    st = {int(i): G.as_f64(lay.init_states[n])
+          for n, i in enumerate(lay.decode_ids)}
+    o_ref, S_ref = oracle_forward(st, b.slot_ids, b.cu_seqlens, b.inputs64(),
+                                  Hm, 64)
+    e = max(rel_err(o, o_ref),
+            max(rel_err(S[n], S_ref[int(i)]) for n, i in enumerate(b.slot_ids)))
+    say(f"mixed layer, segments of 512: err {e:.3e}")
+    assert e < GUARD
