@@ -12,11 +12,14 @@
 // v_mfma_i32_16x16x64_i8 with exact int32 accumulation. A workgroup of four
 // wavefronts owns 64 output rows and up to 128 tokens. k advances in
 // super-chunks of 256: the tokens' codes go through two LDS buffers (shared
-// by the four wavefronts), each wavefront holds its 16 weight rows'
-// fragments in registers and reuses each for 8 token tiles, and the next
-// super-chunk's codes and weights are loaded while the current one is
-// multiplied (one barrier per super-chunk). Weight codes are read from HBM
-// once per token block.
+// by the four wavefronts; the next super-chunk's codes are loaded while the
+// current one is multiplied, one barrier per super-chunk), and each
+// wavefront streams its 16 weight rows through a ring of four super-chunk
+// register buffers, loaded three super-chunks ahead, reusing each fragment
+// for 8 token tiles. The weight codes are read from HBM once per token
+// block. A k-step's eight token fragments are read from LDS together before
+// its MFMAs, so their latencies overlap. The registers fit two workgroups
+// per CU.
 //
 // MFMA operands: lane 16 g + n supplies row n of its operand with 16 bytes
 // for k = kb + 16 g .. kb + 16 g + 15 (the same k assignment for both
@@ -147,7 +150,7 @@ void quantize_rows_kernel(const typename Elem<DT>::T* __restrict__ x,
 constexpr int kRowsWG = 64;      // output rows per workgroup (16 per wave)
 constexpr int kTokWG = 128;      // tokens per workgroup (8 tiles of 16)
 constexpr int kKS = 256;         // k per super-chunk (4 MFMA k-steps)
-constexpr int kSCM = 8;          // super-chunks per macro-chunk (2048 k)
+constexpr int kWD = 3;           // weight prefetch distance (super-chunks)
 constexpr int kPitch = kKS + 16; // LDS bytes per token row (padded)
 
 __global__ __launch_bounds__(256, 2)
@@ -172,10 +175,13 @@ void q8_matmul_kernel(const int8_t* __restrict__ wq,
       const_cast<int8_t*>(xq), 0, static_cast<int>(B * I), 0x00020000);
   const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<int8_t*>(wq), 0, static_cast<int>(O * I), 0x00020000);
-  // staging: thread t copies 128 bytes (8 x 16) of token t / 2's super-chunk
-  const int st_tok = tid >> 1;
-  const int st_off = 128 * (tid & 1);
+  // staging: thread t copies 16 bytes of tokens 16 e + t / 16 (e = 0..7) at
+  // k offset 16 (t % 16): each load instruction covers four whole 256-byte
+  // token rows of the super-chunk
+  const int st_tok = tid >> 4;
+  const int st_off = 16 * (tid & 15);
   const int xoff = static_cast<int>((b0 + st_tok) * I) + st_off;
+  const int xstride = static_cast<int>(16 * I);         // 16 tokens
   // weight fragment of k-step j: bytes kb + 64 j + 16 g of row o0 + n
   const int woff = static_cast<int>((o0 + n) * I) + 16 * g;
   const int64_t n_sc = (I + kKS - 1) / kKS;    // I % 64 == 0
@@ -189,55 +195,71 @@ void q8_matmul_kernel(const int8_t* __restrict__ wq,
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       xr[e] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(
-          xres, xoff + static_cast<int>(kb) + 16 * e, 0, 0));
+          xres, xoff + static_cast<int>(kb) + xstride * e, 0, 0));
   };
   auto store_x = [&](int buf) {
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-      *reinterpret_cast<i32x4*>(&xl[buf][st_tok * kPitch + st_off + 16 * e]) =
+      *reinterpret_cast<i32x4*>(&xl[buf][(16 * e + st_tok) * kPitch + st_off]) =
           xr[e];
   };
 
-  load_x(0);
-  store_x(0);
-  if (n_sc > 1) load_x(kKS);
-  // macro-chunks of 2048 k: the wavefront's whole weight strip for the
-  // macro-chunk is loaded at once (all 32 fragments in flight together)
-  for (int64_t m0 = 0; m0 < n_sc; m0 += kSCM) {
-    i32x4 wall[kSCM * 4];
+  // the wavefront's weight fragments of one super-chunk (its 16 rows, 256
+  // k): k-steps past I are zero
+  auto load_w = [&](i32x4 (&w)[4], int64_t sc) {
 #pragma unroll
-    for (int f = 0; f < kSCM * 4; ++f) {
-      const int64_t k = (m0 * 4 + f) * 64;     // first k of this k-step
+    for (int j = 0; j < 4; ++j) {
+      const int64_t k = sc * kKS + 64 * j;
       const i32x4 v = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(
           wres, woff + static_cast<int>(k), 0, 0));
-      wall[f] = k < I ? v : i32x4{0, 0, 0, 0};
+      w[j] = k < I ? v : i32x4{0, 0, 0, 0};
     }
-    lds_barrier();                          // super-chunk m0 staged
+  };
+  // one super-chunk: multiply with weights wc, load the weights of the
+  // super-chunk kWD ahead into wn (the ring slot freed by the one before),
+  // stage the next tokens' codes and load the ones after
+  auto step = [&](int64_t sc, i32x4 (&wc)[4], i32x4 (&wn)[4]) {
+    if (sc >= n_sc) return;
+    if (sc + kWD < n_sc) load_w(wn, sc + kWD);
+    const int buf = static_cast<int>(sc & 1);
 #pragma unroll
-    for (int q = 0; q < kSCM; ++q) {
-      const int64_t sc = m0 + q;
-      if (sc < n_sc) {
-        const int buf = static_cast<int>(sc & 1);
+    for (int j = 0; j < 4; ++j) {
+      // the k-step's eight token fragments are read together, so their LDS
+      // latencies overlap, then multiplied
+      i32x4 xf[8];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+      for (int t = 0; t < 8; ++t)
+        xf[t] = *reinterpret_cast<const i32x4*>(
+            &xl[buf][(16 * t + n) * kPitch + 64 * j + 16 * g]);
 #pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            const i32x4 xf = *reinterpret_cast<const i32x4*>(
-                &xl[buf][(16 * t + n) * kPitch + 64 * j + 16 * g]);
-            acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wall[4 * q + j], xf,
-                                                           acc[t], 0, 0, 0);
-            // keeps each accumulator in its own AGPRs (without it the
-            // compiler rotates all 32 accumulator registers every pass)
-            asm volatile("" : "+a"(acc[t]));
-          }
-        }
-        if (sc + 1 < n_sc) {
-          store_x(buf ^ 1);                 // buffer read two steps ago
-          if (sc + 2 < n_sc) load_x((sc + 2) * kKS);
-          if (q + 1 < kSCM) lds_barrier();  // loads stay in flight
-        }
-      }
+      for (int t = 0; t < 8; ++t)
+        acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wc[j], xf[t], acc[t], 0, 0, 0);
+      // keeps each accumulator in its own AGPRs (without it the compiler
+      // rotates all 32 accumulator registers every pass); one pin per
+      // k-step, since an asm statement also bounds instruction scheduling
+      asm volatile("" : "+a"(acc[0]), "+a"(acc[1]), "+a"(acc[2]), "+a"(acc[3]),
+                        "+a"(acc[4]), "+a"(acc[5]), "+a"(acc[6]), "+a"(acc[7]));
     }
+    if (sc + 1 < n_sc) {
+      store_x(buf ^ 1);                     // buffer read two steps ago
+      if (sc + 2 < n_sc) load_x((sc + 2) * kKS);
+      lds_barrier();                        // loads stay in flight
+    }
+  };
+
+  i32x4 w0[4], w1[4], w2[4], w3[4];
+  load_x(0);
+  load_w(w0, 0);
+  if (n_sc > 1) load_w(w1, 1);
+  if (n_sc > 2) load_w(w2, 2);
+  store_x(0);
+  if (n_sc > 1) load_x(kKS);
+  lds_barrier();                            // super-chunk 0 staged
+  for (int64_t sc = 0; sc < n_sc; sc += kWD + 1) {
+    step(sc, w0, w3);
+    step(sc + 1, w1, w0);
+    step(sc + 2, w2, w1);
+    step(sc + 3, w3, w2);
   }
   if (!rows_ok) return;
   // lane (g, n) of tile t: rows o0 + 4 g + r, token b0 + 16 t + n
