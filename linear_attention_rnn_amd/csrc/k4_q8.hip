@@ -278,6 +278,84 @@ void q8_matmul_kernel(const int8_t* __restrict__ wq,
   }
 }
 
+// ---------------- few tokens: matrix-vector form ----------------
+//
+// With at most kGemvMaxB tokens the product is a stream over the weight
+// codes: one wavefront per kGemvRows output rows, each lane taking 16 bytes
+// of every row per 1024-byte chunk of k (two chunks of all rows per pass,
+// their loads issued together),
+// packed int8 dot products into int32, then a wavefront sum per (token,
+// row). The sums are exact, so the result equals the tiled kernel's bit for
+// bit.
+
+constexpr int kGemvRows = 8;     // output rows per wavefront (O % 16 == 0)
+constexpr int kGemvMaxB = 4;     // tokens handled this way
+
+// sum over the wavefront; the result is wavefront-uniform
+__device__ __forceinline__ int wave_sum_i32(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false);   // lane ^ 1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false);   // lane ^ 2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false);  // 7 - l in 8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x140, 0xF, 0xF, false);  // 15 - l in 16
+  return __builtin_amdgcn_readlane(x, 0) + __builtin_amdgcn_readlane(x, 16) +
+         __builtin_amdgcn_readlane(x, 32) + __builtin_amdgcn_readlane(x, 48);
+}
+
+template <int NB>
+__global__ __launch_bounds__(256)
+void q8_gemv_kernel(const int8_t* __restrict__ wq,
+                    const float* __restrict__ ws, int64_t O, int64_t I,
+                    const int8_t* __restrict__ xq,
+                    const float* __restrict__ xs, float* __restrict__ y) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int64_t o0 = wave * kGemvRows;
+  if (o0 >= O) return;                     // O % 16 == 0: all rows or none
+  int acc[NB][kGemvRows];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int r = 0; r < kGemvRows; ++r) acc[b][r] = 0;
+  // two 1024-byte chunks of every row per pass, all loads issued before the
+  // first dot product (the scheduling barrier keeps them together)
+  for (int64_t c0 = 0; c0 < I; c0 += 2048) {
+    i32x4 w[2][kGemvRows], x[2][NB];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int64_t k = c0 + 1024 * h + 16 * lane;
+      const bool ok = k < I;                 // I % 64 == 0: whole 16-byte groups
+#pragma unroll
+      for (int r = 0; r < kGemvRows; ++r)
+        w[h][r] = ok ? *reinterpret_cast<const i32x4*>(wq + (o0 + r) * I + k)
+                     : i32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        x[h][b] = ok ? *reinterpret_cast<const i32x4*>(xq + b * I + k)
+                     : i32x4{0, 0, 0, 0};
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int r = 0; r < kGemvRows; ++r)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            acc[b][r] = __builtin_amdgcn_sdot4(w[h][r][q], x[h][b][q], acc[b][r], false);
+  }
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const float sx = xs[b];
+#pragma unroll
+    for (int r = 0; r < kGemvRows; ++r) {
+      const int sum = wave_sum_i32(acc[b][r]);
+      if (lane == r)
+        y[b * O + o0 + r] = static_cast<float>(sum) * (ws[o0 + r] * sx);
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_q8_quantize(const void* x, int dtype, int64_t rows,
@@ -310,6 +388,18 @@ hipError_t launch_q8_matmul(const int8_t* wq, const float* ws, int64_t O,
                             int64_t I, const int8_t* xq, const float* xs,
                             int64_t B, float* y, hipStream_t stream) {
   if (O <= 0 || B <= 0) return hipSuccess;
+  if (B <= kGemvMaxB) {
+    const int64_t blocks = (O / kGemvRows + 3) / 4;
+    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const dim3 grid(static_cast<unsigned>(blocks)), block(256);
+    switch (B) {
+      case 1: hipLaunchKernelGGL(q8_gemv_kernel<1>, grid, block, 0, stream, wq, ws, O, I, xq, xs, y); break;
+      case 2: hipLaunchKernelGGL(q8_gemv_kernel<2>, grid, block, 0, stream, wq, ws, O, I, xq, xs, y); break;
+      case 3: hipLaunchKernelGGL(q8_gemv_kernel<3>, grid, block, 0, stream, wq, ws, O, I, xq, xs, y); break;
+      default: hipLaunchKernelGGL(q8_gemv_kernel<4>, grid, block, 0, stream, wq, ws, O, I, xq, xs, y); break;
+    }
+    return hipGetLastError();
+  }
   const int64_t gx = (O + kRowsWG - 1) / kRowsWG;
   const int64_t gy = (B + kTokWG - 1) / kTokWG;
   if (gx > 0x7fffffff || gy > 65535) return hipErrorInvalidConfiguration;

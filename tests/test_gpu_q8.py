@@ -46,7 +46,8 @@ def test_quantize_bitexact(dtype):
 
 
 @pytest.mark.parametrize("O,I,B", [(48, 128, 1), (64, 256, 17), (208, 640, 130),
-                                   (16, 64, 300)])
+                                   (16, 64, 300), (64, 1088, 2), (32, 2112, 3),
+                                   (16, 64, 4), (1040, 2048, 1)])
 def test_matmul_matches_oracle(O, I, B):
     rng = np.random.default_rng(O + I + B)
     w = rng.standard_normal((O, I)).astype(np.float32)
@@ -62,6 +63,26 @@ def test_matmul_matches_oracle(O, I, B):
     say(f"q8 matmul O={O} I={I} B={B}: rel err {e:.2e}")
     assert np.all(np.isfinite(y.cpu().numpy()))
     assert e < TOL
+
+
+@pytest.mark.parametrize("B", [1, 2, 3, 4])
+def test_few_tokens_equal_tiled_product_bitwise(B):
+    """Up to four tokens take a matrix-vector kernel; the same tokens with a
+    fifth added take the tiled MFMA kernel. Integer sums are exact and the
+    rescale is the same, so their rows agree bit for bit."""
+    O, I = 96, 2112
+    rng = np.random.default_rng(40 + B)
+    w = torch.from_numpy(rng.standard_normal((O, I)).astype(np.float32)).to(DEV)
+    x = torch.from_numpy(rng.standard_normal((B + 1, I)).astype(np.float32)).to(DEV)
+    wq, ws = _quantize_dev(w)
+    xq, xs = _quantize_dev(x)
+    y_few = torch.empty((B, O), dtype=torch.float32, device=DEV)
+    y_all = torch.empty((B + 1, O), dtype=torch.float32, device=DEV)
+    W.wkv7_q8_matmul(wq, ws, xq[:B].contiguous(), xs[:B].contiguous(), y_few)
+    W.wkv7_q8_matmul(wq, ws, xq, xs, y_all)
+    torch.cuda.synchronize()
+    say(f"q8 few-token path, B={B}")
+    assert torch.equal(y_few.view(torch.int32), y_all[:B].view(torch.int32))
 
 
 def test_full_size_stacked_projection_sampled():
