@@ -272,6 +272,29 @@ def run_small(calls: int = 200, warmup: int = 20, seed: int = 0):
             t1 = time.perf_counter()
             out[f"{name}_us_per_call_wall"] = (t1 - t0) / calls * 1e6
             out[f"{name}_us_per_call_gpu"] = e0.elapsed_time(e1) / calls * 1e3
+        # the same plan call captured 50 times into one HIP graph (on torch's
+        # capture stream, current inside the block) and replayed
+        n_cap, reps = 50, max(1, calls // 50)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(n_cap):
+                W.wkv7_forward_plan(pool, plan, x["r"], x["w"], x["k"],
+                                    x["v"], x["a"], x["b"], o)
+        torch.cuda.synchronize()
+        graph.replay()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(reps):
+            graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        out["graph_us_per_call_wall"] = (t1 - t0) / (reps * n_cap) * 1e6
+        out["graph_us_per_call_gpu"] = e0.elapsed_time(e1) / (reps * n_cap) * 1e3
+        del graph
         W.wkv7_plan_destroy(plan)
     finally:
         W.wkv7_pool_destroy(pool)
@@ -604,9 +627,11 @@ def run_q8_proj(steps: int = 50, warmup: int = 5, seed: int = 5):
     """The INT8 projections upstream of the recurrence in decode: the six
     weight matrices r, w, k, v, a, b of a C=2048 layer stacked into one
     [12288, 2048] int8 matrix (quantized once, outside the timed region);
-    a step quantizes the B input rows (bf16) and runs the INT8 product.
-    B=256 (the decode batch) and B=1 (one sequence's matrix-vector
-    product), each timed with one event pair over K steps."""
+    a step quantizes the B input rows (bf16) and runs the INT8 product,
+    through wkv7_q8_linear (one launch for up to four tokens) and, for
+    reference, through wkv7_q8_quantize + wkv7_q8_matmul. B=256 (the decode
+    batch) and B=1 (one sequence's matrix-vector product), each timed with
+    one event pair over K steps."""
     import torch
     from linear_attention_rnn_amd import wkv7 as W
 
@@ -629,25 +654,33 @@ def run_q8_proj(steps: int = 50, warmup: int = 5, seed: int = 5):
         xsc = torch.empty(B, dtype=torch.float32, device=dev)
         y = torch.empty((B, O), dtype=torch.float32, device=dev)
 
-        def step(i):
+        def step_two(i):
             W.wkv7_q8_quantize(xs[i % 8], xq, xsc, stream=stream)
             W.wkv7_q8_matmul(wq, ws, xq, xsc, y, stream=stream)
 
-        for i in range(warmup):
-            step(i)
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for i in range(steps):
-            step(i)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) / steps * 1e3
+        def step(i):                    # one call (one launch for B <= 4)
+            W.wkv7_q8_linear(wq, ws, xs[i % 8], xq, xsc, y, stream=stream)
+
+        def timed(fn):
+            for i in range(warmup):
+                fn(i)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for i in range(steps):
+                fn(i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / steps * 1e3
+
+        us_two = timed(step_two)
+        us = timed(step)
         ops = 2.0 * B * O * C
         nbytes = O * C + 4 * O + B * C * 2 + B * C + 4 * B + 4 * B * O
         out[f"b{B}"] = {
-            "us_per_step": us, "tops": ops / (us * 1e-6) / 1e12,
+            "us_per_step": us, "two_calls_us_per_step": us_two,
+            "tops": ops / (us * 1e-6) / 1e12,
             "mfma_frac": ops / (us * 1e-6) / 1e12 / INT8_MFMA_PEAK_TOPS,
             "hbm_gbs": nbytes / (us * 1e-6) / 1e9,
             "hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,

@@ -328,6 +328,21 @@ wkv7_status wkv7_q8_matmul(const int8_t* wq, const float* w_scale,
                            const float* x_scale, int64_t B, float* y,
                            void* stream);
 
+/* linear — quantize the inputs and multiply: xq, x_scale = wkv7_q8_quantize
+ * of x [B][in] (dtype WKV7_F32 or WKV7_BF16) and y = wkv7_q8_matmul of wq,
+ * w_scale with them, the same bits as the two calls (page "RWKV-X
+ * Architecture", section "INT8 Quantization": the input is quantized once
+ * and every output row is an integer dot product, rescaled). For at most
+ * four tokens with in <= 2048 (a decode step's projections) it is one
+ * launch, which saves the separate quantization launch; otherwise the two.
+ * xq int8 [B][in] and x_scale float32 [B] are outputs owned by the caller;
+ * wq, w_scale, x, xq and y 16-byte aligned; in a multiple of 64, out of 16
+ * (else WKV7_ERR_UNSUPPORTED); inputs finite. */
+wkv7_status wkv7_q8_linear(const int8_t* wq, const float* w_scale,
+                           int64_t out, int64_t in, const void* x,
+                           int32_t dtype, int64_t B, int8_t* xq,
+                           float* x_scale, float* y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

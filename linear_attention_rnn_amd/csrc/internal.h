@@ -112,6 +112,12 @@ hipError_t launch_q8_quantize(const void* x, int dtype, int64_t rows,
 hipError_t launch_q8_matmul(const int8_t* wq, const float* ws, int64_t O,
                             int64_t I, const int8_t* xq, const float* xs,
                             int64_t B, float* y, hipStream_t stream);
+// Quantize x [B][I] (fp32 or bf16) into xq, xs and multiply: one launch for
+// at most four tokens with I <= 2048, otherwise the two launches above.
+hipError_t launch_q8_linear(const int8_t* wq, const float* ws, int64_t O,
+                            int64_t I, const void* x, int dtype, int64_t B,
+                            int8_t* xq, float* xs, float* y,
+                            hipStream_t stream);
 
 // Zero-fill n slots listed (device int32) in `ids`.
 hipError_t launch_zero_slots(float* pool, size_t slot_floats,

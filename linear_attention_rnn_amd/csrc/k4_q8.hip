@@ -356,6 +356,95 @@ void q8_gemv_kernel(const int8_t* __restrict__ wq,
   }
 }
 
+// Quantize and multiply in one launch, for few tokens with in <= 2048:
+// every wavefront starts its weight loads, then quantizes the inputs'
+// values at its lanes' k positions exactly as quantize_rows_kernel does
+// (the wavefront covers the whole row, so its maximum is the row's), and
+// runs the matrix-vector product on those codes. The first wavefront also
+// stores the codes and scales. Same codes, same integer sums, same rescale:
+// the same bits as the two separate launches.
+constexpr int64_t kFusedMaxI = 2048;
+
+template <int DT, int NB>
+__global__ __launch_bounds__(256)
+void q8_linear_kernel(const int8_t* __restrict__ wq,
+                      const float* __restrict__ ws, int64_t O, int64_t I,
+                      const typename Elem<DT>::T* __restrict__ x,
+                      int8_t* __restrict__ xq, float* __restrict__ xs,
+                      float* __restrict__ y) {
+  using E = Elem<DT>;
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int64_t o0 = wave * kGemvRows;
+  if (o0 >= O) return;                     // O % 16 == 0: all rows or none
+  i32x4 w[2][kGemvRows];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int64_t k = 1024 * h + 16 * lane;
+    const bool ok = k < I;                 // I % 64 == 0: whole 16-byte groups
+#pragma unroll
+    for (int r = 0; r < kGemvRows; ++r)
+      w[h][r] = ok ? *reinterpret_cast<const i32x4*>(wq + (o0 + r) * I + k)
+                   : i32x4{0, 0, 0, 0};
+  }
+  __builtin_amdgcn_sched_barrier(0);       // weight loads go out first
+  i32x4 xc[2][NB];
+  float sx[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    float v[2][16];
+    float m = 0.f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int64_t k = 1024 * h + 16 * lane;
+      if (k < I) {
+        E::get8(x + b * I + k, v[h]);
+        E::get8(x + b * I + k + 8, v[h] + 8);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) v[h][e] = 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(v[h][e]));
+    }
+    m = wave_max_abs(m);
+    const float sc = m / 127.0f;           // IEEE float32 division
+    sx[b] = sc;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        xc[h][b][q] = static_cast<int>(code(v[h][4 * q], sc) | code(v[h][4 * q + 1], sc) << 8 |
+                                       code(v[h][4 * q + 2], sc) << 16 |
+                                       code(v[h][4 * q + 3], sc) << 24);
+      const int64_t k = 1024 * h + 16 * lane;
+      if (wave == 0 && k < I) *reinterpret_cast<i32x4*>(xq + b * I + k) = xc[h][b];
+    }
+    if (wave == 0 && lane == 0) xs[b] = sc;
+  }
+  int acc[NB][kGemvRows];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int r = 0; r < kGemvRows; ++r) {
+      int a = 0;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          a = __builtin_amdgcn_sdot4(w[h][r][q], xc[h][b][q], a, false);
+      acc[b][r] = a;
+    }
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int r = 0; r < kGemvRows; ++r) {
+      const int sum = wave_sum_i32(acc[b][r]);
+      if (lane == r)
+        y[b * O + o0 + r] = static_cast<float>(sum) * (ws[o0 + r] * sx[b]);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_q8_quantize(const void* x, int dtype, int64_t rows,
@@ -406,6 +495,44 @@ hipError_t launch_q8_matmul(const int8_t* wq, const float* ws, int64_t O,
   hipLaunchKernelGGL(q8_matmul_kernel,
                      dim3(static_cast<unsigned>(gx), static_cast<unsigned>(gy)),
                      dim3(256), 0, stream, wq, ws, O, I, xq, xs, B, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_q8_linear(const int8_t* wq, const float* ws, int64_t O,
+                            int64_t I, const void* x, int dtype, int64_t B,
+                            int8_t* xq, float* xs, float* y,
+                            hipStream_t stream) {
+  if (O <= 0 || B <= 0) return hipSuccess;
+  const bool fused = B <= kGemvMaxB && I <= kFusedMaxI &&
+                     reinterpret_cast<uintptr_t>(x) % 16 == 0;
+  if (!fused) {
+    hipError_t e = launch_q8_quantize(x, dtype, B, I, xq, xs, stream);
+    if (e != hipSuccess) return e;
+    return launch_q8_matmul(wq, ws, O, I, xq, xs, B, y, stream);
+  }
+  const int64_t blocks = (O / kGemvRows + 3) / 4;
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  const dim3 grid(static_cast<unsigned>(blocks)), block(256);
+#define WKV7_Q8_LINEAR(DT, NB)                                                  \
+  hipLaunchKernelGGL((q8_linear_kernel<DT, NB>), grid, block, 0, stream, wq,     \
+                     ws, O, I, static_cast<const typename Elem<DT>::T*>(x), xq,  \
+                     xs, y)
+  if (dtype == WKV7_BF16) {
+    switch (B) {
+      case 1: WKV7_Q8_LINEAR(WKV7_BF16, 1); break;
+      case 2: WKV7_Q8_LINEAR(WKV7_BF16, 2); break;
+      case 3: WKV7_Q8_LINEAR(WKV7_BF16, 3); break;
+      default: WKV7_Q8_LINEAR(WKV7_BF16, 4); break;
+    }
+  } else {
+    switch (B) {
+      case 1: WKV7_Q8_LINEAR(WKV7_F32, 1); break;
+      case 2: WKV7_Q8_LINEAR(WKV7_F32, 2); break;
+      case 3: WKV7_Q8_LINEAR(WKV7_F32, 3); break;
+      default: WKV7_Q8_LINEAR(WKV7_F32, 4); break;
+    }
+  }
+#undef WKV7_Q8_LINEAR
   return hipGetLastError();
 }
 

@@ -833,6 +833,39 @@ wkv7_status wkv7_q8_matmul(const int8_t* wq, const float* w_scale,
   return WKV7_OK;
 }
 
+wkv7_status wkv7_q8_linear(const int8_t* wq, const float* w_scale,
+                           int64_t out, int64_t in, const void* x,
+                           int32_t dtype, int64_t B, int8_t* xq,
+                           float* x_scale, float* y, void* stream) {
+  g_last_error.clear();
+  if (dtype != WKV7_F32 && dtype != WKV7_BF16)
+    return fail(WKV7_ERR_UNSUPPORTED, "dtype %d unsupported", dtype);
+  if (out < 0 || in < 1 || B < 0)
+    return fail(WKV7_ERR_INVALID_ARG, "out=%lld, in=%lld, B=%lld",
+                static_cast<long long>(out), static_cast<long long>(in),
+                static_cast<long long>(B));
+  if (in % 64 != 0 || out % 16 != 0)
+    return fail(WKV7_ERR_UNSUPPORTED,
+                "q8 product needs in %% 64 == 0 and out %% 16 == 0 "
+                "(in=%lld, out=%lld)", static_cast<long long>(in),
+                static_cast<long long>(out));
+  if (out == 0 || B == 0) return WKV7_OK;
+  if (out * in >= (int64_t(1) << 31) || B * in >= (int64_t(1) << 31))
+    return fail(WKV7_ERR_UNSUPPORTED,
+                "q8 product operands must each be under 2 GiB of codes");
+  const void* ptrs[6] = {wq, w_scale, x, xq, x_scale, y};
+  const char* names[6] = {"wq", "w_scale", "x", "xq", "x_scale", "y"};
+  for (int i = 0; i < 6; ++i) {
+    if (!ptrs[i]) return fail(WKV7_ERR_INVALID_ARG, "%s is NULL", names[i]);
+    if (i != 4 && !aligned16(ptrs[i]))
+      return fail(WKV7_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[i]);
+  }
+  hipError_t e = wkv7::launch_q8_linear(wq, w_scale, out, in, x, dtype, B, xq,
+                                        x_scale, y, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail_hip(e, "q8 linear launch");
+  return WKV7_OK;
+}
+
 wkv7_status wkv7_image_header_init(wkv7_image_header* hdr, int32_t H,
                                    int32_t N, int32_t n_slots) {
   g_last_error.clear();

@@ -49,6 +49,7 @@ EXPORTS = (
     "wkv7_sessions_create", "wkv7_sessions_destroy", "wkv7_session_begin",
     "wkv7_session_end", "wkv7_session_abort", "wkv7_session_drop_chat",
     "wkv7_sessions_stats", "wkv7_q8_quantize", "wkv7_q8_matmul",
+    "wkv7_q8_linear",
 )
 
 # session outcomes and flags (include/wkv7_session.h)
@@ -180,6 +181,9 @@ lib.wkv7_q8_quantize.restype = _i32
 lib.wkv7_q8_quantize.argtypes = [_vp, _i32, _i64, _i64, _vp, _vp, _vp]
 lib.wkv7_q8_matmul.restype = _i32
 lib.wkv7_q8_matmul.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp]
+lib.wkv7_q8_linear.restype = _i32
+lib.wkv7_q8_linear.argtypes = [_vp, _vp, _i64, _i64, _vp, _i32, _i64, _vp, _vp,
+                               _vp, _vp]
 lib.wkv7_image_header_check.restype = _i32
 lib.wkv7_image_header_check.argtypes = [ctypes.POINTER(wkv7_image_header),
                                         _i32, _i32]
@@ -394,6 +398,17 @@ def wkv7_q8_matmul(wq, w_scale, xq, x_scale, y, stream=None) -> None:
     B = xq.shape[0]
     _check(lib.wkv7_q8_matmul(_dptr(wq), _dptr(w_scale), out, inn, _dptr(xq),
                               _dptr(x_scale), B, _dptr(y), _stream(stream)))
+
+
+def wkv7_q8_linear(wq, w_scale, x, xq, x_scale, y, stream=None) -> None:
+    """Quantize x [B, in] (float32 or bfloat16) into xq, x_scale and
+    y[B, out] = INT8 product of wq [out, in] with them."""
+    out, inn = wq.shape
+    B = x.shape[0]
+    _check(lib.wkv7_q8_linear(_dptr(wq), _dptr(w_scale), out, inn, _dptr(x),
+                              _dtype_code(x),
+                              B, _dptr(xq), _dptr(x_scale), _dptr(y),
+                              _stream(stream)))
 
 
 def wkv7_snapshot(pool: int, slot: int, dst, stream=None) -> None:

@@ -141,3 +141,14 @@ def test_q8_rejects_before_device():
         W.WKV7_ERR_UNSUPPORTED
     assert L.wkv7_q8_matmul(None, None, 16, 64, None, None, 1, None, None) == \
         W.WKV7_ERR_INVALID_ARG
+    # linear: dtype, shape and pointer checks, in that order
+    assert L.wkv7_q8_linear(None, None, 16, 64, None, 7, 1, None, None, None,
+                            None) == W.WKV7_ERR_UNSUPPORTED
+    assert L.wkv7_q8_linear(None, None, 16, 100, None, 0, 1, None, None, None,
+                            None) == W.WKV7_ERR_UNSUPPORTED
+    assert L.wkv7_q8_linear(None, None, 16, 64, None, 1, -1, None, None, None,
+                            None) == W.WKV7_ERR_INVALID_ARG
+    assert L.wkv7_q8_linear(None, None, 16, 64, None, 1, 1, None, None, None,
+                            None) == W.WKV7_ERR_INVALID_ARG
+    assert L.wkv7_q8_linear(None, None, 16, 64, None, 1, 0, None, None, None,
+                            None) == W.WKV7_OK            # nothing to do

@@ -85,6 +85,33 @@ def test_few_tokens_equal_tiled_product_bitwise(B):
     assert torch.equal(y_few.view(torch.int32), y_all[:B].view(torch.int32))
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("O,I,B", [(48, 64, 1), (96, 1088, 2), (32, 2048, 3),
+                                   (16, 2048, 4), (48, 2112, 2), (32, 256, 5)])
+def test_linear_equals_quantize_then_matmul(dtype, O, I, B):
+    """wkv7_q8_linear (one launch for up to four tokens with in <= 2048, two
+    otherwise) gives the same codes, scales and outputs, bit for bit, as
+    wkv7_q8_quantize followed by wkv7_q8_matmul."""
+    rng = np.random.default_rng(O * 7 + I + B)
+    w = torch.from_numpy(rng.standard_normal((O, I)).astype(np.float32)).to(DEV)
+    x = torch.from_numpy(rng.standard_normal((B, I)).astype(np.float32))
+    x = x.to(DEV).to(dtype)
+    x[0, 5] = 0.0
+    wq, ws = _quantize_dev(w)
+    xq1, xs1 = _quantize_dev(x)
+    y1 = torch.empty((B, O), dtype=torch.float32, device=DEV)
+    W.wkv7_q8_matmul(wq, ws, xq1, xs1, y1)
+    xq2 = torch.zeros((B, I), dtype=torch.int8, device=DEV)
+    xs2 = torch.full((B,), float("nan"), dtype=torch.float32, device=DEV)
+    y2 = torch.full((B, O), float("nan"), dtype=torch.float32, device=DEV)
+    W.wkv7_q8_linear(wq, ws, x, xq2, xs2, y2)
+    torch.cuda.synchronize()
+    say(f"q8 linear O={O} I={I} B={B} {dtype}")
+    assert torch.equal(xq1, xq2)
+    assert torch.equal(xs1.view(torch.int32), xs2.view(torch.int32))
+    assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
+
+
 def test_full_size_stacked_projection_sampled():
     """r,w,k,v,a,b weights of a C=2048 layer stacked into [12288, 2048],
     bf16, 256 decode tokens: 512 sampled outputs against exact integer dot
