@@ -676,10 +676,31 @@ def run_q8_proj(steps: int = 50, warmup: int = 5, seed: int = 5):
 
         us_two = timed(step_two)
         us = timed(step)
+        # the same steps replayed from a captured HIP graph (no host launch
+        # cost between kernels: the GPU's own rate for these short kernels)
+        n_cap = 20
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(n_cap):
+                W.wkv7_q8_linear(wq, ws, xs[i % 8], xq, xsc, y)
+        torch.cuda.synchronize()
+        graph.replay()
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        reps = max(1, steps // n_cap)
+        torch.cuda.synchronize()
+        g0.record(stream)
+        for _ in range(reps):
+            graph.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        us_graph = g0.elapsed_time(g1) / (reps * n_cap) * 1e3
+        del graph
         ops = 2.0 * B * O * C
         nbytes = O * C + 4 * O + B * C * 2 + B * C + 4 * B + 4 * B * O
         out[f"b{B}"] = {
             "us_per_step": us, "two_calls_us_per_step": us_two,
+            "graph_us_per_step": us_graph,
             "tops": ops / (us * 1e-6) / 1e12,
             "mfma_frac": ops / (us * 1e-6) / 1e12 / INT8_MFMA_PEAK_TOPS,
             "hbm_gbs": nbytes / (us * 1e-6) / 1e9,
