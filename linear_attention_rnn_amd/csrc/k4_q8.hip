@@ -9,17 +9,18 @@
 // scale 0 and codes 0), so codes and scales are reproducible bit for bit.
 //
 // The product y[b][o] = (sum_i wq[o][i] xq[b][i]) * ws[o] * xs[b] runs on
-// v_mfma_i32_16x16x64_i8 with exact int32 accumulation. A workgroup of four
-// wavefronts owns 64 output rows and up to 128 tokens. k advances in
-// super-chunks of 256: the tokens' codes go through two LDS buffers (shared
-// by the four wavefronts; the next super-chunk's codes are loaded while the
+// v_mfma_i32_16x16x64_i8 with exact int32 accumulation. A workgroup of 4 to
+// 8 wavefronts owns 16 output rows per wavefront and up to 128 tokens; the
+// launch takes the fewest wavefronts that put the grid on the CUs in one
+// round (otherwise four, two workgroups per CU). k advances in super-chunks
+// of 256: the tokens' codes go through two LDS buffers (staged by the first
+// four wavefronts; the next super-chunk's codes are loaded while the
 // current one is multiplied, one barrier per super-chunk), and each
 // wavefront streams its 16 weight rows through a ring of four super-chunk
 // register buffers, loaded three super-chunks ahead, reusing each fragment
 // for 8 token tiles. The weight codes are read from HBM once per token
 // block. A k-step's eight token fragments are read from LDS together before
-// its MFMAs, so their latencies overlap. The registers fit two workgroups
-// per CU.
+// its MFMAs, so their latencies overlap.
 //
 // MFMA operands: lane 16 g + n supplies row n of its operand with 16 bytes
 // for k = kb + 16 g .. kb + 16 g + 15 (the same k assignment for both
@@ -147,13 +148,14 @@ void quantize_rows_kernel(const typename Elem<DT>::T* __restrict__ x,
 
 // ---------------- INT8 product on MFMA ----------------
 
-constexpr int kRowsWG = 64;      // output rows per workgroup (16 per wave)
 constexpr int kTokWG = 128;      // tokens per workgroup (8 tiles of 16)
 constexpr int kKS = 256;         // k per super-chunk (4 MFMA k-steps)
 constexpr int kWD = 3;           // weight prefetch distance (super-chunks)
 constexpr int kPitch = kKS + 16; // LDS bytes per token row (padded)
 
-__global__ __launch_bounds__(256, 2)
+// blockDim.x = 64 W for W = 4..8 wavefronts (16 output rows each): the
+// launch picks W so that the grid fits the CUs in one round when it can.
+__global__ __launch_bounds__(512, 1)
 void q8_matmul_kernel(const int8_t* __restrict__ wq,
                       const float* __restrict__ ws, int64_t O, int64_t I,
                       const int8_t* __restrict__ xq,
@@ -165,7 +167,8 @@ void q8_matmul_kernel(const int8_t* __restrict__ wq,
   const int wv = tid >> 6;
   const int g = lane >> 4;
   const int n = lane & 15;
-  const int64_t o0 = static_cast<int64_t>(blockIdx.x) * kRowsWG + 16 * wv;
+  const int64_t o0 = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 2) + 16 * wv;
+  const bool stager = tid < 256;           // the first four wavefronts stage
   const int64_t b0 = static_cast<int64_t>(blockIdx.y) * kTokWG;
   const bool rows_ok = o0 < O;             // O % 16 == 0: all 16 rows or none
   // Loads go through buffer resources sized to the arrays: a token past B or
@@ -192,12 +195,14 @@ void q8_matmul_kernel(const int8_t* __restrict__ wq,
 
   i32x4 xr[8];
   auto load_x = [&](int64_t kb) {
+    if (!stager) return;
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       xr[e] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(
           xres, xoff + static_cast<int>(kb) + xstride * e, 0, 0));
   };
   auto store_x = [&](int buf) {
+    if (!stager) return;
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       *reinterpret_cast<i32x4*>(&xl[buf][(16 * e + st_tok) * kPitch + st_off]) =
@@ -489,12 +494,20 @@ hipError_t launch_q8_matmul(const int8_t* wq, const float* ws, int64_t O,
     }
     return hipGetLastError();
   }
-  const int64_t gx = (O + kRowsWG - 1) / kRowsWG;
+  // Wavefronts per workgroup: the fewest (4..8) that put the grid on the
+  // 256 CUs in one round, one workgroup per CU; else 4 (two workgroups per
+  // CU, several rounds). With 4 and more workgroups than CUs, part of the
+  // CUs would hold two while the rest hold one and finish early.
   const int64_t gy = (B + kTokWG - 1) / kTokWG;
+  int waves = 4;
+  for (int wc = 4; wc <= 8; ++wc) {
+    if (((O + 16 * wc - 1) / (16 * wc)) * gy <= 256) { waves = wc; break; }
+  }
+  const int64_t gx = (O + 16 * waves - 1) / (16 * waves);
   if (gx > 0x7fffffff || gy > 65535) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(q8_matmul_kernel,
                      dim3(static_cast<unsigned>(gx), static_cast<unsigned>(gy)),
-                     dim3(256), 0, stream, wq, ws, O, I, xq, xs, B, y);
+                     dim3(64 * waves), 0, stream, wq, ws, O, I, xq, xs, B, y);
   return hipGetLastError();
 }
 

@@ -47,7 +47,11 @@ def test_quantize_bitexact(dtype):
 
 @pytest.mark.parametrize("O,I,B", [(48, 128, 1), (64, 256, 17), (208, 640, 130),
                                    (16, 64, 300), (64, 1088, 2), (32, 2112, 3),
-                                   (16, 64, 4), (1040, 2048, 1)])
+                                   (16, 64, 4), (1040, 2048, 1),
+                                   # workgroups of 5, 7 and 8 wavefronts (the
+                                   # launch fits the grid on the CUs in one round)
+                                   (9600, 128, 200), (13440, 128, 200),
+                                   (16000, 128, 200)])
 def test_matmul_matches_oracle(O, I, B):
     rng = np.random.default_rng(O + I + B)
     w = rng.standard_normal((O, I)).astype(np.float32)
