@@ -215,6 +215,56 @@ def run_prefill(steps: int, warmup: int, seed: int = 2):
     }
 
 
+def run_prefill_f32(steps: int = 5, warmup: int = 3, seed: int = 2):
+    """The 8 x 4096 x H=32 prefill with fp32 inputs, which take the precise
+    chunked kernel (chunks of 64, every product in split-bf16 operands); one
+    step = reset the 8 slots + one plan forward, timed with an event pair
+    around the forward."""
+    import torch
+    import wkv7_inputs as G
+    from linear_attention_rnn_amd import wkv7 as W
+
+    dev = torch.device("cuda:0")
+    n_seq, T, H = 8, 4096, 32
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    x = G.draw_tokens_device(gen, n_seq * T, H, N, "f32", dev)
+    ids = np.arange(n_seq, dtype=np.int32)
+    cu = (np.arange(n_seq + 1) * T).astype(np.int32)
+    o = torch.empty((n_seq * T, H, N), dtype=torch.float32, device=dev)
+    pool = W.wkv7_pool_create(n_seq, H, N)
+    stream = torch.cuda.current_stream()
+    try:
+        plan = W.wkv7_plan_create(pool, ids, cu)
+        times = []
+        for i in range(warmup + steps):
+            W.wkv7_reset(pool, ids, stream=stream)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            W.wkv7_forward_plan(pool, plan, x["r"], x["w"], x["k"], x["v"],
+                                x["a"], x["b"], o, stream=stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if i >= warmup:
+                times.append(e0.elapsed_time(e1))
+        W.wkv7_plan_destroy(plan)
+    finally:
+        W.wkv7_pool_destroy(pool)
+    k_ms = float(np.mean(times))
+    tokens = n_seq * T
+    bytes_alg = tokens * H * (6 * N * 4 + N * 4) + n_seq * H * 2 * 4 * N * N
+    return {"workload": "prefill_b8_t4096_h32_f32in_f32state",
+            "kernel": "chunk_kernel (fp32 inputs, chunks of 64, split-bf16 "
+                      "products)",
+            "tokens_per_s": tokens / (k_ms * 1e-3), "kernel_ms": k_ms,
+            "hbm": {"achieved": bytes_alg / (k_ms * 1e-3) / 1e9,
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": bytes_alg / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                    "bytes_per_launch": bytes_alg},
+            "steps": steps, "warmup": warmup}
+
+
 def _draw_device(gen, T: int, H: int, dtype: str, dev, chunk: int = 16384):
     """Synthetic inputs [T, H, N] drawn on the device in token chunks (the
     float32 temporaries of a whole large batch would be several GB)."""
@@ -896,8 +946,8 @@ def main(argv=None) -> int:
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--legs",
                     default="decode,prefill,decode_cold,decode_large,"
-                            "prefill_ragged,mixed,prefill_long,q8_proj,"
-                            "small,ceilings",
+                            "prefill_f32,prefill_ragged,mixed,prefill_long,"
+                            "q8_proj,small,ceilings",
                     help="comma list of legs to run (profiling one kernel)")
     ap.add_argument("--prefill-steps", type=int, default=10)
     args = ap.parse_args(argv)
@@ -976,6 +1026,8 @@ def main(argv=None) -> int:
         line["decode_cold"] = run_decode_cold()
     if "small" in legs:
         line["small"] = run_small()
+    if not args.no_prefill and "prefill_f32" in legs:
+        line["prefill_f32"] = run_prefill_f32()
     if not args.no_prefill and "prefill_ragged" in legs:
         line["prefill_ragged"] = run_prefill_ragged()
     if "mixed" in legs:
