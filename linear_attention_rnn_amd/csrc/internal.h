@@ -91,9 +91,17 @@ hipError_t launch_chunked(const SeqArgs& args, bool precise,
 // Pipelined chunked-prefill kernel for bf16 inputs with an fp16 value side
 // (32-token chunks), over pool slots (args.items) or over segments
 // (launch_chunked_p_seg: `segs`, n_items of them; args.items unused).
-hipError_t launch_chunked_p(const SeqArgs& args, hipStream_t stream);
+hipError_t launch_chunked_p(const SeqArgs& args, hipStream_t stream,
+                            const WorkItem* dec = nullptr, int32_t n_dec = 0);
+// Segment items (SegItem) instead of pool slots; same kernel code.
 hipError_t launch_chunked_p_seg(const SeqArgs& args, const SegItem* segs,
-                                hipStream_t stream);
+                                hipStream_t stream, const WorkItem* dec = nullptr,
+                                int32_t n_dec = 0);
+// Trailing workgroups of a chunked-kernel launch that run n_dec decode
+// items (eight (item, head) pairs each).
+inline int64_t chunk_decode_blocks(int32_t n_dec, int32_t H) {
+  return n_dec > 0 ? (static_cast<int64_t>(n_dec) * H + 7) / 8 : 0;
+}
 // Carry scan of split sequences: one workgroup per (sequence, head).
 hipError_t launch_seg_scan(const ScanItem* items, int32_t n_items, int32_t H,
                            hipStream_t stream);

@@ -52,6 +52,8 @@
 namespace wkv7 {
 namespace {
 
+#include "seq_wave.h"
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -420,9 +422,15 @@ __device__ __forceinline__ void exact_chunk(const SeqArgs& p, f32x4* S, int t0,
 
 // SEG = false: items are pool slots (p.items); true: segments (segs) with
 // their own state buffers and flags.
+// Workgroups past the (item, head) grid run the decode work items `dec` of
+// the same call, eight (item, head) pairs per workgroup, one per
+// wavefront, with the sequential recurrence (the same bits as the
+// sequential kernel): a batch's decode tokens then fill CUs that its
+// prefills leave idle, in the same launch.
 template <bool SEG>
 __global__ __launch_bounds__(512, 1)
-void chunk_p_kernel(SeqArgs p, const SegItem* segs) {
+void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
+                    int32_t n_dec) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
   __bf16* GR = reinterpret_cast<__bf16*>(lds + kOffGR);
   __bf16* Ahat = GR;                       // pair [t][j]
@@ -437,6 +445,14 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t n_main = static_cast<int64_t>(p.n_items) * p.H;
+  if (static_cast<int64_t>(blockIdx.x) >= n_main) {
+    const int64_t q = (static_cast<int64_t>(blockIdx.x) - n_main) * 8 + wv;
+    const int di = static_cast<int>(q / p.H);
+    const int dh = static_cast<int>(q - static_cast<int64_t>(di) * p.H);
+    if (di < n_dec) seqw::seq_wave<WKV7_BF16, false>(p, dec[di], dh, lane);
+    return;
+  }
   const bool is_key = wv < 4;
   const int g = lane >> 4;
   const int n16 = lane & 15;
@@ -802,22 +818,26 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs) {
 
 }  // namespace
 
-hipError_t launch_chunked_p(const SeqArgs& args, hipStream_t stream) {
+hipError_t launch_chunked_p(const SeqArgs& args, hipStream_t stream,
+                            const WorkItem* dec, int32_t n_dec) {
   if (args.n_items <= 0) return hipSuccess;
-  const int64_t blocks = static_cast<int64_t>(args.n_items) * args.H;
+  const int64_t blocks = static_cast<int64_t>(args.n_items) * args.H +
+                         chunk_decode_blocks(n_dec, args.H);
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(chunk_p_kernel<false>, dim3(static_cast<unsigned>(blocks)),
-                     dim3(512), 0, stream, args, nullptr);
+                     dim3(512), 0, stream, args, nullptr, dec, n_dec);
   return hipGetLastError();
 }
 
 hipError_t launch_chunked_p_seg(const SeqArgs& args, const SegItem* segs,
-                                hipStream_t stream) {
+                                hipStream_t stream, const WorkItem* dec,
+                                int32_t n_dec) {
   if (args.n_items <= 0) return hipSuccess;
-  const int64_t blocks = static_cast<int64_t>(args.n_items) * args.H;
+  const int64_t blocks = static_cast<int64_t>(args.n_items) * args.H +
+                         chunk_decode_blocks(n_dec, args.H);
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(chunk_p_kernel<true>, dim3(static_cast<unsigned>(blocks)),
-                     dim3(512), 0, stream, args, segs);
+                     dim3(512), 0, stream, args, segs, dec, n_dec);
   return hipGetLastError();
 }
 

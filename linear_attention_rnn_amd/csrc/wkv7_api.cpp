@@ -84,6 +84,7 @@ struct wkv7_pool {
   size_t seg_scratch_floats = 0;
   float* xfer_stage = nullptr;       // staging of scattered hibernate/resume
   size_t xfer_stage_bytes = 0;
+  int n_cus = 0;                     // compute units of the pool's device
   std::vector<int32_t> free_ids;     // stack; top = back
   std::vector<uint8_t> allocated;
   Stage ring[kRing];
@@ -377,24 +378,39 @@ wkv7_status check_forward_args(int32_t dtype, int64_t T_tot, const void* r,
 // launches: segment transitions and zero-start states together with the
 // unsplit chunked sequences, the carry scan, the segments' outputs); on the
 // other chunked paths every chunked sequence runs whole.
+// Decode items (the sequential kernel's work) ride in trailing workgroups of
+// the batch's chunked launch when the two together fit the CUs in one round
+// (the chunked kernel holds one workgroup per CU); with segment-parallel
+// prefill that is the output launch (phase 3: one item per segment, never
+// more than the transition launch, which has two per non-last segment plus
+// the unsplit sequences). Otherwise, or when the chunked work takes another
+// kernel, they get a launch of their own. Either way the decode items
+// compute the same bits.
 wkv7_status launch_batch(const wkv7_pool* p, const wkv7::Launch& L,
                          int32_t dtype, const void* r, const void* w,
                          const void* k, const void* v, const void* a,
                          const void* b, float* o, hipStream_t hs) {
   wkv7::SeqArgs args{p->state, nullptr, 0, p->H, dtype, r, w, k, v, a, b, o};
-  if (L.n_seq > 0) {
+  const bool fast = dtype == WKV7_BF16 && !p->chunk_precise;
+  const bool segmented = L.n_phase3 > 0 && fast;
+  bool fuse = false;
+  if (L.n_seq > 0 && fast) {
+    const int64_t chunk_items = segmented ? L.n_phase3 : L.n_chunk_all;
+    fuse = chunk_items > 0 &&
+           chunk_items * p->H + wkv7::chunk_decode_blocks(L.n_seq, p->H) <= p->n_cus;
+  }
+  if (L.n_seq > 0 && !fuse) {
     args.items = L.seq;
     args.n_items = L.n_seq;
     hipError_t e = wkv7::launch_seq(args, hs);
     if (e != hipSuccess) return fail_hip(e, "sequential kernel launch");
   }
-  const bool segmented = L.n_phase3 > 0 && dtype == WKV7_BF16 &&
-                         !p->chunk_precise;
   if (!segmented) {
     if (L.n_chunk_all > 0) {
       args.items = L.chunk_all;
       args.n_items = L.n_chunk_all;
-      hipError_t e = wkv7::launch_chunked(args, p->chunk_precise, hs);
+      hipError_t e = fuse ? wkv7::launch_chunked_p(args, hs, L.seq, L.n_seq)
+                          : wkv7::launch_chunked(args, p->chunk_precise, hs);
       if (e != hipSuccess) return fail_hip(e, "chunked kernel launch");
     }
     return WKV7_OK;
@@ -406,7 +422,8 @@ wkv7_status launch_batch(const wkv7_pool* p, const wkv7::Launch& L,
   e = wkv7::launch_seg_scan(L.scan, L.n_scan, p->H, hs);
   if (e != hipSuccess) return fail_hip(e, "segment scan launch");
   args.n_items = L.n_phase3;
-  e = wkv7::launch_chunked_p_seg(args, L.phase3, hs);
+  e = fuse ? wkv7::launch_chunked_p_seg(args, L.phase3, hs, L.seq, L.n_seq)
+           : wkv7::launch_chunked_p_seg(args, L.phase3, hs);
   if (e != hipSuccess) return fail_hip(e, "segment prefill launch");
   return WKV7_OK;
 }
@@ -469,6 +486,9 @@ wkv7_status wkv7_pool_create(int32_t n_slots, int32_t H, int32_t N,
   if (!p) return fail(WKV7_ERR_OOM, "host allocation failed");
   hipError_t e = hipGetDevice(&p->device);
   if (e != hipSuccess) { delete p; return fail_hip(e, "hipGetDevice"); }
+  e = hipDeviceGetAttribute(&p->n_cus, hipDeviceAttributeMultiprocessorCount,
+                            p->device);
+  if (e != hipSuccess) { delete p; return fail_hip(e, "hipDeviceGetAttribute"); }
   p->n_slots = n_slots;
   p->H = H;
   p->N = N;
