@@ -894,6 +894,7 @@ def cpu_baseline(seconds: float, seed: int = 1, max_workers: int = 16):
 
     tok1, t1 = _oracle_decode_slice(0, 256, seed, seconds)
     single = tok1 / t1
+    _progress(f"cpu baseline: one core {single:.0f} tokens/s")
     cores = max(1, min(max_workers, len(os.sched_getaffinity(0))))
     value, used, sample_par = single, 1, ""
     if cores > 1:
@@ -935,13 +936,19 @@ def _cpu_model() -> str:
     return "unknown CPU"
 
 
+def _progress(msg: str) -> None:
+    """One line per finished leg on stderr (stdout carries only the JSON
+    line), so that a long run shows it is alive."""
+    print(f"bench.py: {msg}", file=sys.stderr, flush=True)
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--legs",
@@ -984,6 +991,7 @@ def main(argv=None) -> int:
         print(json.dumps(out), flush=True)
         return 0
     d = run_decode(args.steps, args.warmup)
+    _progress(f"decode: {d['kernel_ms'] * 1e3:.1f} us per launch")
     achieved = d["bytes_per_launch"] / (d["kernel_ms"] * 1e-3) / 1e9
     traffic = load_traffic("decode", d["bytes_per_launch"])
     line = {
@@ -1020,25 +1028,35 @@ def main(argv=None) -> int:
     }
     if not args.no_prefill and "prefill" in legs:
         line["prefill"] = run_prefill(args.prefill_steps, 20)
+        _progress("prefill done")
     if "decode_large" in legs:
         line["decode_large"] = run_decode_large()
+        _progress("decode_large done")
     if "decode_cold" in legs:
         line["decode_cold"] = run_decode_cold()
+        _progress("decode_cold done")
     if "small" in legs:
         line["small"] = run_small()
+        _progress("small done")
     if not args.no_prefill and "prefill_f32" in legs:
         line["prefill_f32"] = run_prefill_f32()
+        _progress("prefill_f32 done")
     if not args.no_prefill and "prefill_ragged" in legs:
         line["prefill_ragged"] = run_prefill_ragged()
+        _progress("prefill_ragged done")
     if "mixed" in legs:
         line["mixed"] = run_mixed()
         line["mixed_segmented"] = run_mixed(segment_len=512)
+        _progress("mixed done")
     if not args.no_prefill and "prefill_long" in legs:
         line["prefill_long"] = run_prefill_long()
+        _progress("prefill_long done")
     if "q8_proj" in legs:
         line["q8_proj"] = run_q8_proj()
+        _progress("q8_proj done")
     if "ceilings" in legs:
         c = run_ceilings()
+        _progress("ceilings done")
         line["ceilings"] = c
         _with_ceiling(line["roofline"], achieved, c["hbm_ceiling_decode"])
         if "prefill" in line:
@@ -1058,6 +1076,7 @@ def main(argv=None) -> int:
             hr["pcie_d2h_contiguous_GBps"] = c["pcie_d2h_256MiB"]
             hr["pcie_h2d_contiguous_GBps"] = c["pcie_h2d_256MiB"]
     if not args.no_cpu_baseline:
+        _progress("cpu baseline (oracle) running")
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(line), flush=True)
     return 0
