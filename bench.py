@@ -16,6 +16,7 @@ built, a chunked-prefill leg (8 sequences of 4096 tokens, H=32).
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -938,7 +939,11 @@ def _cpu_model() -> str:
 
 def _progress(msg: str) -> None:
     """One line per finished leg on stderr (stdout carries only the JSON
-    line), so that a long run shows it is alive."""
+    line), so that a long run shows it is alive. Python's cyclic garbage
+    collector is off while legs run (a full collection inside a timed loop
+    of short calls shows up as host time per call, as timeit avoids too);
+    it runs here, between legs."""
+    gc.collect()
     print(f"bench.py: {msg}", file=sys.stderr, flush=True)
 
 
@@ -972,6 +977,8 @@ def main(argv=None) -> int:
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 2
+    gc.collect()
+    gc.disable()
 
     legs = set(args.legs.split(","))
     if legs == {"prefill"}:
