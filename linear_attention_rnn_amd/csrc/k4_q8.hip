@@ -8,24 +8,14 @@
 // would (IEEE division, roundf: halves away from zero; an all-zero row has
 // scale 0 and codes 0), so codes and scales are reproducible bit for bit.
 //
-// The product y[b][o] = (sum_i wq[o][i] xq[b][i]) * ws[o] * xs[b] runs on
-// v_mfma_i32_16x16x64_i8 with exact int32 accumulation. A workgroup of 4 to
-// 8 wavefronts owns 16 output rows per wavefront and up to 128 tokens; the
-// launch takes the fewest wavefronts that put the grid on the CUs in one
-// round (otherwise four, two workgroups per CU). k advances in super-chunks
-// of 256: the tokens' codes go through two LDS buffers (staged by the first
-// four wavefronts; the next super-chunk's codes are loaded while the
-// current one is multiplied, one barrier per super-chunk), and each
-// wavefront streams its 16 weight rows through a ring of four super-chunk
-// register buffers, loaded three super-chunks ahead, reusing each fragment
-// for 8 token tiles. The weight codes are read from HBM once per token
-// block. A k-step's eight token fragments are read from LDS together before
-// its MFMAs, so their latencies overlap.
-//
-// MFMA operands: lane 16 g + n supplies row n of its operand with 16 bytes
-// for k = kb + 16 g .. kb + 16 g + 15 (the same k assignment for both
-// operands, so the sum is over every k once); the result lane holds
-// C[4 g + r][n].
+// The product y[b][o] = (sum_i wq[o][i] xq[b][i]) * ws[o] * xs[b] is exact
+// int32 accumulation followed by one float32 rescale, in two kernels that
+// give the same bits: for more than four tokens a tiled kernel on
+// v_mfma_i32_32x32x32_i8 (96 output rows x 128 tokens per workgroup, a
+// staging wavefront feeding the tokens' codes into LDS by direct-to-LDS
+// loads, the weights streamed into registers; described at the kernel),
+// for up to four tokens a stream over the weight codes with packed int8
+// dot products.
 
 #include "internal.h"
 #include "../../include/wkv7.h"
@@ -146,140 +136,297 @@ void quantize_rows_kernel(const typename Elem<DT>::T* __restrict__ x,
     qr[i] = static_cast<int8_t>(code(E::get(xr, i), s));
 }
 
+// Few rows (the tokens of one step): one 256-thread workgroup per row, the
+// four wavefronts taking the row's 512-value chunks in turn (at most two
+// each), so that every SIMD works; the wavefront maxima meet in LDS. The
+// same maximum (max is exact in any order), division and rounding as the
+// one-wavefront kernel, so the same codes and scales.
+constexpr int kSplitMaxRows = 1024;    // fewer rows take this kernel
+
+template <int DT>
+__global__ __launch_bounds__(256)
+void quantize_split_kernel(const typename Elem<DT>::T* __restrict__ x,
+                           int64_t rows, int64_t cols, int8_t* __restrict__ q,
+                           float* __restrict__ scale) {
+  using E = Elem<DT>;
+  __shared__ float red[4];
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int64_t row = blockIdx.x;
+  if (row >= rows) return;
+  const typename E::T* xr = x + row * cols;
+  int8_t* qr = q + row * cols;
+  const int nch = static_cast<int>((cols + 511) / 512);
+  float v[2][8];
+  float m = 0.f;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int c = wv + 4 * u;
+    const int64_t i = 512 * c + 8 * lane;
+    if (c < nch && i < cols) {
+      E::get8(xr + i, v[u]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[u][e] = 0.f;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[u][e]));
+  m = wave_max_abs(m);
+  if (lane == 0) red[wv] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = m / 127.0f;                 // IEEE float32 division
+  if (threadIdx.x == 0) scale[row] = s;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int c = wv + 4 * u;
+    const int64_t i = 512 * c + 8 * lane;
+    if (c < nch && i < cols) {
+      uint2 packed;
+      packed.x = code(v[u][0], s) | code(v[u][1], s) << 8 |
+                 code(v[u][2], s) << 16 | code(v[u][3], s) << 24;
+      packed.y = code(v[u][4], s) | code(v[u][5], s) << 8 |
+                 code(v[u][6], s) << 16 | code(v[u][7], s) << 24;
+      *reinterpret_cast<uint2*>(qr + i) = packed;
+    }
+  }
+}
+
 // ---------------- INT8 product on MFMA ----------------
 
-constexpr int kTokWG = 128;      // tokens per workgroup (8 tiles of 16)
-constexpr int kKS = 256;         // k per super-chunk (4 MFMA k-steps)
-constexpr int kWD = 3;           // weight prefetch distance (super-chunks)
-constexpr int kPitch = kKS + 16; // LDS bytes per token row (padded)
+constexpr int kRowsW = 32;       // output rows per compute wavefront
+constexpr int kCompW = 3;        // compute wavefronts per workgroup
+constexpr int kRowsWG = kRowsW * kCompW;
+constexpr int kTokWG = 128;      // tokens per workgroup (4 tiles of 32)
+constexpr int kKS = 128;         // k per super-chunk (4 MFMA k-steps of 32)
+constexpr int kNBuf = 6;         // LDS token buffers (super-chunks)
+constexpr int kWRing = 8;        // weight register ring (super-chunks)
+constexpr int kBufBytes = kTokWG * kKS;
+typedef int i32x16 __attribute__((ext_vector_type(16)));
 
-// blockDim.x = 64 W for W = 4..8 wavefronts (16 output rows each): the
-// launch picks W so that the grid fits the CUs in one round when it can.
-__global__ __launch_bounds__(512, 1)
+// Barrier without a wait on the wavefront's own LDS reads (those in flight
+// target a buffer nobody writes before the next barrier); the asm
+// statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void plain_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Workgroup: 96 output rows x 128 tokens, 256 threads. Wavefronts 0-2
+// compute, 32 rows each, on v_mfma_i32_32x32x32_i8 (four 32 x 32 tiles of
+// int32 accumulators); wavefront 3 stages the tokens' codes.
+//
+// k advances in super-chunks of 128. The staging wavefront copies each
+// super-chunk's codes (128 tokens x 128 bytes) from HBM straight into one
+// of six LDS buffers (16-byte direct-to-LDS loads, no registers), five
+// super-chunks ahead, and before each step's barrier waits for the
+// super-chunk two ahead; the compute wavefronts may therefore read the
+// next super-chunk's first fragments before that barrier, and their LDS
+// reads run one k-step ahead of the MFMAs throughout. Each compute
+// wavefront streams its 32 weight rows through a ring of eight
+// super-chunk register buffers (loads seven super-chunks ahead). Every
+// load is issued whether or not its super-chunk exists (past the end:
+// zeros or unused), so within each role the compiler's count of loads in
+// flight is exact and each wait covers only the load it needs.
+//
+// LDS layout of a buffer: token r's 16-byte chunk c (k = 16 c .. 16 c + 15
+// of the super-chunk) sits at r * 128 + 16 (c ^ (r & 7)): the eight tokens
+// read together by a quarter wavefront then hit eight different bank
+// groups, and each direct-to-LDS load (lane i to byte 16 i) still covers
+// eight whole token rows.
+//
+// MFMA operands: lane 32 h + n supplies row n of its operand with 16 bytes
+// for k = kb + 16 h .. kb + 16 h + 15 (the same k assignment for both
+// operands); accumulator register a of lane 32 h + n holds
+// C[8 (a / 4) + 4 h + a % 4][n].
+__global__ __launch_bounds__(256, 1)
 void q8_matmul_kernel(const int8_t* __restrict__ wq,
                       const float* __restrict__ ws, int64_t O, int64_t I,
                       const int8_t* __restrict__ xq,
                       const float* __restrict__ xs, int64_t B,
                       float* __restrict__ y) {
-  __shared__ __attribute__((aligned(16))) int8_t xl[2][kTokWG * kPitch];
+  __shared__ __attribute__((aligned(16))) int8_t xl[kNBuf * kBufBytes];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wv = tid >> 6;
-  const int g = lane >> 4;
-  const int n = lane & 15;
-  const int64_t o0 = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 2) + 16 * wv;
-  const bool stager = tid < 256;           // the first four wavefronts stage
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t b0 = static_cast<int64_t>(blockIdx.y) * kTokWG;
-  const bool rows_ok = o0 < O;             // O % 16 == 0: all 16 rows or none
-  // Loads go through buffer resources sized to the arrays: a token past B or
-  // a row past O reads as zeros, with no branch. k-steps past I are zeroed
-  // on the weight side, so whatever the token side reads there adds 0.
+  const int64_t n_sc = (I + kKS - 1) / kKS;   // I % 64 == 0
+  // Loads go through buffer resources sized to the arrays: a token past B
+  // or a row past O reads as zeros (or, past 2^32 bytes of offset, codes
+  // of other rows and tokens, whose results are never stored); k past I
+  // is zero on the weight side, so whatever the token side reads there
+  // adds 0.
   const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<int8_t*>(xq), 0, static_cast<int>(B * I), 0x00020000);
   const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<int8_t*>(wq), 0, static_cast<int>(O * I), 0x00020000);
-  // staging: thread t copies 16 bytes of tokens 16 e + t / 16 (e = 0..7) at
-  // k offset 16 (t % 16): each load instruction covers four whole 256-byte
-  // token rows of the super-chunk
-  const int st_tok = tid >> 4;
-  const int st_off = 16 * (tid & 15);
-  const int xoff = static_cast<int>((b0 + st_tok) * I) + st_off;
-  const int xstride = static_cast<int>(16 * I);         // 16 tokens
-  // weight fragment of k-step j: bytes kb + 64 j + 16 g of row o0 + n
-  const int woff = static_cast<int>((o0 + n) * I) + 16 * g;
-  const int64_t n_sc = (I + kKS - 1) / kKS;    // I % 64 == 0
 
-  i32x4 acc[8];
+  if (wv == kCompW) {
+    // ---- staging wavefront ----
+    // load q (0..15) of a super-chunk fills buffer rows 8 q .. 8 q + 7;
+    // lane i: row 8 q + i / 8, position i % 8, so chunk (i % 8) ^ (i / 8)
+    // (offsets are 32-bit unsigned: past 2^32 they wrap, see above)
+    const int pr = lane >> 3;
+    const int ch = (lane & 7) ^ pr;
+    const uint32_t xo = static_cast<uint32_t>((b0 + pr) * I) + 16u * ch;
+    const uint32_t qstride = static_cast<uint32_t>(8 * I);
+    auto fill = [&](int64_t sc) {
+      int8_t* buf = xl + static_cast<int>(sc % kNBuf) * kBufBytes;
+      const uint32_t ko = xo + static_cast<uint32_t>(sc * kKS);
 #pragma unroll
-  for (int t = 0; t < 8; ++t) acc[t] = i32x4{0, 0, 0, 0};
+      for (int q = 0; q < 16; ++q)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            xres, (__attribute__((address_space(3))) void*)(buf + 1024 * q), 16,
+            static_cast<int>(ko + q * qstride), 0, 0, 0);
+    };
+    // super-chunks 0 .. kNBuf - 2 in flight; 0 and 1 complete before the
+    // first barrier (16 loads per super-chunk, counted in order)
+#pragma unroll
+    for (int c = 0; c < kNBuf - 1; ++c) fill(c);
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (((kNBuf - 3) * 16) & 15) |
+                               ((((kNBuf - 3) * 16) >> 4) << 14));
+    plain_barrier();
+    for (int64_t sc = 0; sc < n_sc; ++sc) {
+      // buffer (sc - 1) % kNBuf was read in the step before, which every
+      // compute wavefront has left
+      fill(sc + kNBuf - 1);
+      // super-chunk sc + 2 complete (sc + 3 .. sc + kNBuf - 1 in flight)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | (((kNBuf - 3) * 16) & 15) |
+                                 ((((kNBuf - 3) * 16) >> 4) << 14));
+      plain_barrier();
+    }
+    // the last loads (past the end, never read) have landed before the
+    // compute wavefronts reuse the buffers for their outputs
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    plain_barrier();
+    return;
+  }
 
-  i32x4 xr[8];
-  auto load_x = [&](int64_t kb) {
-    if (!stager) return;
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      xr[e] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(
-          xres, xoff + static_cast<int>(kb) + xstride * e, 0, 0));
-  };
-  auto store_x = [&](int buf) {
-    if (!stager) return;
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      *reinterpret_cast<i32x4*>(&xl[buf][(16 * e + st_tok) * kPitch + st_off]) =
-          xr[e];
-  };
-
-  // the wavefront's weight fragments of one super-chunk (its 16 rows, 256
-  // k): k-steps past I are zero
+  // ---- compute wavefronts ----
+  const int h = lane >> 5;
+  const int n = lane & 31;
+  const int64_t o0 = static_cast<int64_t>(blockIdx.x) * kRowsWG + kRowsW * wv;
+  // weight fragment of k-step j: bytes kb + 32 j + 16 h of row o0 + n
+  const uint32_t woff = static_cast<uint32_t>((o0 + n) * I) + 16u * h;
+  const uint32_t wend = static_cast<uint32_t>(O * I);
   auto load_w = [&](i32x4 (&w)[4], int64_t sc) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int64_t k = sc * kKS + 64 * j;
-      const i32x4 v = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(
-          wres, woff + static_cast<int>(k), 0, 0));
-      w[j] = k < I ? v : i32x4{0, 0, 0, 0};
+      const int64_t k = sc * kKS + 32 * j;
+      const uint32_t off = k < I ? woff + static_cast<uint32_t>(k) : wend;
+      w[j] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(
+          wres, static_cast<int>(off), 0, 0));
     }
   };
-  // one super-chunk: multiply with weights wc, load the weights of the
-  // super-chunk kWD ahead into wn (the ring slot freed by the one before),
-  // stage the next tokens' codes and load the ones after
-  auto step = [&](int64_t sc, i32x4 (&wc)[4], i32x4 (&wn)[4]) {
-    if (sc >= n_sc) return;
-    if (sc + kWD < n_sc) load_w(wn, sc + kWD);
-    const int buf = static_cast<int>(sc & 1);
+  // token fragment of tile t, k-step j: token 32 t + n, chunk 2 j + h
+  auto read_x = [&](i32x4 (&x)[4], int64_t sc, int j) {
+    const int8_t* buf = xl + static_cast<int>(sc % kNBuf) * kBufBytes;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      // the k-step's eight token fragments are read together, so their LDS
-      // latencies overlap, then multiplied
-      i32x4 xf[8];
-#pragma unroll
-      for (int t = 0; t < 8; ++t)
-        xf[t] = *reinterpret_cast<const i32x4*>(
-            &xl[buf][(16 * t + n) * kPitch + 64 * j + 16 * g]);
-#pragma unroll
-      for (int t = 0; t < 8; ++t)
-        acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wc[j], xf[t], acc[t], 0, 0, 0);
-      // keeps each accumulator in its own AGPRs (without it the compiler
-      // rotates all 32 accumulator registers every pass); one pin per
-      // k-step, since an asm statement also bounds instruction scheduling
-      asm volatile("" : "+a"(acc[0]), "+a"(acc[1]), "+a"(acc[2]), "+a"(acc[3]),
-                        "+a"(acc[4]), "+a"(acc[5]), "+a"(acc[6]), "+a"(acc[7]));
-    }
-    if (sc + 1 < n_sc) {
-      store_x(buf ^ 1);                     // buffer read two steps ago
-      if (sc + 2 < n_sc) load_x((sc + 2) * kKS);
-      lds_barrier();                        // loads stay in flight
-    }
+    for (int t = 0; t < 4; ++t)
+      x[t] = *reinterpret_cast<const i32x4*>(
+          buf + (32 * t + n) * kKS + 16 * ((2 * j + h) ^ (n & 7)));
   };
 
-  i32x4 w0[4], w1[4], w2[4], w3[4];
-  load_x(0);
+  i32x16 acc[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) acc[t] = i32x16{};
+  i32x4 xa[4], xb[4];
+  // one super-chunk: load the weights kWRing - 1 super-chunks ahead into
+  // wn (the slot freed by the super-chunk before), then four k-steps, each
+  // reading the next k-step's token fragments before its MFMAs
+  auto step = [&](int64_t sc, i32x4 (&wc)[4], i32x4 (&wn)[4]) {
+    load_w(wn, sc + kWRing - 1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      i32x4 (&cur)[4] = (j & 1) ? xb : xa;
+      i32x4 (&nxt)[4] = (j & 1) ? xa : xb;
+      if (j < 3) read_x(nxt, sc, j + 1);
+      else read_x(nxt, sc + 1, 0);        // complete since the last barrier
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        acc[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wc[j], cur[t], acc[t], 0, 0, 0);
+      // keeps each accumulator in its own AGPRs; one pin per k-step, since
+      // an asm statement also bounds instruction scheduling
+      asm volatile("" : "+a"(acc[0]), "+a"(acc[1]), "+a"(acc[2]), "+a"(acc[3]));
+    }
+    plain_barrier();
+  };
+
+  i32x4 w0[4], w1[4], w2[4], w3[4], w4[4], w5[4], w6[4], w7[4];
   load_w(w0, 0);
-  if (n_sc > 1) load_w(w1, 1);
-  if (n_sc > 2) load_w(w2, 2);
-  store_x(0);
-  if (n_sc > 1) load_x(kKS);
-  lds_barrier();                            // super-chunk 0 staged
-  for (int64_t sc = 0; sc < n_sc; sc += kWD + 1) {
-    step(sc, w0, w3);
+  load_w(w1, 1);
+  load_w(w2, 2);
+  load_w(w3, 3);
+  load_w(w4, 4);
+  load_w(w5, 5);
+  load_w(w6, 6);
+  plain_barrier();                          // super-chunks 0 and 1 staged
+  read_x(xa, 0, 0);
+  int64_t sc = 0;
+  for (; sc + kWRing <= n_sc; sc += kWRing) {
+    step(sc, w0, w7);
     step(sc + 1, w1, w0);
     step(sc + 2, w2, w1);
     step(sc + 3, w3, w2);
+    step(sc + 4, w4, w3);
+    step(sc + 5, w5, w4);
+    step(sc + 6, w6, w5);
+    step(sc + 7, w7, w6);
   }
-  if (!rows_ok) return;
-  // lane (g, n) of tile t: rows o0 + 4 g + r, token b0 + 16 t + n
-  const float4 wsc = *reinterpret_cast<const float4*>(ws + o0 + 4 * g);
+  if (sc < n_sc) step(sc, w0, w7);
+  if (sc + 1 < n_sc) step(sc + 1, w1, w0);
+  if (sc + 2 < n_sc) step(sc + 2, w2, w1);
+  if (sc + 3 < n_sc) step(sc + 3, w3, w2);
+  if (sc + 4 < n_sc) step(sc + 4, w4, w3);
+  if (sc + 5 < n_sc) step(sc + 5, w5, w4);
+  if (sc + 6 < n_sc) step(sc + 6, w6, w5);
+
+  plain_barrier();                          // staging loads all landed
+
+  // Outputs, one 32 x 32 tile at a time through this wavefront's own LDS
+  // region (rows of 36 floats, so the quarter-wavefront writes hit eight
+  // bank groups): lane (h, n), register 4 q + r of tile t holds row
+  // o0 + 8 q + 4 h + r, token b0 + 32 t + n. Written to LDS as [token][row],
+  // read back as 16-byte row chunks, so that each store instruction writes
+  // eight whole 128-byte output rows. Rescaled on the way in, with the same
+  // expression as the matrix-vector kernel (equal bits).
+  constexpr int kTP = 36;
+  float* tl = reinterpret_cast<float*>(xl) + wv * (32 * kTP);
+  float4 wsc[4];
 #pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const int64_t b = b0 + 16 * t + n;
-    if (b >= B) continue;
-    const float sx = xs[b];
-    float4 out;
-    out.x = static_cast<float>(acc[t][0]) * (wsc.x * sx);
-    out.y = static_cast<float>(acc[t][1]) * (wsc.y * sx);
-    out.z = static_cast<float>(acc[t][2]) * (wsc.z * sx);
-    out.w = static_cast<float>(acc[t][3]) * (wsc.w * sx);
-    *reinterpret_cast<float4*>(y + b * O + o0 + 4 * g) = out;
+  for (int q = 0; q < 4; ++q) {
+    const int64_t o = o0 + 8 * q + 4 * h;    // rows in fours, all below O or none
+    wsc[q] = o < O ? *reinterpret_cast<const float4*>(ws + o)
+                   : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  const int rn = lane >> 3;                  // read-back: token rn + 8 e
+  const int rc = lane & 7;                   // 16-byte chunk: rows 4 rc .. + 3
+  const bool row_ok = o0 + 4 * rc < O;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int64_t bw = b0 + 32 * t + n;
+    const float sx = bw < B ? xs[bw] : 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float4 v;
+      v.x = static_cast<float>(acc[t][4 * q + 0]) * (wsc[q].x * sx);
+      v.y = static_cast<float>(acc[t][4 * q + 1]) * (wsc[q].y * sx);
+      v.z = static_cast<float>(acc[t][4 * q + 2]) * (wsc[q].z * sx);
+      v.w = static_cast<float>(acc[t][4 * q + 3]) * (wsc[q].w * sx);
+      *reinterpret_cast<float4*>(tl + n * kTP + 8 * q + 4 * h) = v;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float4 v = *reinterpret_cast<const float4*>(tl + (rn + 8 * e) * kTP + 4 * rc);
+      const int64_t b = b0 + 32 * t + rn + 8 * e;
+      if (row_ok && b < B)
+        *reinterpret_cast<float4*>(y + b * O + o0 + 4 * rc) = v;
+    }
   }
 }
 
@@ -466,6 +613,16 @@ hipError_t launch_q8_quantize(const void* x, int dtype, int64_t rows,
                    reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
                    reinterpret_cast<uintptr_t>(q) % 8 == 0 &&
                    (cols * esz) % 16 == 0;
+  if (vec && rows < kSplitMaxRows) {
+    const dim3 g1(static_cast<unsigned>(rows));
+    if (dtype == WKV7_BF16)
+      hipLaunchKernelGGL((quantize_split_kernel<WKV7_BF16>), g1, block, 0, stream,
+                         static_cast<const uint16_t*>(x), rows, cols, q, scale);
+    else
+      hipLaunchKernelGGL((quantize_split_kernel<WKV7_F32>), g1, block, 0, stream,
+                         static_cast<const float*>(x), rows, cols, q, scale);
+    return hipGetLastError();
+  }
   if (dtype == WKV7_BF16) {
     const uint16_t* xb = static_cast<const uint16_t*>(x);
     if (vec) hipLaunchKernelGGL((quantize_rows_kernel<WKV7_BF16, true>), grid, block, 0, stream, xb, rows, cols, q, scale);
@@ -494,20 +651,12 @@ hipError_t launch_q8_matmul(const int8_t* wq, const float* ws, int64_t O,
     }
     return hipGetLastError();
   }
-  // Wavefronts per workgroup: the fewest (4..8) that put the grid on the
-  // 256 CUs in one round, one workgroup per CU; else 4 (two workgroups per
-  // CU, several rounds). With 4 and more workgroups than CUs, part of the
-  // CUs would hold two while the rest hold one and finish early.
+  const int64_t gx = (O + kRowsWG - 1) / kRowsWG;
   const int64_t gy = (B + kTokWG - 1) / kTokWG;
-  int waves = 4;
-  for (int wc = 4; wc <= 8; ++wc) {
-    if (((O + 16 * wc - 1) / (16 * wc)) * gy <= 256) { waves = wc; break; }
-  }
-  const int64_t gx = (O + 16 * waves - 1) / (16 * waves);
   if (gx > 0x7fffffff || gy > 65535) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(q8_matmul_kernel,
                      dim3(static_cast<unsigned>(gx), static_cast<unsigned>(gy)),
-                     dim3(64 * waves), 0, stream, wq, ws, O, I, xq, xs, B, y);
+                     dim3(64 * (kCompW + 1)), 0, stream, wq, ws, O, I, xq, xs, B, y);
   return hipGetLastError();
 }
 

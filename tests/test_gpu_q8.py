@@ -45,13 +45,38 @@ def test_quantize_bitexact(dtype):
     assert list(q_ref[6, :5]) == [127, 3, -3, 1, -1]
 
 
+# Rows of whole 16-byte groups: up to 1023 rows take the row-split kernel
+# (four wavefronts per row), more rows the one-wavefront kernel; rows longer
+# than 4096 values the two-pass form.
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("rows,cols", [(37, 2048), (300, 1088), (5, 4096),
+                                       (2, 8), (1100, 512), (3, 4104)])
+def test_quantize_bitexact_vector_rows(dtype, rows, cols):
+    rng = np.random.default_rng(rows * 7 + cols)
+    x = (rng.standard_normal((rows, cols)) *
+         10.0 ** rng.integers(-4, 4, (rows, 1))).astype(np.float32)
+    x[1] = 0.0                                   # zero row
+    x[0, :5] = [127.0, 2.5, -2.5, 0.5, -0.5]     # exact halves at scale 1
+    x[0, 5:] = 0.0
+    x[0, cols - 1] = -127.0                      # the maximum in the last chunk
+    xt = torch.from_numpy(x).to(dtype)
+    x_in = xt.float().numpy()
+    q, s = _quantize_dev(xt.to(DEV))
+    q_ref, s_ref = quantize_rows(x_in)
+    say(f"quantize rows={rows} cols={cols} {dtype}")
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+    assert list(q_ref[0, :5]) == [127, 3, -3, 1, -1]
+
+
 @pytest.mark.parametrize("O,I,B", [(48, 128, 1), (64, 256, 17), (208, 640, 130),
                                    (16, 64, 300), (64, 1088, 2), (32, 2112, 3),
                                    (16, 64, 4), (1040, 2048, 1),
-                                   # workgroups of 5, 7 and 8 wavefronts (the
-                                   # launch fits the grid on the CUs in one round)
-                                   (9600, 128, 200), (13440, 128, 200),
-                                   (16000, 128, 200)])
+                                   # rows a multiple of the workgroup's 96 or
+                                   # not, I a multiple of the 128-wide k step
+                                   # or not, partial token blocks
+                                   (9600, 128, 200), (13440, 192, 200),
+                                   (16000, 128, 200), (112, 4160, 129)])
 def test_matmul_matches_oracle(O, I, B):
     rng = np.random.default_rng(O + I + B)
     w = rng.standard_normal((O, I)).astype(np.float32)
