@@ -837,7 +837,8 @@ def run_ceilings(reps: int = 10):
     res = torch.empty(blocks * P.WAVES_PER_BLOCK, dtype=torch.float32,
                       device=dev)
     for kind, key, iters in ((P.MFMA_BF16, "mfma_bf16_16x16x32", 20000),
-                             (P.MFMA_I8, "mfma_i8_16x16x64", 20000)):
+                             (P.MFMA_I8, "mfma_i8_16x16x64", 20000),
+                             (P.MFMA_I8_32, "mfma_i8_32x32x32", 10000)):
         ops = {}
 
         def run():
@@ -1074,10 +1075,11 @@ def main(argv=None) -> int:
             _with_ceiling(h, h["achieved"], c["hbm_ceiling_decode_large"])
         if "q8_proj" in line:
             q = line["q8_proj"]
-            q["measured_int8_tops"] = c["mfma_i8_16x16x64"]
+            # the tiled product runs on v_mfma_i32_32x32x32_i8
+            q["measured_int8_tops"] = c["mfma_i8_32x32x32"]
             for k, v in q.items():
                 if isinstance(v, dict) and "tops" in v:
-                    v["mfma_frac_of_measured"] = v["tops"] / c["mfma_i8_16x16x64"]
+                    v["mfma_frac_of_measured"] = v["tops"] / c["mfma_i8_32x32x32"]
         if "decode_large" in line:
             hr = line["decode_large"]["hibernate_resume"]
             hr["pcie_d2h_contiguous_GBps"] = c["pcie_d2h_256MiB"]

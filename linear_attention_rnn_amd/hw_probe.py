@@ -14,7 +14,9 @@ EXPORTS = ("hwprobe_copy", "hwprobe_mfma", "hwprobe_mfma_per_iter")
 
 MFMA_BF16 = 0      # v_mfma_f32_16x16x32_bf16: 16,384 flops per instruction
 MFMA_I8 = 1        # v_mfma_i32_16x16x64_i8: 32,768 ops per instruction
-OPS_PER_MFMA = {MFMA_BF16: 2 * 16 * 16 * 32, MFMA_I8: 2 * 16 * 16 * 64}
+MFMA_I8_32 = 2     # v_mfma_i32_32x32x32_i8: 65,536 ops per instruction
+OPS_PER_MFMA = {MFMA_BF16: 2 * 16 * 16 * 32, MFMA_I8: 2 * 16 * 16 * 64,
+                MFMA_I8_32: 2 * 32 * 32 * 32}
 WAVES_PER_BLOCK = 4
 
 

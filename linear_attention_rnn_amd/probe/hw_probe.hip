@@ -14,6 +14,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kCopyThreads = 256;
 constexpr int kCopyUnroll = 4;
@@ -111,6 +112,34 @@ void probe_mfma_i8_kernel(float* out, int iters, float seed) {
     out[blockIdx.x * (kMfmaThreads / 64) + (threadIdx.x >> 6)] = static_cast<float>(s);
 }
 
+// The same with v_mfma_i32_32x32x32_i8 (int8 operands, 32 x 32 tile of
+// int32 accumulators, 16 registers per lane).
+__global__ __launch_bounds__(kMfmaThreads)
+void probe_mfma_i8_32_kernel(float* out, int iters, float seed) {
+  const int lane = threadIdx.x & 63;
+  const int sv = static_cast<int>(seed);
+  i32x4 av, bv;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    av[e] = (lane + e + sv) & 0x03030303;
+    bv[e] = (lane * 3 + e + sv) & 0x03030303;
+  }
+  i32x16 c0 = {}, c1 = c0, c2 = c0, c3 = c0, c4 = c0, c5 = c0, c6 = c0, c7 = c0;
+#define PROBE_MFMA_I8_32(c) \
+  asm volatile("v_mfma_i32_32x32x32_i8 %0, %1, %2, %0" : "+a"(c) : "v"(av), "v"(bv))
+  for (int it = 0; it < iters; ++it) {
+    PROBE_MFMA_I8_32(c0); PROBE_MFMA_I8_32(c1); PROBE_MFMA_I8_32(c2); PROBE_MFMA_I8_32(c3);
+    PROBE_MFMA_I8_32(c4); PROBE_MFMA_I8_32(c5); PROBE_MFMA_I8_32(c6); PROBE_MFMA_I8_32(c7);
+  }
+#undef PROBE_MFMA_I8_32
+  const i32x16 t = c0 + c1 + c2 + c3 + c4 + c5 + c6 + c7;
+  int s = 0;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s += t[r];
+  if (lane == 0)
+    out[blockIdx.x * (kMfmaThreads / 64) + (threadIdx.x >> 6)] = static_cast<float>(s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -144,19 +173,23 @@ int hwprobe_copy(const void* src, void* dst, size_t bytes, int nontemporal,
 
 // Runs `blocks` workgroups of four wavefronts, each wavefront issuing
 // iters x 8 matrix instructions (kind 0: v_mfma_f32_16x16x32_bf16, 16,384
-// flops each; kind 1: v_mfma_i32_16x16x64_i8, 32,768 ops each). `out` must
-// hold blocks x 4 floats. Returns a hipError_t value.
+// flops each; kind 1: v_mfma_i32_16x16x64_i8, 32,768 ops each; kind 2:
+// v_mfma_i32_32x32x32_i8, 65,536 ops each). `out` must hold blocks x 4
+// floats. Returns a hipError_t value.
 int hwprobe_mfma(int kind, int blocks, int iters, float* out, size_t out_floats,
                  void* stream) {
-  if (!out || blocks <= 0 || blocks > 65536 || iters < 0 || (kind != 0 && kind != 1) ||
+  if (!out || blocks <= 0 || blocks > 65536 || iters < 0 || (kind < 0 || kind > 2) ||
       out_floats < static_cast<size_t>(blocks) * (kMfmaThreads / 64))
     return hipErrorInvalidValue;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (kind == 0)
     hipLaunchKernelGGL(probe_mfma_bf16_kernel, dim3(blocks), dim3(kMfmaThreads), 0, s,
                        out, iters, 0.125f);
-  else
+  else if (kind == 1)
     hipLaunchKernelGGL(probe_mfma_i8_kernel, dim3(blocks), dim3(kMfmaThreads), 0, s,
+                       out, iters, 1.0f);
+  else
+    hipLaunchKernelGGL(probe_mfma_i8_32_kernel, dim3(blocks), dim3(kMfmaThreads), 0, s,
                        out, iters, 1.0f);
   return hipGetLastError();
 }

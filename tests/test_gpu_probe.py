@@ -29,7 +29,7 @@ def test_copy_is_exact(nbytes, nt, blocks):
     assert int(dst[n:].abs().sum()) == 0                # nothing past the end
 
 
-@pytest.mark.parametrize("kind", [P.MFMA_BF16, P.MFMA_I8])
+@pytest.mark.parametrize("kind", [P.MFMA_BF16, P.MFMA_I8, P.MFMA_I8_32])
 def test_mfma_loop_runs(kind):
     say(f"probe mfma kind {kind}")
     blocks = 8

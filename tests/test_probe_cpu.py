@@ -26,6 +26,7 @@ def test_probe_rejects_before_device():
     assert P.lib.hwprobe_copy(addr16, addr16, 16, 0, -1, None) == inval
     assert P.lib.hwprobe_copy(addr16, addr16, 0, 0, 0, None) == 0
     assert P.lib.hwprobe_mfma(0, 4, 1, addr16, 15, None) == inval   # < 4 x 4
-    assert P.lib.hwprobe_mfma(2, 1, 1, addr16, 16, None) == inval
+    assert P.lib.hwprobe_mfma(3, 1, 1, addr16, 16, None) == inval
+    assert P.lib.hwprobe_mfma(-1, 1, 1, addr16, 16, None) == inval
     assert P.lib.hwprobe_mfma(0, 0, 1, addr16, 16, None) == inval
     assert P.lib.hwprobe_mfma(0, 1, -1, addr16, 16, None) == inval
