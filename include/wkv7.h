@@ -73,11 +73,12 @@ enum { WKV7_F32 = 0, WKV7_BF16 = 1 };
 enum {
   /* Sequences with at least this many tokens take the chunked-prefill
    * kernel; shorter ones (including every decode token) take the
-   * sequential kernel. Default 64; must be >= 1. The choice depends on the
+   * sequential kernel. Default 32; must be >= 1. The choice depends on the
    * sequence length only, so a slot's result never depends on the rest of
-   * the batch. The chunked kernel runs a chunk token by token when its
-   * decay exceeds the range of its scaled operands, so both paths accept
-   * any w in (0, 1]. */
+   * the batch (the sequential kernel's variants for few and for many
+   * sequences compute the same bits). The chunked kernel runs a chunk token
+   * by token when its decay exceeds the range of its scaled operands, so
+   * both paths accept any w in (0, 1]. */
   WKV7_OPT_PREFILL_MIN_LEN = 1,
   /* Operand precision of the chunked kernel for bf16 inputs. 0 (default):
    * the key-side Gram products use split bf16 (hi + lo) operands and the

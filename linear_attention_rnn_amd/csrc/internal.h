@@ -47,7 +47,9 @@ struct ScanItem {
 // items of its two kernel phases (the first also runs the chunked sequences
 // that are not split) and the scan items.
 struct Launch {
+  // sequential items: the single-token ones first (n_seq_single of them)
   const WorkItem* seq = nullptr;           int32_t n_seq = 0;
+  int32_t n_seq_single = 0;
   const WorkItem* chunk_all = nullptr;     int32_t n_chunk_all = 0;
   const SegItem* phase1 = nullptr;         int32_t n_phase1 = 0;
   const SegItem* phase3 = nullptr;         int32_t n_phase3 = 0;
@@ -81,6 +83,9 @@ __device__ __forceinline__ void lds_barrier() {
 
 // Sequential kernel: one wavefront per (sequence, head), state in registers.
 hipError_t launch_seq(const SeqArgs& args, hipStream_t stream);
+// The same recurrence with four wavefronts per (sequence, head) (the same
+// bits), for items of more than one token.
+hipError_t launch_seq4(const SeqArgs& args, hipStream_t stream);
 
 // Chunked-prefill kernel for sequences of at least one chunk. bf16 inputs
 // take the fp16-value-side kernel unless `precise`; fp32 inputs always take

@@ -77,7 +77,7 @@ struct wkv7_pool {
   int32_t n_slots = 0, H = 0, N = 0;
   float* state = nullptr;
   size_t slot_floats = 0;
-  int64_t prefill_min_len = 64;
+  int64_t prefill_min_len = 32;
   bool chunk_precise = false;
   int64_t segment_len = 0;           // 0: segment-parallel prefill off
   float* seg_scratch = nullptr;      // wkv7_forward's segment buffers
@@ -205,11 +205,13 @@ bool aligned16(const void* q) {
   return (reinterpret_cast<uintptr_t>(q) & 15u) == 0;
 }
 
-// A validated batch: work items with the sequential-kernel items first,
-// then the chunked ones, longest first.
+// A validated batch: work items with the sequential-kernel items first
+// (single-token ones, then longer ones), then the chunked ones, longest
+// first.
 struct Batch {
   std::vector<WorkItem> items;       // sequential items, then all chunked
   int32_t n_seq_items = 0;
+  int32_t n_seq_single = 0;          // leading single-token items
   int64_t T_tot = 0;
   // with segment-parallel prefill on: chunked items run whole (unsplit) and
   // those split into segments of `seg_len` tokens
@@ -238,15 +240,18 @@ wkv7_status build_batch(const wkv7_pool* p, const int32_t* slot_ids,
                   cu_seqlens[s + 1]);
   if (wkv7_status st = check_ids(p, slot_ids, n_seqs, true, what)) return st;
   out->T_tot = cu_seqlens[n_seqs];
-  std::vector<WorkItem> chunk_items;
+  std::vector<WorkItem> chunk_items, multi_items;
   out->items.reserve(static_cast<size_t>(n_seqs));
   for (int32_t s = 0; s < n_seqs; ++s) {
     const int32_t len = cu_seqlens[s + 1] - cu_seqlens[s];
     if (len == 0) continue;
     WorkItem it{slot_ids[s], cu_seqlens[s], len, 0};
     if (len >= p->prefill_min_len) chunk_items.push_back(it);
+    else if (len > 1) multi_items.push_back(it);
     else out->items.push_back(it);
   }
+  out->n_seq_single = static_cast<int32_t>(out->items.size());
+  out->items.insert(out->items.end(), multi_items.begin(), multi_items.end());
   std::stable_sort(chunk_items.begin(), chunk_items.end(),
                    [](const WorkItem& x, const WorkItem& y) {
                      return x.len > y.len;
@@ -294,6 +299,7 @@ std::vector<int32_t> serialize(const wkv7_pool* p, const Batch& bt,
   auto at = [](size_t off) { return reinterpret_cast<const void*>(off); };
   *lay = wkv7::Launch{};
   lay->n_seq = bt.n_seq_items;
+  lay->n_seq_single = bt.n_seq_single;
   lay->n_chunk_all = bt.n_chunk_items();
   lay->seq = static_cast<const WorkItem*>(at(put(bt.items.data(),
                                                  bt.items.size() * sizeof(WorkItem))));
@@ -378,14 +384,15 @@ wkv7_status check_forward_args(int32_t dtype, int64_t T_tot, const void* r,
 // launches: segment transitions and zero-start states together with the
 // unsplit chunked sequences, the carry scan, the segments' outputs); on the
 // other chunked paths every chunked sequence runs whole.
-// Decode items (the sequential kernel's work) ride in trailing workgroups of
-// the batch's chunked launch when the two together fit the CUs in one round
+// Decode items (single-token sequences) ride in trailing workgroups of the
+// batch's chunked launch when the two together fit the CUs in one round
 // (the chunked kernel holds one workgroup per CU); with segment-parallel
 // prefill that is the output launch (phase 3: one item per segment, never
 // more than the transition launch, which has two per non-last segment plus
 // the unsplit sequences). Otherwise, or when the chunked work takes another
-// kernel, they get a launch of their own. Either way the decode items
-// compute the same bits.
+// kernel, they get a launch of their own. Short multi-token sequences take
+// the four-wavefront sequential kernel while the batch has few of them.
+// Every route computes the same bits for a sequential item.
 wkv7_status launch_batch(const wkv7_pool* p, const wkv7::Launch& L,
                          int32_t dtype, const void* r, const void* w,
                          const void* k, const void* v, const void* a,
@@ -393,23 +400,38 @@ wkv7_status launch_batch(const wkv7_pool* p, const wkv7::Launch& L,
   wkv7::SeqArgs args{p->state, nullptr, 0, p->H, dtype, r, w, k, v, a, b, o};
   const bool fast = dtype == WKV7_BF16 && !p->chunk_precise;
   const bool segmented = L.n_phase3 > 0 && fast;
+  const int32_t n_single = L.n_seq_single;
+  const int32_t n_multi = L.n_seq - L.n_seq_single;
   bool fuse = false;
-  if (L.n_seq > 0 && fast) {
+  if (n_single > 0 && fast) {
     const int64_t chunk_items = segmented ? L.n_phase3 : L.n_chunk_all;
     fuse = chunk_items > 0 &&
-           chunk_items * p->H + wkv7::chunk_decode_blocks(L.n_seq, p->H) <= p->n_cus;
+           chunk_items * p->H + wkv7::chunk_decode_blocks(n_single, p->H) <= p->n_cus;
   }
-  if (L.n_seq > 0 && !fuse) {
+  if (n_single > 0 && !fuse) {
     args.items = L.seq;
-    args.n_items = L.n_seq;
+    args.n_items = n_single;
     hipError_t e = wkv7::launch_seq(args, hs);
+    if (e != hipSuccess) return fail_hip(e, "sequential kernel launch");
+  }
+  if (n_multi > 0) {
+    // Four wavefronts per (sequence, head) cut a short sequence's latency
+    // about fourfold while the batch leaves the GPU room (up to 8 chains per
+    // CU, four wavefronts each); beyond that the one-wavefront kernel's
+    // throughput is better (it reads each token's inputs once, not four
+    // times). Both compute the same bits, so the choice cannot change a
+    // result.
+    args.items = L.seq + n_single;
+    args.n_items = n_multi;
+    const bool wide = static_cast<int64_t>(n_multi) * p->H <= 8 * p->n_cus;
+    hipError_t e = wide ? wkv7::launch_seq4(args, hs) : wkv7::launch_seq(args, hs);
     if (e != hipSuccess) return fail_hip(e, "sequential kernel launch");
   }
   if (!segmented) {
     if (L.n_chunk_all > 0) {
       args.items = L.chunk_all;
       args.n_items = L.n_chunk_all;
-      hipError_t e = fuse ? wkv7::launch_chunked_p(args, hs, L.seq, L.n_seq)
+      hipError_t e = fuse ? wkv7::launch_chunked_p(args, hs, L.seq, n_single)
                           : wkv7::launch_chunked(args, p->chunk_precise, hs);
       if (e != hipSuccess) return fail_hip(e, "chunked kernel launch");
     }
@@ -422,7 +444,7 @@ wkv7_status launch_batch(const wkv7_pool* p, const wkv7::Launch& L,
   e = wkv7::launch_seg_scan(L.scan, L.n_scan, p->H, hs);
   if (e != hipSuccess) return fail_hip(e, "segment scan launch");
   args.n_items = L.n_phase3;
-  e = fuse ? wkv7::launch_chunked_p_seg(args, L.phase3, hs, L.seq, L.n_seq)
+  e = fuse ? wkv7::launch_chunked_p_seg(args, L.phase3, hs, L.seq, n_single)
            : wkv7::launch_chunked_p_seg(args, L.phase3, hs);
   if (e != hipSuccess) return fail_hip(e, "segment prefill launch");
   return WKV7_OK;

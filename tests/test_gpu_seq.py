@@ -142,6 +142,99 @@ def test_same_call_twice_and_permuted_order_bitwise():
         assert torch.equal(S.view(torch.int32), outs[0][1].view(torch.int32))
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_multi_token_sequential_equals_token_steps_bitwise(dtype):
+    """Short multi-token sequences (four wavefronts per (sequence, head),
+    inputs through a ring loaded ahead, the ring's tail run as no-ops) give
+    the same bits as feeding the same tokens one call at a time (single-
+    token calls run the one-wavefront decode kernel): lengths around the
+    ring depths (8 tokens for bf16 inputs, 4 for fp32)."""
+    H = 3
+    lens = [2, 3, 4, 5, 7, 8, 9, 16, 17, 63]
+    rng = np.random.default_rng(31)
+    n = len(lens)
+    ids = rng.permutation(24)[:n].astype(np.int32)
+    say(f"multi-token sequential vs token steps dtype={dtype} lens={lens}")
+    b = G.make_batch(rng, ids, lens, H, 64, dtype)
+    init = G.draw_states(rng, n, H, 64)
+    init[0, 0, 0, :4] = torch.tensor([-0.0, 0.0, -0.0, 1e-40])  # signed zeros, a denormal
+    x = {k: b.inputs[k].to(DEV).contiguous() for k in G.NAMES}
+    pool = _pool(24, H, seq_only=True)
+    try:
+        set_states(pool, ids, init)
+        o_all = torch.full((b.T_tot, H, 64), float("nan"), device=DEV)
+        W.wkv7_forward(pool, ids, b.cu_seqlens, x["r"], x["w"], x["k"],
+                       x["v"], x["a"], x["b"], o_all)
+        torch.cuda.synchronize()
+        S_all = get_states(pool, ids)
+        set_states(pool, ids, init)
+        o_step = torch.full_like(o_all, float("nan"))
+        for t in range(max(lens)):
+            live = [s for s in range(n) if lens[s] > t]
+            rows = torch.tensor([int(b.cu_seqlens[s]) + t for s in live],
+                                device=DEV)
+            cu = np.arange(len(live) + 1, dtype=np.int32)
+            xt = {k: x[k][rows].contiguous() for k in G.NAMES}
+            ot = torch.empty((len(live), H, 64), device=DEV)
+            W.wkv7_forward(pool, ids[live], cu, xt["r"], xt["w"], xt["k"],
+                           xt["v"], xt["a"], xt["b"], ot)
+            o_step[rows] = ot
+        torch.cuda.synchronize()
+        S_step = get_states(pool, ids)
+    finally:
+        W.wkv7_pool_destroy(pool)
+    assert torch.equal(o_all.cpu().view(torch.int32), o_step.cpu().view(torch.int32))
+    assert torch.equal(S_all.view(torch.int32), S_step.view(torch.int32))
+
+
+def test_many_short_sequences_same_bits_either_kernel():
+    """Short multi-token sequences take the four-wavefront kernel while a
+    call has at most 8 (sequence, head) chains per CU and the one-wavefront
+    kernel beyond that: 36 sequences x H=64 (2304 chains, more than the 2048
+    of a 256-CU part) in one call, then the same sequences four at a time.
+    Same bits both ways, and both against the oracle."""
+    H = 64
+    rng = np.random.default_rng(41)
+    n = 36
+    lens = rng.integers(2, 21, n).tolist()
+    ids = np.arange(n, dtype=np.int32)
+    say(f"many short sequences H={H} n={n} lens={lens}")
+    b = G.make_batch(rng, ids, lens, H, 64, "bf16")
+    init = G.draw_states(rng, n, H, 64)
+    x = {k: b.inputs[k].to(DEV).contiguous() for k in G.NAMES}
+    pool = _pool(n, H)
+    try:
+        set_states(pool, ids, init)
+        o_big = torch.full((b.T_tot, H, 64), float("nan"), device=DEV)
+        W.wkv7_forward(pool, ids, b.cu_seqlens, x["r"], x["w"], x["k"],
+                       x["v"], x["a"], x["b"], o_big)
+        torch.cuda.synchronize()
+        S_big = get_states(pool, ids)
+        set_states(pool, ids, init)
+        o_small = torch.full_like(o_big, float("nan"))
+        for g0 in range(0, n, 4):
+            grp = list(range(g0, min(n, g0 + 4)))
+            lo, hi = int(b.cu_seqlens[grp[0]]), int(b.cu_seqlens[grp[-1] + 1])
+            cu = (b.cu_seqlens[grp[0]:grp[-1] + 2] - lo).astype(np.int32)
+            xg = {k: x[k][lo:hi].contiguous() for k in G.NAMES}
+            og = torch.empty((hi - lo, H, 64), device=DEV)
+            W.wkv7_forward(pool, ids[grp], cu, xg["r"], xg["w"], xg["k"],
+                           xg["v"], xg["a"], xg["b"], og)
+            o_small[lo:hi] = og
+        torch.cuda.synchronize()
+        S_small = get_states(pool, ids)
+    finally:
+        W.wkv7_pool_destroy(pool)
+    assert torch.equal(o_big.cpu().view(torch.int32), o_small.cpu().view(torch.int32))
+    assert torch.equal(S_big.view(torch.int32), S_small.view(torch.int32))
+    states = {int(i): G.as_f64(init[m]) for m, i in enumerate(ids)}
+    o_ref, S_ref = _oracle(b, states)
+    e_o = rel_err(o_big.cpu(), o_ref)
+    e_s = max(rel_err(S_big[m], S_ref[int(i)]) for m, i in enumerate(ids))
+    say(f"  o err {e_o:.3e}  S err {e_s:.3e}")
+    assert e_o < 1e-5 and e_s < 1e-5
+
+
 def test_forward_errors_leave_pool_untouched():
     H = 2
     rng = np.random.default_rng(9)
