@@ -353,6 +353,63 @@ def run_small(calls: int = 200, warmup: int = 20, seed: int = 0):
     return out
 
 
+def run_short(reps: int = 50, warmup: int = 5, seed: int = 6):
+    """Short multi-token sequences: GPU microseconds per plan call on the
+    default split (sequential below PREFILL_MIN_LEN tokens) and with every
+    sequence forced onto each kernel, for a few (sequence, head) chains
+    (8 sequences x H=32, latency-bound) and for many (256 x H=32,
+    throughput-bound). bf16 and fp32 inputs, zeroed slots, fresh-drawn
+    synthetic tokens."""
+    import torch
+    import wkv7_inputs as G
+    from linear_attention_rnn_amd import wkv7 as W
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    H = 32
+    big = 1 << 30
+    out = {"workload": "short_sequences_h32", "unit": "us per call (GPU)",
+           "cases": []}
+    for dtype in ("bf16", "f32"):
+        for nseq, T in ((8, 8), (8, 24), (8, 48), (256, 8), (256, 24)):
+            g = torch.Generator(device=dev)
+            g.manual_seed(seed)
+            x = G.draw_tokens_device(g, nseq * T, H, N, dtype, dev)
+            o = torch.empty((nseq * T, H, N), dtype=torch.float32, device=dev)
+            ids = np.arange(nseq, dtype=np.int32)
+            cu = (np.arange(nseq + 1) * T).astype(np.int32)
+            case = {"dtype": dtype, "n_seq": nseq, "T": T}
+            for name, min_len in (("default", None), ("sequential", big),
+                                  ("chunked", 1)):
+                pool = W.wkv7_pool_create(nseq, H, N)
+                try:
+                    if min_len is not None:
+                        W.wkv7_pool_set_option(
+                            pool, W.WKV7_OPT_PREFILL_MIN_LEN, min_len)
+                    plan = W.wkv7_plan_create(pool, ids, cu)
+
+                    def call():
+                        W.wkv7_forward_plan(pool, plan, x["r"], x["w"],
+                                            x["k"], x["v"], x["a"], x["b"],
+                                            o, stream=stream)
+                    for _ in range(warmup):
+                        call()
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    torch.cuda.synchronize()
+                    e0.record(stream)
+                    for _ in range(reps):
+                        call()
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    case[name] = e0.elapsed_time(e1) / reps * 1e3
+                    W.wkv7_plan_destroy(plan)
+                finally:
+                    W.wkv7_pool_destroy(pool)
+            out["cases"].append(case)
+    return out
+
+
 def run_decode_cold(steps: int = 20, warmup: int = 3, seed: int = 1):
     """The headline decode batch shape with a new random 256-slot subset of
     the 1024-slot pool every step (the pool's 512 MiB is twice the MALL, so
@@ -960,7 +1017,7 @@ def main(argv=None) -> int:
     ap.add_argument("--legs",
                     default="decode,prefill,decode_cold,decode_large,"
                             "prefill_f32,prefill_ragged,mixed,prefill_long,"
-                            "q8_proj,small,ceilings",
+                            "q8_proj,small,short,ceilings",
                     help="comma list of legs to run (profiling one kernel)")
     ap.add_argument("--prefill-steps", type=int, default=10)
     args = ap.parse_args(argv)
@@ -988,6 +1045,9 @@ def main(argv=None) -> int:
         return 0
     if legs == {"q8_proj"}:
         print(json.dumps({"q8_proj": run_q8_proj()}), flush=True)
+        return 0
+    if legs == {"short"}:
+        print(json.dumps({"short": run_short()}), flush=True)
         return 0
     if legs <= {"mixed", "prefill_long"}:
         out = {}
@@ -1046,6 +1106,9 @@ def main(argv=None) -> int:
     if "small" in legs:
         line["small"] = run_small()
         _progress("small done")
+    if "short" in legs:
+        line["short"] = run_short()
+        _progress("short done")
     if not args.no_prefill and "prefill_f32" in legs:
         line["prefill_f32"] = run_prefill_f32()
         _progress("prefill_f32 done")
