@@ -524,8 +524,15 @@ wkv7_status wkv7_pool_create(int32_t n_slots, int32_t H, int32_t N,
   }
   e = hipMemset(p->state, 0, bytes);
   if (e == hipSuccess) e = hipDeviceSynchronize();
+  // The staging events order work only: a copy has finished reading its
+  // pinned host buffer, the kernels reading a device copy have finished
+  // before the next copy overwrites it. Nothing the device writes is read by
+  // the host through them, so they skip the system-scope cache writeback and
+  // invalidation of a default event (measured: ~1 us of GPU time per call
+  // instead of ~3).
   for (int i = 0; e == hipSuccess && i < kRing; ++i)
-    e = hipEventCreateWithFlags(&p->ring[i].ev, hipEventDisableTiming);
+    e = hipEventCreateWithFlags(&p->ring[i].ev,
+                                hipEventDisableTiming | hipEventDisableSystemFence);
   if (e != hipSuccess) {
     std::string msg = std::string("pool initialisation: ") + hipGetErrorString(e);
     wkv7_pool_destroy(p);
