@@ -463,6 +463,11 @@ void q8_gemv_kernel(const int8_t* __restrict__ wq,
   const int64_t wave = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   const int64_t o0 = wave * kGemvRows;
   if (o0 >= O) return;                     // O % 16 == 0: all rows or none
+  // the scales go out first, so the end does not wait on a fresh load
+  const float wsl = ws[o0 + (lane & (kGemvRows - 1))];   // lane r: row r's scale
+  float sxb[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) sxb[b] = xs[b];
   int acc[NB][kGemvRows];
 #pragma unroll
   for (int b = 0; b < NB; ++b)
@@ -471,21 +476,29 @@ void q8_gemv_kernel(const int8_t* __restrict__ wq,
   // two 1024-byte chunks of every row per pass, all loads issued before the
   // first dot product (the scheduling barrier keeps them together)
   for (int64_t c0 = 0; c0 < I; c0 += 2048) {
+    // unconditional loads (a lane past the row reads from the row's start
+    // and its token codes are then zeroed): a conditional load becomes a
+    // branch, and the compiler then waits for every load in flight
     i32x4 w[2][kGemvRows], x[2][NB];
+    bool ok[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int64_t k = c0 + 1024 * h + 16 * lane;
-      const bool ok = k < I;                 // I % 64 == 0: whole 16-byte groups
+      ok[h] = k < I;                         // I % 64 == 0: whole 16-byte groups
+      const int64_t kl = ok[h] ? k : 0;
 #pragma unroll
       for (int r = 0; r < kGemvRows; ++r)
-        w[h][r] = ok ? *reinterpret_cast<const i32x4*>(wq + (o0 + r) * I + k)
-                     : i32x4{0, 0, 0, 0};
+        w[h][r] = *reinterpret_cast<const i32x4*>(wq + (o0 + r) * I + kl);
 #pragma unroll
       for (int b = 0; b < NB; ++b)
-        x[h][b] = ok ? *reinterpret_cast<const i32x4*>(xq + b * I + k)
-                     : i32x4{0, 0, 0, 0};
+        x[h][b] = *reinterpret_cast<const i32x4*>(xq + b * I + kl);
     }
     __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        if (!ok[h]) x[h][b] = i32x4{0, 0, 0, 0};
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -498,23 +511,27 @@ void q8_gemv_kernel(const int8_t* __restrict__ wq,
   }
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    const float sx = xs[b];
+    float mine = 0.f;                      // lane r: row r's sum
 #pragma unroll
     for (int r = 0; r < kGemvRows; ++r) {
-      const int sum = wave_sum_i32(acc[b][r]);
-      if (lane == r)
-        y[b * O + o0 + r] = static_cast<float>(sum) * (ws[o0 + r] * sx);
+      const float sum = static_cast<float>(wave_sum_i32(acc[b][r]));
+      mine = lane == r ? sum : mine;
     }
+    if (lane < kGemvRows) y[b * O + o0 + lane] = mine * (wsl * sxb[b]);
   }
 }
 
-// Quantize and multiply in one launch, for few tokens with in <= 2048:
-// every wavefront starts its weight loads, then quantizes the inputs'
-// values at its lanes' k positions exactly as quantize_rows_kernel does
-// (the wavefront covers the whole row, so its maximum is the row's), and
-// runs the matrix-vector product on those codes. The first wavefront also
-// stores the codes and scales. Same codes, same integer sums, same rescale:
-// the same bits as the two separate launches.
+// Quantize and multiply in one launch, for few tokens with in <= 2048.
+// A workgroup's four wavefronts (32 output rows) each load a quarter of
+// every input row (8 values per lane), then start their weight loads; the
+// wait counter drains in issue order, so waiting for the inputs leaves the
+// weight stream in flight, and the quantization runs under it. The
+// quarters' maxima meet in LDS (the maximum of a set does not depend on the
+// order: it is the row's, as in quantize_rows_kernel), each lane codes its
+// 8 values with the row's scale exactly as quantize_rows_kernel does, and
+// the codes meet in LDS for the matrix-vector product. The first workgroup
+// also stores the codes and scales. Same codes, same integer sums, same
+// rescale: the same bits as the two separate launches.
 constexpr int64_t kFusedMaxI = 2048;
 
 template <int DT, int NB>
@@ -525,58 +542,81 @@ void q8_linear_kernel(const int8_t* __restrict__ wq,
                       int8_t* __restrict__ xq, float* __restrict__ xs,
                       float* __restrict__ y) {
   using E = Elem<DT>;
+  using T = typename E::T;
+  constexpr int kLd = static_cast<int>(8 * sizeof(T) / 16);  // 16-byte loads
+  __shared__ float part[4][NB];
+  __shared__ __align__(16) uint8_t codes[NB][kFusedMaxI];
   const int lane = threadIdx.x & 63;
-  const int64_t wave = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  const int64_t o0 = wave * kGemvRows;
-  if (o0 >= O) return;                     // O % 16 == 0: all rows or none
+  const int wv = threadIdx.x >> 6;
+  const int64_t o0 = (static_cast<int64_t>(blockIdx.x) * 4 + wv) * kGemvRows;
+  // O % 16 == 0: a wavefront has all its rows or none; one with none still
+  // takes part in the quantization and reads a valid block of rows
+  const bool rows_ok = o0 < O;
+  const int64_t oc = rows_ok ? o0 : O - kGemvRows;
+  // the wavefront's quarter of each input row (I % 64 == 0: a lane's 8
+  // values lie wholly inside or wholly outside the row)
+  const int kq = 512 * wv + 8 * lane;
+  const bool in_ok = kq < I;
+  const int64_t kql = in_ok ? kq : 0;
+  i32x4 raw[NB][kLd];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int u = 0; u < kLd; ++u)
+      raw[b][u] = reinterpret_cast<const i32x4*>(x + b * I + kql)[u];
+  // weights, unconditionally (a lane past the row reads its start: its
+  // codes are zero, so those products vanish); a conditional load would
+  // become a branch, and the compiler then waits for every load
   i32x4 w[2][kGemvRows];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int64_t k = 1024 * h + 16 * lane;
-    const bool ok = k < I;                 // I % 64 == 0: whole 16-byte groups
+    const int64_t kl = k < I ? k : 0;
 #pragma unroll
     for (int r = 0; r < kGemvRows; ++r)
-      w[h][r] = ok ? *reinterpret_cast<const i32x4*>(wq + (o0 + r) * I + k)
-                   : i32x4{0, 0, 0, 0};
+      w[h][r] = *reinterpret_cast<const i32x4*>(wq + (oc + r) * I + kl);
   }
-  __builtin_amdgcn_sched_barrier(0);       // weight loads go out first
-  i32x4 xc[2][NB];
+  const float wsl = ws[oc + (lane & (kGemvRows - 1))];   // lane r: row r's scale
+  __builtin_amdgcn_sched_barrier(0);       // every load goes out first
+  float v[NB][8];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    E::get8(reinterpret_cast<const T*>(raw[b]), v[b]);
+    float m = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      v[b][e] = in_ok ? v[b][e] : 0.f;
+      m = fmaxf(m, fabsf(v[b][e]));
+    }
+    m = wave_max_abs(m);
+    if (lane == 0) part[wv][b] = m;
+  }
+  lds_barrier();
   float sx[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    float v[2][16];
-    float m = 0.f;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int64_t k = 1024 * h + 16 * lane;
-      if (k < I) {
-        E::get8(x + b * I + k, v[h]);
-        E::get8(x + b * I + k + 8, v[h] + 8);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) v[h][e] = 0.f;
-      }
-#pragma unroll
-      for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(v[h][e]));
-    }
-    m = wave_max_abs(m);
+    const float m = fmaxf(fmaxf(part[0][b], part[1][b]), fmaxf(part[2][b], part[3][b]));
     const float sc = m / 127.0f;           // IEEE float32 division
     sx[b] = sc;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        xc[h][b][q] = static_cast<int>(code(v[h][4 * q], sc) | code(v[h][4 * q + 1], sc) << 8 |
-                                       code(v[h][4 * q + 2], sc) << 16 |
-                                       code(v[h][4 * q + 3], sc) << 24);
-      const int64_t k = 1024 * h + 16 * lane;
-      if (wave == 0 && k < I) *reinterpret_cast<i32x4*>(xq + b * I + k) = xc[h][b];
+    uint2 c;
+    c.x = code(v[b][0], sc) | code(v[b][1], sc) << 8 | code(v[b][2], sc) << 16 |
+          code(v[b][3], sc) << 24;
+    c.y = code(v[b][4], sc) | code(v[b][5], sc) << 8 | code(v[b][6], sc) << 16 |
+          code(v[b][7], sc) << 24;
+    *reinterpret_cast<uint2*>(&codes[b][kq]) = c;
+    if (blockIdx.x == 0) {
+      if (in_ok) *reinterpret_cast<uint2*>(xq + b * I + kq) = c;
+      if (threadIdx.x == 0) xs[b] = sc;
     }
-    if (wave == 0 && lane == 0) xs[b] = sc;
   }
+  lds_barrier();
   int acc[NB][kGemvRows];
 #pragma unroll
-  for (int b = 0; b < NB; ++b)
+  for (int b = 0; b < NB; ++b) {
+    i32x4 xc[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      xc[h] = *reinterpret_cast<const i32x4*>(&codes[b][1024 * h + 16 * lane]);
 #pragma unroll
     for (int r = 0; r < kGemvRows; ++r) {
       int a = 0;
@@ -584,17 +624,20 @@ void q8_linear_kernel(const int8_t* __restrict__ wq,
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          a = __builtin_amdgcn_sdot4(w[h][r][q], xc[h][b][q], a, false);
+          a = __builtin_amdgcn_sdot4(w[h][r][q], xc[h][q], a, false);
       acc[b][r] = a;
     }
+  }
 #pragma unroll
-  for (int b = 0; b < NB; ++b)
+  for (int b = 0; b < NB; ++b) {
+    float mine = 0.f;                      // lane r: row r's sum
 #pragma unroll
     for (int r = 0; r < kGemvRows; ++r) {
-      const int sum = wave_sum_i32(acc[b][r]);
-      if (lane == r)
-        y[b * O + o0 + r] = static_cast<float>(sum) * (ws[o0 + r] * sx[b]);
+      const float sum = static_cast<float>(wave_sum_i32(acc[b][r]));
+      mine = lane == r ? sum : mine;
     }
+    if (rows_ok && lane < kGemvRows) y[b * O + o0 + lane] = mine * (wsl * sx[b]);
+  }
 }
 
 }  // namespace
