@@ -81,15 +81,16 @@ __device__ __forceinline__ void quantize_row_regs(
   const int nch = static_cast<int>((cols + 511) / 512);
   float v[kMaxCh][8];
   float m = 0.f;
+  // every load unconditional, from the row's start where a lane has no
+  // values (zeroed afterwards): a conditional load becomes a branch, and the
+  // compiler then waits for each load before issuing the next
 #pragma unroll
   for (int c = 0; c < kMaxCh; ++c) {
     const int64_t i = 512 * c + 8 * lane;
-    if (c < nch && i < cols) {
-      E::get8(xr + i, v[c]);
-    } else {
+    const bool ok = c < nch && i < cols;
+    E::get8(xr + (ok ? i : 0), v[c]);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[c][e] = 0.f;
-    }
+    for (int e = 0; e < 8; ++e) v[c][e] = ok ? v[c][e] : 0.f;
   }
 #pragma unroll
   for (int c = 0; c < kMaxCh; ++c)
@@ -159,16 +160,15 @@ void quantize_split_kernel(const typename Elem<DT>::T* __restrict__ x,
   const int nch = static_cast<int>((cols + 511) / 512);
   float v[2][8];
   float m = 0.f;
+  // unconditional loads (see quantize_row_regs)
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int c = wv + 4 * u;
     const int64_t i = 512 * c + 8 * lane;
-    if (c < nch && i < cols) {
-      E::get8(xr + i, v[u]);
-    } else {
+    const bool ok = c < nch && i < cols;
+    E::get8(xr + (ok ? i : 0), v[u]);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[u][e] = 0.f;
-    }
+    for (int e = 0; e < 8; ++e) v[u][e] = ok ? v[u][e] : 0.f;
   }
 #pragma unroll
   for (int u = 0; u < 2; ++u)
