@@ -26,6 +26,19 @@ constexpr int kPitch = kN + 4;   // LDS row pitch (floats, 16-byte rows)
 __device__ __forceinline__ float4 ld4(const float* p) {
   return *reinterpret_cast<const float4*>(p);
 }
+// HBM accesses through global-address-space pointers: the work item's
+// pointers come from memory, so plain accesses would compile to flat
+// instructions, which also count against the LDS wait counter, and every
+// LDS wait in the product would then wait for the prefetch as well.
+typedef float gvec4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) gvec4 gfloat4;
+__device__ __forceinline__ float4 ldg4(const float* p) {
+  const gvec4 v = *(const gfloat4*)(p);
+  return make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void stg4(float* p, float4 v) {
+  *(gfloat4*)(p) = gvec4{v.x, v.y, v.z, v.w};
+}
 
 __global__ __launch_bounds__(256)
 void seg_scan_kernel(const ScanItem* items, int32_t n_items, int32_t H) {
@@ -46,21 +59,21 @@ void seg_scan_kernel(const ScanItem* items, int32_t n_items, int32_t H) {
 
   float4 s[4];                       // S block rows r0 + i, columns c0 .. + 3
 #pragma unroll
-  for (int i = 0; i < 4; ++i) s[i] = ld4(it.s0 + hoff + (r0 + i) * kN + c0);
+  for (int i = 0; i < 4; ++i) s[i] = ldg4(it.s0 + hoff + (r0 + i) * kN + c0);
   float4 pn[4], hn[4];               // next segment's P slice and Hs block
   auto fetch = [&](int j) {
     const float* seg = it.base + static_cast<size_t>(j) * 3 * blk;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) pn[q] = ld4(seg + hoff + pr * kN + pc + 4 * q);
+    for (int q = 0; q < 4; ++q) pn[q] = ldg4(seg + hoff + pr * kN + pc + 4 * q);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) hn[i] = ld4(seg + blk + hoff + (r0 + i) * kN + c0);
+    for (int i = 0; i < 4; ++i) hn[i] = ldg4(seg + blk + hoff + (r0 + i) * kN + c0);
   };
   if (it.n_seg > 1) fetch(0);
   for (int j = 0; j < it.n_seg; ++j) {
     float* seg = it.base + static_cast<size_t>(j) * 3 * blk;
 #pragma unroll
     for (int i = 0; i < 4; ++i)          // Sin_j
-      *reinterpret_cast<float4*>(seg + 2 * blk + hoff + (r0 + i) * kN + c0) = s[i];
+      stg4(seg + 2 * blk + hoff + (r0 + i) * kN + c0, s[i]);
     if (j + 1 == it.n_seg) break;
     __syncthreads();                     // previous step's LDS reads done
 #pragma unroll
