@@ -244,22 +244,32 @@ void chunk_kernel(SeqArgs p) {
     const int n = min(kChunk, it.len - ch * kChunk);
 
     // ---- inputs of this chunk; rows past the end are w = 1, rest 0 ----
+    // Every load is issued, rows past the end re-reading the last row, and
+    // the padding is selected afterwards: a conditional load becomes a
+    // branch, and the compiler then waits for each token's loads before
+    // issuing the next token's.
     float xr[16], xw[16], xk[16], xa[16], xb[16], xv[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int t = 16 * q + e;
-      if (t < n) {
-        const size_t off = (static_cast<size_t>(t0 + t) * p.H + h) * kN + j;
-        xr[e] = ldx<DT>(p.r, off);
-        xw[e] = ldx<DT>(p.w, off);
-        xk[e] = ldx<DT>(p.k, off);
-        xa[e] = ldx<DT>(p.a, off);
-        xb[e] = ldx<DT>(p.b, off);
-        xv[e] = ldx<DT>(p.v, off);
-      } else {
-        xr[e] = 0.f; xw[e] = 1.f; xk[e] = 0.f;
-        xa[e] = 0.f; xb[e] = 0.f; xv[e] = 0.f;
-      }
+      const int tc = t < n ? t : n - 1;                 // n >= 1
+      const size_t off = (static_cast<size_t>(t0 + tc) * p.H + h) * kN + j;
+      xr[e] = ldx<DT>(p.r, off);
+      xw[e] = ldx<DT>(p.w, off);
+      xk[e] = ldx<DT>(p.k, off);
+      xa[e] = ldx<DT>(p.a, off);
+      xb[e] = ldx<DT>(p.b, off);
+      xv[e] = ldx<DT>(p.v, off);
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const bool pad = 16 * q + e >= n;
+      xr[e] = pad ? 0.f : xr[e];
+      xw[e] = pad ? 1.f : xw[e];
+      xk[e] = pad ? 0.f : xk[e];
+      xa[e] = pad ? 0.f : xa[e];
+      xb[e] = pad ? 0.f : xb[e];
+      xv[e] = pad ? 0.f : xv[e];
     }
     // V^T[i = j][s = 16 q + e]
     put16(Vt, j, 16 * q, xv);
