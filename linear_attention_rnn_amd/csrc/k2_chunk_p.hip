@@ -61,6 +61,10 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+// The state pointers of segment items come from memory; accessed as plain
+// pointers they would compile to flat instructions, which also count
+// against the LDS wait counter.
+typedef __attribute__((address_space(1))) f32x4 gf32x4;
 
 constexpr int kL = 32;                   // chunk length
 constexpr int kP64 = 68;                 // pitch of 64-wide rows (elements)
@@ -499,10 +503,8 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
           S[jt][r] = (16 * vb + n16 == 16 * jt + 4 * g + r) ? 1.f : 0.f;
     } else if (s_in) {
 #pragma unroll
-      for (int jt = 0; jt < 4; ++jt) {
-        float4 x = *reinterpret_cast<const float4*>(s_in + soff + 16 * jt);
-        S[jt] = f32x4{x.x, x.y, x.z, x.w};
-      }
+      for (int jt = 0; jt < 4; ++jt)   // global accesses (see gf32x4)
+        S[jt] = *(const gf32x4*)(s_in + soff + 16 * jt);
     }
   }
 
@@ -811,8 +813,7 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
   if (!is_key && s_out) {
 #pragma unroll
     for (int jt = 0; jt < 4; ++jt)
-      *reinterpret_cast<float4*>(s_out + soff + 16 * jt) =
-          make_float4(S[jt][0], S[jt][1], S[jt][2], S[jt][3]);
+      *(gf32x4*)(s_out + soff + 16 * jt) = S[jt];
   }
 }
 
