@@ -537,283 +537,296 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
   }
   __syncthreads();                                                // TOT of chunk 0
 
-  // fallback flags of chunk step - 1, known to every thread from the end
-  // of the step before: early (its inputs or decays out of the fast path's
-  // range) and gram (its Gram matrices out of the fp16 range)
-  bool early_prev = false, gram_prev = false;
+  // The key and value wavefronts run separate loops with the same barriers
+  // in the same order (two per step; all waves of the workgroup reach each
+  // one), so each role's registers hold only its own state.
   const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-
-  for (int step = 0; step <= nch; ++step) {
-    const int cK = step;            // chunk whose operands and Grams are built
-    const int cV = step - 1;        // chunk whose T is built and value side run
-    const bool k_on = is_key && cK < nch;
-    const bool v_on = !is_key && cV >= 0;
-    const int bK = cK & 1, bV = cV & 1;
-    _Float16* VOk = reinterpret_cast<_Float16*>(lds + kOffVO + bK * kVOBytes);
-    _Float16* LLk = reinterpret_cast<_Float16*>(lds + kOffLL + bK * kLLBytes);
-    const _Float16* VOv = reinterpret_cast<const _Float16*>(lds + kOffVO + bV * kVOBytes);
-    const _Float16* LLv = reinterpret_cast<const _Float16*>(lds + kOffLL + bV * kLLBytes);
-    const int nV = min(kL, len - cV * kL);
-    const int t0K = tok0 + cK * kL;
-    const int t0V = tok0 + cV * kL;
-
-    // ===== interval 1 =====
-    bool bad_k = false;
-    if (k_on) {
-      // key: operands of chunk cK. Decay over the row groups before the
-      // thread's group (pre), after it (suf) and over the whole chunk (lam).
-      // The wavefront's two groups are 2 (wv & 3) and the one after, so the
-      // products outside them have wavefront-uniform bounds.
-      float g0[8], g1[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) { g0[q] = TOT[q * 64 + j0]; g1[q] = TOT[q * 64 + j0 + 1]; }
-      float lo0, lo1, hi0, hi1;      // products below and above the pair
-      switch (wv & 3) {
-        case 0: outer_products<0>(g0, g1, lo0, lo1, hi0, hi1); break;
-        case 1: outer_products<1>(g0, g1, lo0, lo1, hi0, hi1); break;
-        case 2: outer_products<2>(g0, g1, lo0, lo1, hi0, hi1); break;
-        default: outer_products<3>(g0, g1, lo0, lo1, hi0, hi1); break;
+  if (is_key) {
+    for (int step = 0; step <= nch; ++step) {
+      const int cK = step;          // chunk whose operands and Grams are built
+      const bool k_on = cK < nch;
+      const int bK = cK & 1;
+      _Float16* VOk = reinterpret_cast<_Float16*>(lds + kOffVO + bK * kVOBytes);
+      _Float16* LLk = reinterpret_cast<_Float16*>(lds + kOffLL + bK * kLLBytes);
+      const int t0K = tok0 + cK * kL;
+      // ===== interval 1 =====
+      bool bad_k = false;
+      if (k_on) {
+        // key: operands of chunk cK. Decay over the row groups before the
+        // thread's group (pre), after it (suf) and over the whole chunk (lam).
+        // The wavefront's two groups are 2 (wv & 3) and the one after, so the
+        // products outside them have wavefront-uniform bounds.
+        float g0[8], g1[8];
+  #pragma unroll
+        for (int q = 0; q < 8; ++q) { g0[q] = TOT[q * 64 + j0]; g1[q] = TOT[q * 64 + j0 + 1]; }
+        float lo0, lo1, hi0, hi1;      // products below and above the pair
+        switch (wv & 3) {
+          case 0: outer_products<0>(g0, g1, lo0, lo1, hi0, hi1); break;
+          case 1: outer_products<1>(g0, g1, lo0, lo1, hi0, hi1); break;
+          case 2: outer_products<2>(g0, g1, lo0, lo1, hi0, hi1); break;
+          default: outer_products<3>(g0, g1, lo0, lo1, hi0, hi1); break;
+        }
+        const int wq = 2 * (wv & 3);
+        const bool second = (lane >> 5) != 0;   // group wq + 1
+        const float ga0 = g0[wq], ga1 = g1[wq], gb0 = g0[wq + 1], gb1 = g1[wq + 1];
+        const float pre0 = second ? lo0 * ga0 : lo0, pre1 = second ? lo1 * ga1 : lo1;
+        const float suf0 = second ? hi0 : gb0 * hi0, suf1 = second ? hi1 : gb1 * hi1;
+        const float lam0 = (lo0 * ga0) * (gb0 * hi0), lam1 = (lo1 * ga1) * (gb1 * hi1);
+        if (rg == 0) { LAMb[bK * 64 + j0] = lam0; LAMb[bK * 64 + j0 + 1] = lam1; }
+        // hardware reciprocal (1 ulp): the scaled Gram operands are split into
+        // bf16 pairs, far coarser; a lam below the fast path's range takes the
+        // token-by-token path, which does not use these operands
+        const float inv0 = __builtin_amdgcn_rcpf(lam0), inv1 = __builtin_amdgcn_rcpf(lam1);
+        _Float16* Abar = VOk;
+        _Float16* Rbar = VOk + kM64;
+        _Float16* BbT = VOk + 2 * kM64;
+        _Float16* KbT = BbT + kMT;
+        _Float16* Vt = KbT + kMT;
+        // range of the raw inputs (|Abar| <= |a| etc. when every |w| <= 1)
+        uint32_t mx = 0u, mw = 0u;
+  #pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          mx = absmax_bits(mx, x.a[e]); mx = absmax_bits(mx, x.r[e]);
+          mx = absmax_bits(mx, x.b[e]); mx = absmax_bits(mx, x.k[e]);
+          mx = absmax_bits(mx, x.v[e]); mw = absmax_bits(mw, x.w[e]);
+        }
+        bad_k = !(lam0 >= kMinLamL) || !(lam1 >= kMinLamL) ||
+                any_half_ge(mx, 0x4700u) ||     // |x| >= 2^15 (or NaN/Inf)
+                any_half_ge(mw, 0x3f81u);       // |w| > 1 (or NaN)
+        float sfx0 = suf0, sfx1 = suf1;
+        float bt0[4], bt1[4], kt0[4], kt1[4], vt0[4], vt1[4];
+  #pragma unroll
+        for (int e = 3; e >= 0; --e) {
+          const int t = 4 * rg + e;
+          const float lp0 = e == 0 ? pre0 : pre0 * P0[e - 1];
+          const float lp1 = e == 0 ? pre1 : pre1 * P1[e - 1];
+          const float lt0 = pre0 * P0[e], lt1 = pre1 * P1[e];
+          const float ab0 = bf_lo(x.a[e]) * lp0, ab1 = bf_hi(x.a[e]) * lp1;
+          const float rb0 = bf_lo(x.r[e]) * lt0, rb1 = bf_hi(x.r[e]) * lt1;
+          const float bb0 = bf_lo(x.b[e]) * sfx0, bb1 = bf_hi(x.b[e]) * sfx1;
+          const float kb0 = bf_lo(x.k[e]) * sfx0, kb1 = bf_hi(x.k[e]) * sfx1;
+          put2p(Ahat, kM64, kP64, t, j0, ab0 * inv0, ab1 * inv1);
+          put2p(Rhat, kM64, kP64, t, j0, rb0 * inv0, rb1 * inv1);
+          put2p(Bbar, kM64, kP64, t, j0, bb0, bb1);
+          put2p(Kbar, kM64, kP64, t, j0, kb0, kb1);
+          put2h(Abar, kP64, t, j0, ab0, ab1);
+          put2h(Rbar, kP64, t, j0, rb0, rb1);
+          bt0[e] = bb0; bt1[e] = bb1; kt0[e] = kb0; kt1[e] = kb1;
+          vt0[e] = bf_lo(x.v[e]); vt1[e] = bf_hi(x.v[e]);
+          sfx0 *= w0[e]; sfx1 *= w1[e];
+        }
+        put4h(BbT, kP32, j0, 4 * rg, f32x4{bt0[0], bt0[1], bt0[2], bt0[3]});
+        put4h(BbT, kP32, j0 + 1, 4 * rg, f32x4{bt1[0], bt1[1], bt1[2], bt1[3]});
+        put4h(KbT, kP32, j0, 4 * rg, f32x4{kt0[0], kt0[1], kt0[2], kt0[3]});
+        put4h(KbT, kP32, j0 + 1, 4 * rg, f32x4{kt1[0], kt1[1], kt1[2], kt1[3]});
+        put4h(Vt, kP32, j0, 4 * rg, f32x4{vt0[0], vt0[1], vt0[2], vt0[3]});
+        put4h(Vt, kP32, j0 + 1, 4 * rg, f32x4{vt1[0], vt1[1], vt1[2], vt1[3]});
+        // next chunk's inputs, in flight from here on
+        if (cK + 1 < nch)
+          load_raw(nxt, p, t0K + kL, min(kL, len - (cK + 1) * kL), h, rg, jp);
       }
-      const int wq = 2 * (wv & 3);
-      const bool second = (lane >> 5) != 0;   // group wq + 1
-      const float ga0 = g0[wq], ga1 = g1[wq], gb0 = g0[wq + 1], gb1 = g1[wq + 1];
-      const float pre0 = second ? lo0 * ga0 : lo0, pre1 = second ? lo1 * ga1 : lo1;
-      const float suf0 = second ? hi0 : gb0 * hi0, suf1 = second ? hi1 : gb1 * hi1;
-      const float lam0 = (lo0 * ga0) * (gb0 * hi0), lam1 = (lo1 * ga1) * (gb1 * hi1);
-      if (rg == 0) { LAMb[bK * 64 + j0] = lam0; LAMb[bK * 64 + j0 + 1] = lam1; }
-      // hardware reciprocal (1 ulp): the scaled Gram operands are split into
-      // bf16 pairs, far coarser; a lam below the fast path's range takes the
-      // token-by-token path, which does not use these operands
-      const float inv0 = __builtin_amdgcn_rcpf(lam0), inv1 = __builtin_amdgcn_rcpf(lam1);
-      _Float16* Abar = VOk;
-      _Float16* Rbar = VOk + kM64;
-      _Float16* BbT = VOk + 2 * kM64;
-      _Float16* KbT = BbT + kMT;
-      _Float16* Vt = KbT + kMT;
-      // range of the raw inputs (|Abar| <= |a| etc. when every |w| <= 1)
-      uint32_t mx = 0u, mw = 0u;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        mx = absmax_bits(mx, x.a[e]); mx = absmax_bits(mx, x.r[e]);
-        mx = absmax_bits(mx, x.b[e]); mx = absmax_bits(mx, x.k[e]);
-        mx = absmax_bits(mx, x.v[e]); mw = absmax_bits(mw, x.w[e]);
-      }
-      bad_k = !(lam0 >= kMinLamL) || !(lam1 >= kMinLamL) ||
-              any_half_ge(mx, 0x4700u) ||     // |x| >= 2^15 (or NaN/Inf)
-              any_half_ge(mw, 0x3f81u);       // |w| > 1 (or NaN)
-      float sfx0 = suf0, sfx1 = suf1;
-      float bt0[4], bt1[4], kt0[4], kt1[4], vt0[4], vt1[4];
-#pragma unroll
-      for (int e = 3; e >= 0; --e) {
-        const int t = 4 * rg + e;
-        const float lp0 = e == 0 ? pre0 : pre0 * P0[e - 1];
-        const float lp1 = e == 0 ? pre1 : pre1 * P1[e - 1];
-        const float lt0 = pre0 * P0[e], lt1 = pre1 * P1[e];
-        const float ab0 = bf_lo(x.a[e]) * lp0, ab1 = bf_hi(x.a[e]) * lp1;
-        const float rb0 = bf_lo(x.r[e]) * lt0, rb1 = bf_hi(x.r[e]) * lt1;
-        const float bb0 = bf_lo(x.b[e]) * sfx0, bb1 = bf_hi(x.b[e]) * sfx1;
-        const float kb0 = bf_lo(x.k[e]) * sfx0, kb1 = bf_hi(x.k[e]) * sfx1;
-        put2p(Ahat, kM64, kP64, t, j0, ab0 * inv0, ab1 * inv1);
-        put2p(Rhat, kM64, kP64, t, j0, rb0 * inv0, rb1 * inv1);
-        put2p(Bbar, kM64, kP64, t, j0, bb0, bb1);
-        put2p(Kbar, kM64, kP64, t, j0, kb0, kb1);
-        put2h(Abar, kP64, t, j0, ab0, ab1);
-        put2h(Rbar, kP64, t, j0, rb0, rb1);
-        bt0[e] = bb0; bt1[e] = bb1; kt0[e] = kb0; kt1[e] = kb1;
-        vt0[e] = bf_lo(x.v[e]); vt1[e] = bf_hi(x.v[e]);
-        sfx0 *= w0[e]; sfx1 *= w1[e];
-      }
-      put4h(BbT, kP32, j0, 4 * rg, f32x4{bt0[0], bt0[1], bt0[2], bt0[3]});
-      put4h(BbT, kP32, j0 + 1, 4 * rg, f32x4{bt1[0], bt1[1], bt1[2], bt1[3]});
-      put4h(KbT, kP32, j0, 4 * rg, f32x4{kt0[0], kt0[1], kt0[2], kt0[3]});
-      put4h(KbT, kP32, j0 + 1, 4 * rg, f32x4{kt1[0], kt1[1], kt1[2], kt1[3]});
-      put4h(Vt, kP32, j0, 4 * rg, f32x4{vt0[0], vt0[1], vt0[2], vt0[3]});
-      put4h(Vt, kP32, j0 + 1, 4 * rg, f32x4{vt1[0], vt1[1], vt1[2], vt1[3]});
-      // next chunk's inputs, in flight from here on
-      if (cK + 1 < nch)
-        load_raw(nxt, p, t0K + kL, min(kL, len - (cK + 1) * kL), h, rg, jp);
-    }
-    // value side, first half: X and T of chunk cV (or the whole chunk exactly)
-    bool v_exact_done = false;
-    float inv_s = 1.f;
-    f16x8 Sf0 = {}, Sf1 = {}, Vf = {}, Tf0 = {}, Tf1 = {};
-    f32x4 X[2] = {z, z};
-    if (v_on) {
-      bool exact = early_prev || gram_prev;
-      if (!exact) {
-        const _Float16* Abar = VOv;
-        const _Float16* Vt = VOv + 2 * kM64 + 2 * kMT;
-        const _Float16* Aak = LLv;
-        float m = 0.f;
-#pragma unroll
-        for (int jt = 0; jt < 4; ++jt) m = abs_max4(S[jt], m);
-        const float sS = pow2_scale(wave_max(m), &inv_s);
-        Sf0 = frag8h(S[0], S[1], sS);
-        Sf1 = frag8h(S[2], S[3], sS);
-        Vf = ldh8(Vt, kP32, 16 * vb + n16, 0, g);
-#pragma unroll
+      // B2. The range flags of chunk cK travel with B3: its Grams are built
+      // either way, and the value side reads them only if no flag was
+      // raised.
+      __syncthreads();                                            // B2
+      // ===== interval 2 =====
+      float gmax = 0.f;
+      if (k_on) {
+        // key: Gram matrix wv, tiles (tt, st) = (0,0), (1,0), (1,1) as C[s][t]
+        const __bf16* Pm = (wv & 1) ? Kbar : Bbar;
+        const __bf16* Qm = (wv >= 2) ? Rhat : Ahat;
+        const bool strict = wv < 2;
+        f32x4 gt[3];
+        int ti = 0;
+  #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-          f32x4 cs = mmah(ldh8(Abar, kP64, 16 * tt + n16, 0, g), Sf0, z);
-          cs = mmah(ldh8(Abar, kP64, 16 * tt + n16, 32, g), Sf1, cs);
-          const f32x4 cv = mmah(ldh8(Aak, kP32, 16 * tt + n16, 0, g), Vf, z);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) X[tt][r] = fmaf(cs[r], inv_s, cv[r]);
+  #pragma unroll
+          for (int st = 0; st <= tt; ++st) {
+            f32x4 c = z;
+  #pragma unroll
+            for (int kc = 0; kc < 2; ++kc)
+              c = mm3(ldp8(Pm, kM64, kP64, 16 * st + n16, 32 * kc, g),
+                      ldp8(Qm, kM64, kP64, 16 * tt + n16, 32 * kc, g), c);
+            const int t = 16 * tt + n16;
+  #pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int s = 16 * st + 4 * g + r;
+              const bool keep = strict ? (s < t) : (s <= t);
+              c[r] = keep ? c[r] : 0.f;
+            }
+            gt[ti++] = c;
+          }
         }
-        // T = [[D_0, 0], [T_10, D_1]], D_p = (I - A_pp)^-1, T_10 = D_1 A_10 D_0
-        const _Float16* ABr = AB;
-        const _Float16* ABt = ABr + kM32;
-        const Frag D0 = inverse_unit_lower(ldh4(ABr, kP32, n16, 4 * g),
-                                           ldh4(ABt, kP32, n16, 4 * g), g, n16);
-        const Frag D1 = inverse_unit_lower(ldh4(ABr, kP32, 16 + n16, 16 + 4 * g),
-                                           ldh4(ABt, kP32, 16 + n16, 16 + 4 * g), g, n16);
-        // Y = A_10 D_0 needs row(A_10) and col(D_0) only
-        const f16x4 a10 = ldh4(ABr, kP32, 16 + n16, 4 * g);
-        Frag Y;
-        Y.fcol = mmh16(a10, D0.col, z);
-        Y.frow = mmh16(D0.col, a10, z);
-        Y.row = h4(Y.frow);
-        Y.col = h4(Y.fcol);
-        const Frag T10 = product(D1, Y);
-        float tm = abs_max4(D0.frow, 0.f);
-        tm = abs_max4(D1.frow, tm);
-        tm = abs_max4(T10.frow, tm);
-        // operand fragments of T's row tiles: k in [0,16) then [16,32)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          Tf0[r] = static_cast<_Float16>(D0.frow[r]);
-          Tf0[4 + r] = static_cast<_Float16>(0.f);
-          Tf1[r] = static_cast<_Float16>(T10.frow[r]);
-          Tf1[4 + r] = static_cast<_Float16>(D1.frow[r]);
+        if (wv == 0) {
+          // A_ab in fp16 as [t][s] rows and as [s][t] rows (tile ti holds
+          // C[s][t] = A_ab[t][s])
+          _Float16* ABr = AB;
+          _Float16* ABt = ABr + kM32;
+          ti = 0;
+  #pragma unroll
+          for (int tt = 0; tt < 2; ++tt) {
+  #pragma unroll
+            for (int st = 0; st <= tt; ++st, ++ti) {
+              gmax = abs_max4(gt[ti], gmax);
+              put4h(ABr, kP32, 16 * tt + n16, 16 * st + 4 * g, gt[ti]);
+  #pragma unroll
+              for (int r = 0; r < 4; ++r)
+                ABt[(16 * st + 4 * g + r) * kP32 + 16 * tt + n16] =
+                    static_cast<_Float16>(gt[ti][r]);
+            }
+          }
+        } else {
+          _Float16* dst = LLk + (wv - 1) * kM32;
+          ti = 0;
+  #pragma unroll
+          for (int tt = 0; tt < 2; ++tt) {
+  #pragma unroll
+            for (int st = 0; st <= tt; ++st, ++ti) {
+              gmax = abs_max4(gt[ti], gmax);
+              put4h(dst, kP32, 16 * tt + n16, 16 * st + 4 * g, gt[ti]);
+            }
+          }
+          put4h(dst, kP32, n16, 16 + 4 * g, z);
         }
-        exact = !(wave_max(tm) < kHalfSafe);   // T out of fp16 range
       }
-      if (exact) {
-        // the whole chunk token by token
-        exact_chunk(p, S, t0V, nV, h, vb, g, n16, zero_v, no_out);
-        v_exact_done = true;
-      }
+      if (cK + 1 < nch) prep(cK + 1);   // the next chunk
+      (void)barrier_or2(FLG + 8, wv, lane, k_on && bad_k,
+                        k_on && !(gmax < kHalfSafe));             // B3
     }
-    // B2. The key side's range flags for chunk cK travel with B3: its Grams
-    // are built either way, and the value side reads them only if no flag
-    // was raised.
-    __syncthreads();                                              // B2
-
-    // ===== interval 2 =====
-    float gmax = 0.f;
-    if (k_on) {
-      // key: Gram matrix wv, tiles (tt, st) = (0,0), (1,0), (1,1) as C[s][t]
-      const __bf16* Pm = (wv & 1) ? Kbar : Bbar;
-      const __bf16* Qm = (wv >= 2) ? Rhat : Ahat;
-      const bool strict = wv < 2;
-      f32x4 gt[3];
-      int ti = 0;
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-#pragma unroll
-        for (int st = 0; st <= tt; ++st) {
-          f32x4 c = z;
-#pragma unroll
-          for (int kc = 0; kc < 2; ++kc)
-            c = mm3(ldp8(Pm, kM64, kP64, 16 * st + n16, 32 * kc, g),
-                    ldp8(Qm, kM64, kP64, 16 * tt + n16, 32 * kc, g), c);
-          const int t = 16 * tt + n16;
-#pragma unroll
+  } else {
+    // fallback flags of chunk step - 1, known from the end of the step
+    // before: early (its inputs or decays out of the fast path's range)
+    // and gram (its Gram matrices out of the fp16 range)
+    bool early_prev = false, gram_prev = false;
+    // The start state has arrived before the loop: without this wait the
+    // compiler keeps S's registers pending from these loads and, at every
+    // state update, waits for the step's output stores as well.
+    __builtin_amdgcn_s_waitcnt(0x0F70);                // vmcnt(0)
+    for (int step = 0; step <= nch; ++step) {
+      const int cV = step - 1;      // chunk whose T is built and value side run
+      const bool v_on = cV >= 0;
+      const int bV = cV & 1;
+      const _Float16* VOv = reinterpret_cast<const _Float16*>(lds + kOffVO + bV * kVOBytes);
+      const _Float16* LLv = reinterpret_cast<const _Float16*>(lds + kOffLL + bV * kLLBytes);
+      const int nV = min(kL, len - cV * kL);
+      const int t0V = tok0 + cV * kL;
+      // ===== interval 1 =====
+      // value side, first half: X and T of chunk cV (or the whole chunk exactly)
+      bool v_exact_done = false;
+      float inv_s = 1.f;
+      f16x8 Sf0 = {}, Sf1 = {}, Vf = {}, Tf0 = {}, Tf1 = {};
+      f32x4 X[2] = {z, z};
+      if (v_on) {
+        bool exact = early_prev || gram_prev;
+        if (!exact) {
+          const _Float16* Abar = VOv;
+          const _Float16* Vt = VOv + 2 * kM64 + 2 * kMT;
+          const _Float16* Aak = LLv;
+          float m = 0.f;
+  #pragma unroll
+          for (int jt = 0; jt < 4; ++jt) m = abs_max4(S[jt], m);
+          const float sS = pow2_scale(wave_max(m), &inv_s);
+          Sf0 = frag8h(S[0], S[1], sS);
+          Sf1 = frag8h(S[2], S[3], sS);
+          Vf = ldh8(Vt, kP32, 16 * vb + n16, 0, g);
+  #pragma unroll
+          for (int tt = 0; tt < 2; ++tt) {
+            f32x4 cs = mmah(ldh8(Abar, kP64, 16 * tt + n16, 0, g), Sf0, z);
+            cs = mmah(ldh8(Abar, kP64, 16 * tt + n16, 32, g), Sf1, cs);
+            const f32x4 cv = mmah(ldh8(Aak, kP32, 16 * tt + n16, 0, g), Vf, z);
+  #pragma unroll
+            for (int r = 0; r < 4; ++r) X[tt][r] = fmaf(cs[r], inv_s, cv[r]);
+          }
+          // T = [[D_0, 0], [T_10, D_1]], D_p = (I - A_pp)^-1, T_10 = D_1 A_10 D_0
+          const _Float16* ABr = AB;
+          const _Float16* ABt = ABr + kM32;
+          const Frag D0 = inverse_unit_lower(ldh4(ABr, kP32, n16, 4 * g),
+                                             ldh4(ABt, kP32, n16, 4 * g), g, n16);
+          const Frag D1 = inverse_unit_lower(ldh4(ABr, kP32, 16 + n16, 16 + 4 * g),
+                                             ldh4(ABt, kP32, 16 + n16, 16 + 4 * g), g, n16);
+          // Y = A_10 D_0 needs row(A_10) and col(D_0) only
+          const f16x4 a10 = ldh4(ABr, kP32, 16 + n16, 4 * g);
+          Frag Y;
+          Y.fcol = mmh16(a10, D0.col, z);
+          Y.frow = mmh16(D0.col, a10, z);
+          Y.row = h4(Y.frow);
+          Y.col = h4(Y.fcol);
+          const Frag T10 = product(D1, Y);
+          float tm = abs_max4(D0.frow, 0.f);
+          tm = abs_max4(D1.frow, tm);
+          tm = abs_max4(T10.frow, tm);
+          // operand fragments of T's row tiles: k in [0,16) then [16,32)
+  #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int s = 16 * st + 4 * g + r;
-            const bool keep = strict ? (s < t) : (s <= t);
-            c[r] = keep ? c[r] : 0.f;
+            Tf0[r] = static_cast<_Float16>(D0.frow[r]);
+            Tf0[4 + r] = static_cast<_Float16>(0.f);
+            Tf1[r] = static_cast<_Float16>(T10.frow[r]);
+            Tf1[4 + r] = static_cast<_Float16>(D1.frow[r]);
           }
-          gt[ti++] = c;
+          exact = !(wave_max(tm) < kHalfSafe);   // T out of fp16 range
+        }
+        if (exact) {
+          // the whole chunk token by token
+          exact_chunk(p, S, t0V, nV, h, vb, g, n16, zero_v, no_out);
+          v_exact_done = true;
         }
       }
-      if (wv == 0) {
-        // A_ab in fp16 as [t][s] rows and as [s][t] rows (tile ti holds
-        // C[s][t] = A_ab[t][s])
-        _Float16* ABr = AB;
-        _Float16* ABt = ABr + kM32;
-        ti = 0;
-#pragma unroll
+      __syncthreads();                                            // B2
+      // ===== interval 2 =====
+      if (v_on && !v_exact_done) {
+        // value side, second half: U, O, state update of chunk cV
+        const _Float16* Rbar = VOv + kM64;
+        const _Float16* BbT = VOv + 2 * kM64;
+        const _Float16* KbT = BbT + kMT;
+        const _Float16* Mrb = LLv + kM32;
+        const _Float16* Mrk = LLv + 2 * kM32;
+        const float* lam = LAMb + bV * 64;
+        float inv_x;
+        const float sX = pow2_scale(wave_max(abs_max4(X[1], abs_max4(X[0], 0.f))), &inv_x);
+        const f16x8 Xf = frag8h(X[0], X[1], sX);
+        f32x4 U[2];
+        U[0] = mmah(Tf0, Xf, z);
+        U[1] = mmah(Tf1, Xf, z);
+        float inv_u;
+        const float sU = pow2_scale(wave_max(abs_max4(U[1], abs_max4(U[0], 0.f))), &inv_u);
+        const float inv_ux = inv_u * inv_x;
+        const f16x8 Uf = frag8h(U[0], U[1], sU);
+  #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-#pragma unroll
-          for (int st = 0; st <= tt; ++st, ++ti) {
-            gmax = abs_max4(gt[ti], gmax);
-            put4h(ABr, kP32, 16 * tt + n16, 16 * st + 4 * g, gt[ti]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              ABt[(16 * st + 4 * g + r) * kP32 + 16 * tt + n16] =
-                  static_cast<_Float16>(gt[ti][r]);
+          f32x4 cs = mmah(Sf0, ldh8(Rbar, kP64, 16 * tt + n16, 0, g), z);
+          cs = mmah(Sf1, ldh8(Rbar, kP64, 16 * tt + n16, 32, g), cs);
+          const f32x4 cu = mmah(Uf, ldh8(Mrb, kP32, 16 * tt + n16, 0, g), z);
+          const f32x4 cv = mmah(Vf, ldh8(Mrk, kP32, 16 * tt + n16, 0, g), z);
+          const int t = 16 * tt + n16;
+          if (t < nV && !no_out) {
+            float4 ov;
+            ov.x = fmaf(cs[0], inv_s, fmaf(cu[0], inv_ux, cv[0]));
+            ov.y = fmaf(cs[1], inv_s, fmaf(cu[1], inv_ux, cv[1]));
+            ov.z = fmaf(cs[2], inv_s, fmaf(cu[2], inv_ux, cv[2]));
+            ov.w = fmaf(cs[3], inv_s, fmaf(cu[3], inv_ux, cv[3]));
+            *reinterpret_cast<float4*>(p.o + static_cast<size_t>(t0V + t) * rowstride
+                                       + static_cast<size_t>(h) * kN + 16 * vb + 4 * g) = ov;
           }
         }
-      } else {
-        _Float16* dst = LLk + (wv - 1) * kM32;
-        ti = 0;
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-#pragma unroll
-          for (int st = 0; st <= tt; ++st, ++ti) {
-            gmax = abs_max4(gt[ti], gmax);
-            put4h(dst, kP32, 16 * tt + n16, 16 * st + 4 * g, gt[ti]);
-          }
-        }
-        put4h(dst, kP32, n16, 16 + 4 * g, z);
-      }
-    }
-    if (is_key && cK + 1 < nch) prep(cK + 1);   // key: prepare the next chunk
-    if (v_on && !v_exact_done) {
-      // value side, second half: U, O, state update of chunk cV
-      const _Float16* Rbar = VOv + kM64;
-      const _Float16* BbT = VOv + 2 * kM64;
-      const _Float16* KbT = BbT + kMT;
-      const _Float16* Mrb = LLv + kM32;
-      const _Float16* Mrk = LLv + 2 * kM32;
-      const float* lam = LAMb + bV * 64;
-      float inv_x;
-      const float sX = pow2_scale(wave_max(abs_max4(X[1], abs_max4(X[0], 0.f))), &inv_x);
-      const f16x8 Xf = frag8h(X[0], X[1], sX);
-      f32x4 U[2];
-      U[0] = mmah(Tf0, Xf, z);
-      U[1] = mmah(Tf1, Xf, z);
-      float inv_u;
-      const float sU = pow2_scale(wave_max(abs_max4(U[1], abs_max4(U[0], 0.f))), &inv_u);
-      const float inv_ux = inv_u * inv_x;
-      const f16x8 Uf = frag8h(U[0], U[1], sU);
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        f32x4 cs = mmah(Sf0, ldh8(Rbar, kP64, 16 * tt + n16, 0, g), z);
-        cs = mmah(Sf1, ldh8(Rbar, kP64, 16 * tt + n16, 32, g), cs);
-        const f32x4 cu = mmah(Uf, ldh8(Mrb, kP32, 16 * tt + n16, 0, g), z);
-        const f32x4 cv = mmah(Vf, ldh8(Mrk, kP32, 16 * tt + n16, 0, g), z);
-        const int t = 16 * tt + n16;
-        if (t < nV && !no_out) {
-          float4 ov;
-          ov.x = fmaf(cs[0], inv_s, fmaf(cu[0], inv_ux, cv[0]));
-          ov.y = fmaf(cs[1], inv_s, fmaf(cu[1], inv_ux, cv[1]));
-          ov.z = fmaf(cs[2], inv_s, fmaf(cu[2], inv_ux, cv[2]));
-          ov.w = fmaf(cs[3], inv_s, fmaf(cu[3], inv_ux, cv[3]));
-          *reinterpret_cast<float4*>(p.o + static_cast<size_t>(t0V + t) * rowstride
-                                     + static_cast<size_t>(h) * kN + 16 * vb + 4 * g) = ov;
+  #pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+          const f32x4 cu = mmah(ldh8(BbT, kP32, 16 * jt + n16, 0, g), Uf, z);
+          const f32x4 cv = mmah(ldh8(KbT, kP32, 16 * jt + n16, 0, g), Vf, z);
+  #pragma unroll
+          for (int r = 0; r < 4; ++r)
+            S[jt][r] = fmaf(lam[16 * jt + 4 * g + r], S[jt][r],
+                            fmaf(cu[r], inv_ux, cv[r]));
         }
       }
-#pragma unroll
-      for (int jt = 0; jt < 4; ++jt) {
-        const f32x4 cu = mmah(ldh8(BbT, kP32, 16 * jt + n16, 0, g), Uf, z);
-        const f32x4 cv = mmah(ldh8(KbT, kP32, 16 * jt + n16, 0, g), Vf, z);
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          S[jt][r] = fmaf(lam[16 * jt + 4 * g + r], S[jt][r],
-                          fmaf(cu[r], inv_ux, cv[r]));
-      }
+      const uint32_t f3 = barrier_or2(FLG + 8, wv, lane, false, false);  // B3
+      early_prev = (f3 & 1u) != 0;
+      gram_prev = (f3 & 2u) != 0;
     }
-    const uint32_t f3 = barrier_or2(FLG + 8, wv, lane, k_on && bad_k,
-                                    k_on && !(gmax < kHalfSafe));  // B3
-    early_prev = (f3 & 1u) != 0;
-    gram_prev = (f3 & 2u) != 0;
-  }
-
-  if (!is_key && s_out) {
+    if (s_out) {
 #pragma unroll
-    for (int jt = 0; jt < 4; ++jt)
-      *(gf32x4*)(s_out + soff + 16 * jt) = S[jt];
+      for (int jt = 0; jt < 4; ++jt)
+        *(gf32x4*)(s_out + soff + 16 * jt) = S[jt];
+    }
   }
 }
 
