@@ -121,10 +121,10 @@ def rel_max_err(got: np.ndarray, ref: np.ndarray,
     """max |got - ref| / rms(scale or ref), in float64 (the parity metric)."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
-    sc = ref if scale is None else np.asarray(scale, dtype=np.float64)
-    rms = float(np.sqrt(np.mean(sc * sc)))
     if got.size == 0:
         return 0.0
+    sc = ref if scale is None else np.asarray(scale, dtype=np.float64)
+    rms = float(np.sqrt(np.mean(sc * sc)))
     if rms == 0.0:
         return float(np.max(np.abs(got - ref)))
     return float(np.max(np.abs(got - ref)) / rms)

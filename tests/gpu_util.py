@@ -8,6 +8,7 @@ import numpy as np
 import torch
 
 from linear_attention_rnn_amd import wkv7 as W
+from oracle import rel_max_err
 from wkv7_inputs import NAMES, as_f64
 
 DEV = "cuda:0"
@@ -53,10 +54,8 @@ def run_forward(pool, batch, stream=None):
 
 
 def rel_err(got, ref):
-    got = np.asarray(got, dtype=np.float64)
-    ref = np.asarray(ref, dtype=np.float64)
-    rms = np.sqrt(np.mean(ref * ref))
-    return float(np.max(np.abs(got - ref)) / rms) if got.size else 0.0
+    """The parity metric, max |got - ref| / rms(ref) (oracle.rel_max_err)."""
+    return rel_max_err(got, ref)
 
 
 def tol_for(dtype):

@@ -129,33 +129,3 @@ def test_chunked_matches_sequential_within_rounding():
                         min_len=1 << 30)
     assert rel_err(o1, o2.double().numpy()) < GUARD["bf16", 0]
     assert rel_err(S1, S2.double().numpy()) < GUARD["bf16", 0]
-
-
-def test_prefill_full_size_sampled():
-    """8 sequences of T=4096, H=32, bf16, zero state, in the launch
-    configuration the benchmark times; outputs and final states of sampled
-    (sequence, head) pairs against the oracle, run one pair at a time."""
-    wl = G.cfg_prefill(seed=2)
-    b = wl.batch
-    say(f"prefill {wl.name}: T_tot={b.T_tot}")
-    pool = W.wkv7_pool_create(wl.n_slots, wl.H, 64)
-    try:
-        o = run_forward(pool, b)
-        S = get_states(pool, b.slot_ids)
-    finally:
-        W.wkv7_pool_destroy(pool)
-    assert np.all(np.isfinite(o.numpy()))
-    rng = np.random.default_rng(5)
-    pairs = [(int(s), int(hh)) for s, hh in
-             zip(rng.integers(0, 8, 6), rng.integers(0, wl.H, 6))]
-    worst_o = worst_s = 0.0
-    for s, hh in pairs:
-        lo, hi = b.cu_seqlens[s], b.cu_seqlens[s + 1]
-        x = {n: G.as_f64(b.inputs[n][lo:hi, hh]) for n in G.NAMES}
-        o_ref, S_ref = wkv7_sequence(np.zeros((64, 64)), **x)
-        e_o = rel_err(o[lo:hi, hh], o_ref)
-        e_s = rel_err(S[s, hh], S_ref)
-        say(f"  seq {s} head {hh}: o err {e_o:.3e}  S err {e_s:.3e}")
-        worst_o, worst_s = max(worst_o, e_o), max(worst_s, e_s)
-    assert worst_o < 2e-2 and worst_s < 2e-2
-    assert worst_o < GUARD["bf16", 0] and worst_s < GUARD["bf16", 0]

@@ -46,40 +46,6 @@ def test_small_config_sequential(dtype):
     assert e_o < tol_for(dtype)
 
 
-def test_decode_full_size_steps():
-    """Decode: 256 random ids of a 1024-slot pool, H=32, bf16; 3 steps.
-
-    Also checks that the 768 inactive slots stay bit-identical.
-    """
-    wl = G.cfg_decode(seed=1)
-    ids = wl.batch.slot_ids
-    say(f"decode {wl.name}: ids={len(ids)} H={wl.H}")
-    pool = _pool(wl.n_slots, wl.H)
-    try:
-        # inactive slots hold a recognisable random pattern
-        rng = np.random.default_rng(99)
-        others = np.setdiff1d(np.arange(wl.n_slots), ids).astype(np.int32)
-        other_states = G.draw_states(rng, len(others), wl.H, wl.N, std=1.0)
-        set_states(pool, others, other_states)
-        set_states(pool, ids, wl.init_states)
-        S = G.as_f64(wl.init_states)
-        for step in range(3):
-            b = G.decode_step_inputs(1, step, ids, wl.H, wl.N)
-            o = run_forward(pool, b)
-            o_ref, S = wkv7_decode_batch(S, b.inputs64())
-            got_S = get_states(pool, ids)
-            e_o, e_s = rel_err(o, o_ref), rel_err(got_S, S)
-            say(f"  step {step}: o err {e_o:.3e}  S err {e_s:.3e}")
-            assert e_o < 1e-5 and e_s < 1e-5
-            S = G.as_f64(got_S)   # continue from the device state
-        after = get_states(pool, others)
-        assert torch.equal(after.view(torch.int32),
-                           other_states.view(torch.int32)), \
-            "inactive slots changed"
-    finally:
-        W.wkv7_pool_destroy(pool)
-
-
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_ragged_sequential(dtype):
     """Ragged lengths incl. 0, 1, a tile edge and a ragged tail; mixed
