@@ -167,6 +167,36 @@ wkv7_status wkv7_forward(wkv7_pool* pool, const int32_t* slot_ids,
                          const void* k, const void* v, const void* a,
                          const void* b, float* o, void* stream);
 
+/* forward without allocation — for callers that cannot allocate device or
+ * pinned memory during the call (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation). The same validation,
+ * errors, kernels and results, bit for bit, as wkv7_forward on the same
+ * arguments; the difference is where the kernels' scratch lives.
+ *
+ * The work description and, with WKV7_OPT_SEGMENT_LEN on, the segment
+ * buffers (three H*N*N float32 blocks per segment) go into one static
+ * device array of 32 MiB that the library holds on every GPU it runs on
+ * until the process ends (its address is looked up once per device, at the
+ * first pool creation there). The work description (16 bytes per
+ * non-empty sequence, plus 32 bytes per segment and per split sequence when
+ * segments are on) may take at most 64 KiB of it, and both parts together
+ * at most 32 MiB; a larger batch fails with WKV7_ERR_INVALID_ARG before any
+ * device work. The work description is copied in through one of the
+ * pool's pinned staging buffers, preallocated at pool creation; the call
+ * waits on the host only when that buffer's previous copy (eight calls
+ * earlier) has not yet run. The call itself makes no device, pinned or
+ * runtime allocation.
+ *
+ * Every call on a GPU, from any pool, uses that GPU's one array, which keeps
+ * the last call's contents: calls on one GPU must be ordered (one stream,
+ * or events); calls that overlap on one GPU race and give wrong results.
+ * Nothing in the array needs to start at zero. */
+wkv7_status wkv7_forward_noalloc(wkv7_pool* pool, const int32_t* slot_ids,
+                                 const int32_t* cu_seqlens, int32_t n_seqs,
+                                 int32_t dtype, const void* r, const void* w,
+                                 const void* k, const void* v, const void* a,
+                                 const void* b, float* o, void* stream);
+
 /* plans — the metadata of a batch, validated once and kept on the device,
  * for callers that run the same batch layout step after step (steady-state
  * decode) or capture steps into a HIP graph. Page "rvLLM", section "What

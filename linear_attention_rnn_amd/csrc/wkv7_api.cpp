@@ -44,6 +44,9 @@ wkv7_status fail_hip(hipError_t e, const char* what) {
 // completed, so the host never overwrites data a queued copy still reads,
 // whatever stream the calls used.
 constexpr int kRing = 8;
+// Every entry holds at least this many int32 (allocated at pool creation, so
+// the allocation-free forward can stage through any entry).
+constexpr size_t kStageMinInts = wkv7::kStaticMetaBytes / 4;
 
 struct Stage {
   int32_t* host = nullptr;
@@ -84,6 +87,7 @@ struct wkv7_pool {
   size_t seg_scratch_floats = 0;
   float* xfer_stage = nullptr;       // staging of scattered hibernate/resume
   size_t xfer_stage_bytes = 0;
+  void* static_scratch = nullptr;    // the device's static scratch array
   int n_cus = 0;                     // compute units of the pool's device
   std::vector<int32_t> free_ids;     // stack; top = back
   std::vector<uint8_t> allocated;
@@ -135,7 +139,7 @@ wkv7_status stage_upload(wkv7_pool* p, const int32_t* data, size_t n,
     s.pending = false;
   }
   if (s.cap_ints < n) {
-    size_t cap = std::max<size_t>(n, 4096);
+    size_t cap = std::max<size_t>(n, kStageMinInts);
     if (s.host) (void)hipHostFree(s.host);
     if (s.dev) (void)hipFree(s.dev);
     s.host = nullptr;
@@ -530,13 +534,25 @@ wkv7_status wkv7_pool_create(int32_t n_slots, int32_t H, int32_t N,
   // the host through them, so they skip the system-scope cache writeback and
   // invalidation of a default event (measured: ~1 us of GPU time per call
   // instead of ~3).
-  for (int i = 0; e == hipSuccess && i < kRing; ++i)
-    e = hipEventCreateWithFlags(&p->ring[i].ev,
+  for (int i = 0; e == hipSuccess && i < kRing; ++i) {
+    Stage& st = p->ring[i];
+    e = hipEventCreateWithFlags(&st.ev,
                                 hipEventDisableTiming | hipEventDisableSystemFence);
+    if (e == hipSuccess)
+      e = hipHostMalloc(reinterpret_cast<void**>(&st.host), kStageMinInts * 4);
+    if (e == hipSuccess)
+      e = hipMalloc(reinterpret_cast<void**>(&st.dev), kStageMinInts * 4);
+    if (e == hipSuccess) st.cap_ints = kStageMinInts;
+  }
   if (e != hipSuccess) {
     std::string msg = std::string("pool initialisation: ") + hipGetErrorString(e);
     wkv7_pool_destroy(p);
     return fail(WKV7_ERR_HIP, "%s", msg.c_str());
+  }
+  if (wkv7_status st = wkv7::static_scratch_setup(&p->static_scratch)) {
+    std::string msg = g_last_error;
+    wkv7_pool_destroy(p);
+    return fail(st, "%s", msg.c_str());
   }
   p->allocated.assign(static_cast<size_t>(n_slots), 0);
   p->free_ids.resize(static_cast<size_t>(n_slots));
@@ -666,6 +682,66 @@ wkv7_status wkv7_forward(wkv7_pool* p, const int32_t* slot_ids,
   if (wkv7_status st = launch_batch(p, L, dtype, r, w, k, v, a, b, o, hs))
     return st;
   return stage_commit(stage, hs);
+}
+
+wkv7_status wkv7_forward_noalloc(wkv7_pool* p, const int32_t* slot_ids,
+                                 const int32_t* cu_seqlens, int32_t n_seqs,
+                                 int32_t dtype, const void* r, const void* w,
+                                 const void* k, const void* v, const void* a,
+                                 const void* b, float* o, void* stream) {
+  g_last_error.clear();
+  if (wkv7_status st = check_pool(p)) return st;
+  Batch bt;
+  if (wkv7_status st = build_batch(p, slot_ids, cu_seqlens, n_seqs,
+                                   "forward_noalloc", &bt))
+    return st;
+  if (wkv7_status st = check_forward_args(dtype, bt.T_tot, r, w, k, v, a, b, o))
+    return st;
+  if (bt.items.empty()) return WKV7_OK;
+  if (!p->static_scratch)
+    return fail(WKV7_ERR_HIP, "the device's static scratch is not set up");
+  // segment buffers at the start of the scratch, the work description after
+  // them (256-byte aligned)
+  char* base = static_cast<char*>(p->static_scratch);
+  const size_t seg_bytes = seg_scratch_floats(p, bt) * 4;
+  const size_t meta_off = (seg_bytes + 255) & ~size_t(255);
+  wkv7::Launch L;
+  const std::vector<int32_t> words =
+      serialize(p, bt, reinterpret_cast<float*>(base), &L);
+  const size_t meta_bytes = words.size() * 4;
+  if (meta_bytes > wkv7::kStaticMetaBytes ||
+      meta_off + meta_bytes > wkv7::kStaticScratchBytes)
+    return fail(WKV7_ERR_INVALID_ARG,
+                "forward_noalloc: the batch needs %zu bytes of work description "
+                "and %zu of segment buffers; the static scratch holds %zu "
+                "bytes, at most %zu of them work description",
+                meta_bytes, seg_bytes, wkv7::kStaticScratchBytes,
+                wkv7::kStaticMetaBytes);
+
+  DeviceGuard guard(p->device);
+  if (!guard.ok) return fail(WKV7_ERR_HIP, "cannot select the pool's device");
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  // Stage through the next ring entry (preallocated, never grown here): wait
+  // until the copy that last read its host buffer has finished.
+  Stage& sg = p->ring[p->ring_pos];
+  p->ring_pos = (p->ring_pos + 1) % kRing;
+  hipError_t e;
+  if (sg.pending) {
+    e = hipEventSynchronize(sg.ev);
+    if (e != hipSuccess) return fail_hip(e, "hipEventSynchronize(staging)");
+    sg.pending = false;
+  }
+  sg.n_ints = 0;          // its device buffer no longer mirrors the host one
+  std::memcpy(sg.host, words.data(), meta_bytes);
+  e = hipMemcpyAsync(base + meta_off, sg.host, meta_bytes,
+                     hipMemcpyHostToDevice, hs);
+  if (e != hipSuccess) return fail_hip(e, "hipMemcpyAsync(metadata)");
+  sg.stream = hs;
+  e = hipEventRecord(sg.ev, hs);
+  if (e != hipSuccess) return fail_hip(e, "hipEventRecord(staging)");
+  sg.pending = true;
+  relocate(&L, base + meta_off);
+  return launch_batch(p, L, dtype, r, w, k, v, a, b, o, hs);
 }
 
 wkv7_status wkv7_plan_create(wkv7_pool* p, const int32_t* slot_ids,

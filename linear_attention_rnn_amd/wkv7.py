@@ -42,7 +42,7 @@ EXPORTS = (
     "wkv7_last_error", "wkv7_version", "wkv7_pool_create", "wkv7_pool_destroy",
     "wkv7_slot_bytes", "wkv7_pool_state_ptr", "wkv7_pool_shape",
     "wkv7_pool_set_option", "wkv7_slot_alloc", "wkv7_slot_free",
-    "wkv7_forward", "wkv7_snapshot", "wkv7_fork", "wkv7_reset",
+    "wkv7_forward", "wkv7_forward_noalloc", "wkv7_snapshot", "wkv7_fork", "wkv7_reset",
     "wkv7_hibernate", "wkv7_resume", "wkv7_plan_create", "wkv7_plan_tokens",
     "wkv7_forward_plan", "wkv7_plan_destroy", "wkv7_migrate",
     "wkv7_image_header_init", "wkv7_image_header_check",
@@ -136,6 +136,9 @@ lib.wkv7_slot_free.argtypes = [_vp, _pi32, _i32]
 lib.wkv7_forward.restype = _i32
 lib.wkv7_forward.argtypes = [_vp, _pi32, _pi32, _i32, _i32, _vp, _vp, _vp,
                              _vp, _vp, _vp, _vp, _vp]
+lib.wkv7_forward_noalloc.restype = _i32
+lib.wkv7_forward_noalloc.argtypes = [_vp, _pi32, _pi32, _i32, _i32, _vp, _vp,
+                                     _vp, _vp, _vp, _vp, _vp, _vp]
 lib.wkv7_snapshot.restype = _i32
 lib.wkv7_snapshot.argtypes = [_vp, _i32, _vp, _vp]
 lib.wkv7_fork.restype = _i32
@@ -287,6 +290,20 @@ def wkv7_forward(pool: int, slot_ids, cu_seqlens, r, w, k, v, a, b, o,
     _check(lib.wkv7_forward(pool, _iptr(ids), _iptr(cu), ids.size, code,
                             _dptr(r), _dptr(w), _dptr(k), _dptr(v), _dptr(a),
                             _dptr(b), _dptr(o), _stream(stream)))
+
+
+def wkv7_forward_noalloc(pool: int, slot_ids, cu_seqlens, r, w, k, v, a, b,
+                         o, stream=None, dtype: Optional[int] = None) -> None:
+    """wkv7_forward with the kernels' scratch in the library's static array."""
+    ids = _ids(slot_ids)
+    cu = _ids(cu_seqlens)
+    if cu.size != ids.size + 1:
+        raise ValueError("cu_seqlens must have len(slot_ids) + 1 entries")
+    code = _dtype_code(r) if dtype is None else dtype
+    _check(lib.wkv7_forward_noalloc(pool, _iptr(ids), _iptr(cu), ids.size,
+                                    code, _dptr(r), _dptr(w), _dptr(k),
+                                    _dptr(v), _dptr(a), _dptr(b), _dptr(o),
+                                    _stream(stream)))
 
 
 def wkv7_plan_create(pool: int, slot_ids, cu_seqlens) -> int:
