@@ -20,21 +20,27 @@ O = Rbar S0^T + M_rb U + M_rk V and S_L = S0 diag(Lambda_L) + U^T Bbar + V^T Kba
 with the L x L matrices built from operands scaled about a mid-chunk
 reference rho (A_* strictly lower, M_* lower including the diagonal).
 
-This module is test infrastructure: it pins the oracle and checks the
-precision plans of the device kernels; it is not used by either at run time.
+This module is test infrastructure: it pins the oracle (in float64) and,
+with reduced-precision products plugged in, models the operand precision of
+the device kernels' plans on the CPU; it is not used by either at run time.
 """
 from __future__ import annotations
 
 import numpy as np
 
 
-def chunk_step64(S0, r, w, k, v, a, b, rnd=None):
+def chunk_step64(S0, r, w, k, v, a, b, rnd=None, mm=None):
     """One chunk (n rows) from S0 [N, N]; returns (O [n, N], S_L [N, N]).
 
     `rnd`, if given, is applied to every GEMM operand (to model reduced
     operand precision); products are always accumulated in float64.
+    `mm(P, Q)`, if given, replaces every product P @ Q (to model split
+    operands, which are not a rounding of one operand).
     """
     q = (lambda x: x) if rnd is None else rnd
+    if mm is None:
+        def mm(P, Q):
+            return q(P) @ q(Q)
     n = r.shape[0]
     c = np.cumsum(np.log(w), axis=0)                  # c_t, t = 1..n
     cprev = np.vstack([np.zeros((1, w.shape[1])), c[:-1]])
@@ -44,19 +50,19 @@ def chunk_step64(S0, r, w, k, v, a, b, rnd=None):
     cL = c[-1]
     Ab, Rb = a * np.exp(cprev), r * np.exp(c)
     Bb, Kb = b * np.exp(cL - c), k * np.exp(cL - c)
-    A_ab = np.tril(q(Ah) @ q(Bh).T, -1)
-    A_ak = np.tril(q(Ah) @ q(Kh).T, -1)
-    M_rb = np.tril(q(Rh) @ q(Bh).T, 0)
-    M_rk = np.tril(q(Rh) @ q(Kh).T, 0)
+    A_ab = np.tril(mm(Ah, Bh.T), -1)
+    A_ak = np.tril(mm(Ah, Kh.T), -1)
+    M_rb = np.tril(mm(Rh, Bh.T), 0)
+    M_rk = np.tril(mm(Rh, Kh.T), 0)
     Tinv = np.linalg.inv(np.eye(n) - A_ab)
-    X = q(Ab) @ q(S0).T + q(A_ak) @ q(v)
-    U = q(Tinv) @ q(X)
-    O = q(Rb) @ q(S0).T + q(M_rb) @ q(U) + q(M_rk) @ q(v)
-    S_L = S0 * np.exp(cL)[None, :] + q(U).T @ q(Bb) + q(v).T @ q(Kb)
+    X = mm(Ab, S0.T) + mm(A_ak, v)
+    U = mm(Tinv, X)
+    O = mm(Rb, S0.T) + mm(M_rb, U) + mm(M_rk, v)
+    S_L = S0 * np.exp(cL)[None, :] + mm(U.T, Bb) + mm(v.T, Kb)
     return O, S_L
 
 
-def chunked_sequence64(S0, r, w, k, v, a, b, L=64, rnd=None):
+def chunked_sequence64(S0, r, w, k, v, a, b, L=64, rnd=None, mm=None):
     """Whole sequence in chunks of L (the last one may be shorter)."""
     S = np.array(S0, dtype=np.float64, copy=True)
     T = r.shape[0]
@@ -64,7 +70,7 @@ def chunked_sequence64(S0, r, w, k, v, a, b, L=64, rnd=None):
     for lo in range(0, T, L):
         hi = min(lo + L, T)
         O, S = chunk_step64(S, r[lo:hi], w[lo:hi], k[lo:hi], v[lo:hi],
-                            a[lo:hi], b[lo:hi], rnd=rnd)
+                            a[lo:hi], b[lo:hi], rnd=rnd, mm=mm)
         outs.append(O)
     o = np.concatenate(outs) if outs else np.zeros_like(r)
     return o, S

@@ -1,0 +1,88 @@
+"""Operand-precision plans of the chunked kernels, modelled on the CPU and
+compared with the float64 oracle at the workloads' sequence lengths.
+
+The bars: max|err|/rms 1e-3 for fp32 inputs and 2e-2 for bf16 inputs; the
+GPU tests guard the default bf16 kernel at 1e-2. These tests pin, without a
+GPU, how much of its bar each plan spends and that the spend does not grow
+with the sequence length up to the longest workload prompt (8192 tokens);
+and that a plan with single bf16 operands would not meet the bar, which is
+why the kernels split or use fp16.
+"""
+import numpy as np
+import pytest
+
+import wkv7_inputs as G
+from oracle import rel_max_err
+from oracle import wkv7_cref as C
+from tests import precision_plans as PP
+
+N = 64
+
+
+def _heads(T, n_heads, seed):
+    """bf16-rounded inputs of the workload recipe, zero start state."""
+    rng = np.random.default_rng(seed)
+    b = G.make_batch(rng, [0], [T], n_heads, N, G.BF16)
+    x = b.inputs64()
+    for h in range(n_heads):
+        xh = {n: x[n][:, h] for n in G.NAMES}
+        o_ref, S_ref = C.sequence(np.zeros((N, N)), **xh)
+        yield xh, o_ref, S_ref
+
+
+def _worst(plan, T, n_heads, seed):
+    eo = es = 0.0
+    for xh, o_ref, S_ref in _heads(T, n_heads, seed):
+        o, S = plan(np.zeros((N, N)), **xh)
+        eo = max(eo, rel_max_err(o, o_ref))
+        es = max(es, rel_max_err(S, S_ref))
+    return eo, es
+
+
+@pytest.mark.parametrize("T", [64, 4096])
+def test_fp32_chunk_form_headroom(T):
+    """The chunked form itself costs nothing measurable in fp32."""
+    eo, es = _worst(PP.fp32_sequence, T, 2, seed=200 + T)
+    print(f"fp32 chunk form, T={T}: o {eo:.2e}  S {es:.2e}")
+    assert eo < 1e-5 and es < 1e-5
+
+
+def test_split_bf16_plan():
+    """The precise kernel (every product from split bf16 operands, chunks of
+    64) spends about a twentieth of the fp32-input bar."""
+    eo, es = _worst(PP.split_sequence, 4096, 2, seed=301)
+    print(f"split-bf16 plan, T=4096: o {eo:.2e}  S {es:.2e}")
+    assert eo < 2e-4 and es < 5e-5
+    assert eo > 1e-6          # the model really rounds
+
+
+def test_default_bf16_plan_and_its_growth_with_length():
+    """The default bf16 kernel's plan at the prefill lengths: within 60% of
+    the GPU tests' 1e-2 guard (30% of the 2e-2 bar), and the error does not
+    grow materially from 4096 to 8192 tokens."""
+    res = {T: _worst(PP.fast_sequence, T, 4, seed=400 + T)
+           for T in (64, 4096, 8192)}
+    for T, (eo, es) in res.items():
+        print(f"default bf16 plan, T={T}: o {eo:.2e}  S {es:.2e}")
+    for eo, es in res.values():
+        assert eo < 6e-3 and es < 6e-3
+        assert eo > 1e-4          # fp16 rounding is modelled
+    assert res[8192][0] < 1.5 * res[4096][0]
+    assert res[8192][1] < 1.5 * res[4096][1]
+
+
+def test_single_bf16_operands_would_miss_the_bar():
+    eo, _ = _worst(PP.bf16_sequence, 4096, 2, seed=501)
+    print(f"single-bf16 plan, T=4096: o {eo:.2e}")
+    assert eo > 1e-2
+
+
+def test_plan_models_reduce_to_exact_products_in_float64():
+    """With exact products plugged in, the chunked form equals the oracle to
+    float64 rounding: the models differ from it only where they round."""
+    from tests.chunk_form64 import chunked_sequence64
+    for xh, o_ref, S_ref in _heads(100, 1, seed=600):
+        o, S = chunked_sequence64(np.zeros((N, N)), **xh, L=32,
+                                  mm=lambda P, Q: P @ Q)
+        assert rel_max_err(o, o_ref) < 1e-11
+        assert rel_max_err(S, S_ref) < 1e-11
