@@ -39,9 +39,25 @@
  *
  * Threading and ordering: a pool belongs to one host thread; calls on one
  * pool are not thread-safe. Device work is enqueued on the caller's stream
- * (a hipStream_t passed as void*, NULL = the null stream) and the library
- * never waits for it, except in wkv7_pool_destroy. Calls on one pool that
- * use different streams must be ordered by the caller.
+ * (a hipStream_t passed as void*, NULL = the null stream). Calls on one pool
+ * that use different streams must be ordered by the caller.
+ *
+ * Host waits. The library waits for device work only here:
+ *   - wkv7_pool_create zero-fills the pool and waits for the device;
+ *     wkv7_plan_create copies the plan with a synchronous copy;
+ *   - wkv7_pool_destroy and wkv7_plan_destroy wait for all work on the
+ *     device before freeing (releasing device or pinned memory waits for
+ *     the whole device on this runtime in any case), as does
+ *     wkv7_sessions_destroy;
+ *   - a call that stages host metadata (wkv7_forward, wkv7_forward_noalloc,
+ *     wkv7_fork, wkv7_migrate, wkv7_reset, and wkv7_hibernate/wkv7_resume
+ *     of scattered slots) uses the pool's eight pinned staging buffers in
+ *     turn; when the buffer's previous copy (eight staged calls earlier)
+ *     has not yet run, the call waits on the host for that copy alone.
+ * Nothing else waits: wkv7_forward_plan, wkv7_snapshot, and hibernate or
+ * resume of runs of slots only enqueue. A buffer a call outgrows (staging,
+ * segment buffers) is not freed but kept until wkv7_pool_destroy, and its
+ * replacement is allocated with hipMalloc, which does not wait.
  */
 #ifndef WKV7_H
 #define WKV7_H
@@ -118,8 +134,12 @@ int32_t wkv7_version(void);
 wkv7_status wkv7_pool_create(int32_t n_slots, int32_t H, int32_t N,
                              wkv7_pool** out);
 
-/* Wait for the pool's enqueued work on every stream it has seen, then free
- * everything it owns. A NULL pool is a no-op. */
+/* destroy — wait for all work on the pool's device (so the pool's work on
+ * every stream has finished), then free everything the pool owns (page
+ * "RWKV-X Architecture", section "Adapter API": the state's free call; page
+ * "Virtual Memory for KV Cache and Model Weights": memory is released only
+ * after the transfers that use it have finished). Plans made for the pool
+ * must be destroyed first. A NULL pool is a no-op. */
 wkv7_status wkv7_pool_destroy(wkv7_pool* pool);
 
 /* Bytes in one slot image: H*N*N*4 (0 for NULL). */
@@ -137,12 +157,18 @@ wkv7_status wkv7_pool_shape(const wkv7_pool* pool, int32_t* n_slots,
 wkv7_status wkv7_pool_set_option(wkv7_pool* pool, int32_t opt, int64_t val);
 
 /* admission — take n free slot ids from the host free list into ids_out
- * (host array of n). WKV7_ERR_POOL_FULL if fewer than n are free; then
- * nothing is taken. Allocation does not clear the slots (see wkv7_reset). */
+ * (host array of n) (page "Virtual Memory for KV Cache and Model Weights":
+ * admitting a request needs a free recurrent-state slot besides its KV
+ * blocks; page "wkvm: state-slot inference for RWKV, GDN and Mamba
+ * hybrids", section "The allocation unit wkvm changes": the fixed-size slot
+ * is the unit a request is given). WKV7_ERR_POOL_FULL if fewer than n are
+ * free; then nothing is taken. Allocation does not clear the slots (see
+ * wkv7_reset). Host only; no device work. */
 wkv7_status wkv7_slot_alloc(wkv7_pool* pool, int32_t n, int32_t* ids_out);
 
-/* Return n allocated ids (host array) to the free list. Every id must be
- * allocated and appear once, else nothing is freed. */
+/* Return n allocated ids (host array) to the free list (the same passages:
+ * a finished request gives its slot back). Every id must be allocated and
+ * appear once, else nothing is freed. Host only; no device work. */
 wkv7_status wkv7_slot_free(wkv7_pool* pool, const int32_t* ids, int32_t n);
 
 /* forward — run the recurrence for a packed batch of sequences.
@@ -160,7 +186,10 @@ wkv7_status wkv7_slot_free(wkv7_pool* pool, const int32_t* ids, int32_t n);
  * or misaligned pointers with T_tot > 0, bad cu_seqlens, n_seqs < 0),
  * WKV7_ERR_UNSUPPORTED (dtype). The host arrays may be reused as soon as
  * the call returns (they are staged); the device arrays must stay alive
- * until the stream has passed the call. */
+ * until the stream has passed the call. With WKV7_OPT_SEGMENT_LEN on, a
+ * batch that needs more segment buffers than any before on this pool gets
+ * new, larger ones (hipMalloc; WKV7_ERR_OOM if that fails); the old ones
+ * are kept until the pool is destroyed. */
 wkv7_status wkv7_forward(wkv7_pool* pool, const int32_t* slot_ids,
                          const int32_t* cu_seqlens, int32_t n_seqs,
                          int32_t dtype, const void* r, const void* w,
@@ -234,7 +263,8 @@ wkv7_status wkv7_forward_plan(wkv7_pool* pool, const wkv7_plan* plan,
                               const void* k, const void* v, const void* a,
                               const void* b, float* o, void* stream);
 
-/* Wait for the plan's device to finish the work enqueued so far, then free
+/* Wait for all work on the plan's device (a plan's launches record no
+ * event, so this is how work that used it is known to be done), then free
  * the plan. A NULL plan is a no-op. */
 wkv7_status wkv7_plan_destroy(wkv7_plan* plan);
 
@@ -244,9 +274,12 @@ wkv7_status wkv7_plan_destroy(wkv7_plan* plan);
 wkv7_status wkv7_snapshot(wkv7_pool* pool, int32_t slot, void* dst_device,
                           void* stream);
 
-/* fork — pool[dst[i]] <- pool[src[i]] for i < n (host arrays), bit-exact.
- * dst ids must be distinct and disjoint from src ids
- * (WKV7_ERR_DUPLICATE_SLOT otherwise); src ids may repeat. */
+/* fork — pool[dst[i]] <- pool[src[i]] for i < n (host arrays), bit-exact
+ * (page "wkvm: state-slot inference for RWKV, GDN and Mamba hybrids",
+ * section "The allocation unit wkvm changes": fork is one of the slot
+ * verbs; continuing a fork equals continuing its parent). dst ids must be
+ * distinct and disjoint from src ids (WKV7_ERR_DUPLICATE_SLOT otherwise);
+ * src ids may repeat. */
 wkv7_status wkv7_fork(wkv7_pool* pool, const int32_t* src, const int32_t* dst,
                       int32_t n, void* stream);
 
@@ -274,7 +307,10 @@ wkv7_status wkv7_hibernate(wkv7_pool* pool, const int32_t* ids, int32_t n,
 
 /* resume — copy n consecutive slot images from src (pinned host memory or
  * device memory, e.g. a snapshot) into slots ids[0..n) (distinct),
- * bit-exact. bytes >= n*slot_bytes, else WKV7_ERR_INVALID_ARG. src must
+ * bit-exact (page "wkvm: state-slot inference for RWKV, GDN and Mamba
+ * hybrids", section "The allocation unit wkvm changes": resume is the verb
+ * that brings a hibernated slot back; page "Virtual Memory for KV Cache and
+ * Model Weights": offloaded state is loaded back from host memory). bytes >= n*slot_bytes, else WKV7_ERR_INVALID_ARG. src must
  * stay alive until the stream has passed the call. Scattered ids (at
  * least four runs) take the staging path described under hibernate; a
  * 16-byte-aligned src in device memory of the pool's device is instead

@@ -22,8 +22,11 @@
  *
  * Device work (reset, fork, hibernate, resume) is enqueued on the stream
  * given to wkv7_session_begin; the caller runs wkv7_forward on the returned
- * slot on the same stream. A manager and its pool belong to one host
- * thread.
+ * slot on the same stream. Every turn of a manager must use one stream, the
+ * stream of its first turn (wkv7_session_begin fails with
+ * WKV7_ERR_INVALID_ARG on any other): the manager moves, forks and resets
+ * slots whose last forward it knows to be finished only through that
+ * stream's order. A manager and its pool belong to one host thread.
  */
 #ifndef WKV7_SESSION_H
 #define WKV7_SESSION_H

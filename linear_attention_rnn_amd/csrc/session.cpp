@@ -68,6 +68,12 @@ constexpr size_t kEvictedMemory = 1 << 16;   // remembered dropped keys
 struct wkv7_sessions {
   wkv7_pool* pool = nullptr;
   bool dry = false;
+  // The stream of the first turn: every turn must use it, because the
+  // manager's own device work (hibernate, fork, reset of a recycled slot)
+  // touches slots whose last forward it can only know to be done in that
+  // stream's order.
+  bool stream_set = false;
+  void* stream = nullptr;
   int flags = 0;
   std::vector<int32_t> dry_free;
   // host parking
@@ -334,6 +340,12 @@ wkv7_status wkv7_session_begin(wkv7_sessions* s, const wkv7_turn_key* key,
     return host_fail(WKV7_ERR_INVALID_ARG, "session_begin: NULL argument");
   if (n_tokens < 0 || (n_tokens > 0 && !tokens))
     return host_fail(WKV7_ERR_INVALID_ARG, "session_begin: bad tokens");
+  if (s->stream_set && stream != s->stream)
+    return host_fail(WKV7_ERR_INVALID_ARG,
+                     "session_begin: every turn of a manager must use the "
+                     "stream of its first turn");
+  s->stream_set = true;
+  s->stream = stream;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   const Key chat{key->model, key->user, key->chat, 0};
   const Key want{key->model, key->user, key->chat, key->parent};

@@ -16,6 +16,7 @@
 #include <new>
 #include <string>
 #include <type_traits>
+#include <utility>
 #include <vector>
 
 using wkv7::WorkItem;
@@ -88,6 +89,10 @@ struct wkv7_pool {
   float* xfer_stage = nullptr;       // staging of scattered hibernate/resume
   size_t xfer_stage_bytes = 0;
   void* static_scratch = nullptr;    // the device's static scratch array
+  // Buffers a call has outgrown, freed at destroy: releasing memory waits
+  // for the whole device on this runtime, so no other call frees anything.
+  // (pointer, true for pinned host memory)
+  std::vector<std::pair<void*, bool>> retired;
   int n_cus = 0;                     // compute units of the pool's device
   std::vector<int32_t> free_ids;     // stack; top = back
   std::vector<uint8_t> allocated;
@@ -140,8 +145,8 @@ wkv7_status stage_upload(wkv7_pool* p, const int32_t* data, size_t n,
   }
   if (s.cap_ints < n) {
     size_t cap = std::max<size_t>(n, kStageMinInts);
-    if (s.host) (void)hipHostFree(s.host);
-    if (s.dev) (void)hipFree(s.dev);
+    if (s.host) p->retired.emplace_back(s.host, true);
+    if (s.dev) p->retired.emplace_back(s.dev, false);
     s.host = nullptr;
     s.dev = nullptr;
     s.cap_ints = 0;
@@ -149,7 +154,7 @@ wkv7_status stage_upload(wkv7_pool* p, const int32_t* data, size_t n,
       return fail(WKV7_ERR_OOM, "pinned staging allocation of %zu bytes failed",
                   cap * 4);
     if (hipMalloc(reinterpret_cast<void**>(&s.dev), cap * 4) != hipSuccess) {
-      (void)hipHostFree(s.host);
+      p->retired.emplace_back(s.host, true);
       s.host = nullptr;
       return fail(WKV7_ERR_OOM, "device staging allocation of %zu bytes failed",
                   cap * 4);
@@ -454,11 +459,12 @@ wkv7_status launch_batch(const wkv7_pool* p, const wkv7::Launch& L,
   return WKV7_OK;
 }
 
-// Makes the pool's segment buffers hold at least `floats` (grow only; the
-// free waits for the device, so earlier work still using them finishes).
+// Makes the pool's segment buffers hold at least `floats` (grow only; an
+// outgrown buffer is kept until destroy, since queued work may still use it
+// and freeing would wait for the device).
 wkv7_status ensure_seg_scratch(wkv7_pool* p, size_t floats) {
   if (floats <= p->seg_scratch_floats) return WKV7_OK;
-  if (p->seg_scratch) (void)hipFree(p->seg_scratch);
+  if (p->seg_scratch) p->retired.emplace_back(p->seg_scratch, false);
   p->seg_scratch = nullptr;
   p->seg_scratch_floats = 0;
   if (hipMalloc(reinterpret_cast<void**>(&p->seg_scratch), floats * 4) != hipSuccess)
@@ -575,6 +581,8 @@ wkv7_status wkv7_pool_destroy(wkv7_pool* p) {
   if (p->state) (void)hipFree(p->state);
   if (p->seg_scratch) (void)hipFree(p->seg_scratch);
   if (p->xfer_stage) (void)hipFree(p->xfer_stage);
+  for (const auto& r : p->retired)
+    (void)(r.second ? hipHostFree(r.first) : hipFree(r.first));
   delete p;
   if (e != hipSuccess) return fail_hip(e, "hipDeviceSynchronize(destroy)");
   return WKV7_OK;
@@ -1097,10 +1105,11 @@ int32_t count_runs(const int32_t* ids, int32_t n) {
   return runs;
 }
 
-// Grow-only, like the segment buffers (the free waits for the device).
+// Grow-only, like the segment buffers (an outgrown buffer is kept until
+// destroy).
 wkv7_status ensure_xfer_stage(wkv7_pool* p, size_t bytes) {
   if (bytes <= p->xfer_stage_bytes) return WKV7_OK;
-  if (p->xfer_stage) (void)hipFree(p->xfer_stage);
+  if (p->xfer_stage) p->retired.emplace_back(p->xfer_stage, false);
   p->xfer_stage = nullptr;
   p->xfer_stage_bytes = 0;
   if (hipMalloc(reinterpret_cast<void**>(&p->xfer_stage), bytes) != hipSuccess)

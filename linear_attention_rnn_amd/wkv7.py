@@ -231,6 +231,55 @@ def _dtype_code(t) -> int:
     return -1  # the library reports WKV7_ERR_UNSUPPORTED
 
 
+def _check_io(T_tot: Optional[int], H: Optional[int], dtype: Optional[int],
+              ins, o) -> None:
+    """Argument checks the library cannot make on raw pointers, raised as
+    ValueError before any call: r..b must be contiguous tensors of one dtype,
+    o a contiguous float32 tensor, all on one GPU, each with at least
+    T_tot * H * 64 elements (the rows the call reads or writes), and a
+    dtype code given explicitly must match the inputs' element width. An
+    unsupported dtype, a misaligned pointer or a NULL tensor is left to the
+    library, which rejects it with its own status. T_tot/H None: not yet
+    known (the element counts are then checked by the caller's second call).
+    """
+    import torch
+    named = list(zip(("r", "w", "k", "v", "a", "b"), ins)) + [("o", o)]
+    present = [(n, t) for n, t in named if t is not None]
+    for n, t in present:
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"{n} must be a torch.Tensor, not {type(t)!r}")
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+    ins_present = [(n, t) for n, t in present if n != "o"]
+    if ins_present:
+        d0 = ins_present[0][1].dtype
+        supported = (torch.float32, torch.bfloat16)
+        if d0 in supported:
+            for n, t in ins_present:
+                if t.dtype != d0:
+                    raise ValueError(f"r..b must share one dtype: {n} is "
+                                     f"{t.dtype}, r is {d0}")
+            code = WKV7_F32 if d0 == torch.float32 else WKV7_BF16
+            if dtype is not None and dtype in (WKV7_F32, WKV7_BF16) and \
+                    dtype != code:
+                raise ValueError(f"dtype code {dtype} does not match the "
+                                 f"inputs' {d0}")
+    if o is not None and o.dtype != torch.float32:
+        raise ValueError(f"o must be float32, not {o.dtype}")
+    if T_tot is not None and H is not None:
+        need = T_tot * H * 64
+        for n, t in present:
+            if t.numel() < need:
+                raise ValueError(f"{n} has {t.numel()} elements; the call "
+                                 f"needs [{T_tot}, {H}, 64] = {need}")
+    devs = {(t.device.type, t.device.index) for _, t in present}
+    for n, t in present:
+        if t.device.type != "cuda":
+            raise ValueError(f"{n} is on {t.device}, not on a GPU")
+    if len(devs) > 1:
+        raise ValueError("r..b and o must be on one GPU")
+
+
 def wkv7_version() -> int:
     return int(lib.wkv7_version())
 
@@ -286,6 +335,9 @@ def wkv7_forward(pool: int, slot_ids, cu_seqlens, r, w, k, v, a, b, o,
     cu = _ids(cu_seqlens)
     if cu.size != ids.size + 1:
         raise ValueError("cu_seqlens must have len(slot_ids) + 1 entries")
+    _check_io(None, None, dtype, (r, w, k, v, a, b), o)
+    _check_io(int(cu[-1]), wkv7_pool_shape(pool)[1], dtype,
+              (r, w, k, v, a, b), o)
     code = _dtype_code(r) if dtype is None else dtype
     _check(lib.wkv7_forward(pool, _iptr(ids), _iptr(cu), ids.size, code,
                             _dptr(r), _dptr(w), _dptr(k), _dptr(v), _dptr(a),
@@ -299,6 +351,9 @@ def wkv7_forward_noalloc(pool: int, slot_ids, cu_seqlens, r, w, k, v, a, b,
     cu = _ids(cu_seqlens)
     if cu.size != ids.size + 1:
         raise ValueError("cu_seqlens must have len(slot_ids) + 1 entries")
+    _check_io(None, None, dtype, (r, w, k, v, a, b), o)
+    _check_io(int(cu[-1]), wkv7_pool_shape(pool)[1], dtype,
+              (r, w, k, v, a, b), o)
     code = _dtype_code(r) if dtype is None else dtype
     _check(lib.wkv7_forward_noalloc(pool, _iptr(ids), _iptr(cu), ids.size,
                                     code, _dptr(r), _dptr(w), _dptr(k),
@@ -325,6 +380,10 @@ def wkv7_plan_tokens(plan: int) -> int:
 def wkv7_forward_plan(pool: int, plan: int, r, w, k, v, a, b, o, stream=None,
                       dtype: Optional[int] = None) -> None:
     """wkv7_forward over a plan's batch: kernel launches only (capturable)."""
+    _check_io(None, None, dtype, (r, w, k, v, a, b), o)
+    if plan:
+        _check_io(wkv7_plan_tokens(plan), wkv7_pool_shape(pool)[1], dtype,
+                  (r, w, k, v, a, b), o)
     code = _dtype_code(r) if dtype is None else dtype
     _check(lib.wkv7_forward_plan(pool, plan, code, _dptr(r), _dptr(w),
                                  _dptr(k), _dptr(v), _dptr(a), _dptr(b),

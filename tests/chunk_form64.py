@@ -29,18 +29,15 @@ from __future__ import annotations
 import numpy as np
 
 
-def chunk_step64(S0, r, w, k, v, a, b, rnd=None, mm=None):
+def chunk_step64(S0, r, w, k, v, a, b, mm=None):
     """One chunk (n rows) from S0 [N, N]; returns (O [n, N], S_L [N, N]).
 
-    `rnd`, if given, is applied to every GEMM operand (to model reduced
-    operand precision); products are always accumulated in float64.
-    `mm(P, Q)`, if given, replaces every product P @ Q (to model split
-    operands, which are not a rounding of one operand).
+    `mm(P, Q)`, if given, replaces every product P @ Q (to model a kernel's
+    operand precision: rounded or split operands, rounded results).
     """
-    q = (lambda x: x) if rnd is None else rnd
     if mm is None:
         def mm(P, Q):
-            return q(P) @ q(Q)
+            return P @ Q
     n = r.shape[0]
     c = np.cumsum(np.log(w), axis=0)                  # c_t, t = 1..n
     cprev = np.vstack([np.zeros((1, w.shape[1])), c[:-1]])
@@ -62,7 +59,7 @@ def chunk_step64(S0, r, w, k, v, a, b, rnd=None, mm=None):
     return O, S_L
 
 
-def chunked_sequence64(S0, r, w, k, v, a, b, L=64, rnd=None, mm=None):
+def chunked_sequence64(S0, r, w, k, v, a, b, L=64, mm=None):
     """Whole sequence in chunks of L (the last one may be shorter)."""
     S = np.array(S0, dtype=np.float64, copy=True)
     T = r.shape[0]
@@ -70,7 +67,7 @@ def chunked_sequence64(S0, r, w, k, v, a, b, L=64, rnd=None, mm=None):
     for lo in range(0, T, L):
         hi = min(lo + L, T)
         O, S = chunk_step64(S, r[lo:hi], w[lo:hi], k[lo:hi], v[lo:hi],
-                            a[lo:hi], b[lo:hi], rnd=rnd, mm=mm)
+                            a[lo:hi], b[lo:hi], mm=mm)
         outs.append(O)
     o = np.concatenate(outs) if outs else np.zeros_like(r)
     return o, S

@@ -187,3 +187,23 @@ def test_session_errors(mk):
             W.wkv7_sessions_create(None, *args)
         assert e.value.status == W.WKV7_ERR_INVALID_ARG, args
     assert W.lib.wkv7_sessions_destroy(None) == W.WKV7_OK
+
+
+def test_every_turn_uses_the_first_turns_stream(mk):
+    """The manager's own device work is ordered after a slot's last forward
+    only through one stream, so a turn on another stream is refused (a
+    host-only manager never touches the handles)."""
+    s = mk()
+    slot, _, _ = W.wkv7_session_begin(s, MODEL, USER, 1, 0, [1, 2],
+                                      stream=0x1000)
+    W.wkv7_session_end(s, slot, 100, [1, 2, 3])
+    before = W.wkv7_sessions_stats(s)
+    with pytest.raises(W.Wkv7Error) as ei:
+        W.wkv7_session_begin(s, MODEL, USER, 1, 100, [1, 2, 3, 4],
+                             stream=0x2000)
+    assert ei.value.status == W.WKV7_ERR_INVALID_ARG
+    assert "stream" in ei.value.message
+    assert W.wkv7_sessions_stats(s) == before     # nothing moved or counted
+    slot2, reuse, oc = W.wkv7_session_begin(s, MODEL, USER, 1, 100,
+                                            [1, 2, 3, 4], stream=0x1000)
+    assert (slot2, reuse, oc) == (slot, 3, HIT)
