@@ -927,6 +927,10 @@ def _oracle_decode_slice(lo: int, hi: int, seed: int, seconds: float,
         wl = G.cfg_decode(seed=seed)
         S = G.as_f64(wl.init_states[lo:hi])
         ids = wl.batch.slot_ids
+        # one untimed step first (the state's pages are touched there)
+        b = G.decode_step_inputs(seed, 10**6, ids, wl.H, wl.N)
+        _, S = wkv7_decode_batch(S, {k: v[lo:hi]
+                                     for k, v in b.inputs64().items()})
         if barrier is not None:
             barrier.wait()
         n_steps, t_used = 0, 0.0
@@ -943,56 +947,200 @@ def _oracle_decode_slice(lo: int, hi: int, seed: int, seconds: float,
     return res
 
 
-def cpu_baseline(seconds: float, seed: int = 1, max_workers: int = 16):
-    """The float64 oracle on a bounded sample of the headline workload:
-    whole decode steps of the 256-slot, H=32 batch. First on one core; then
-    the batch's slots are split over worker processes (one per core of this
-    process's CPU set, at most `max_workers`), all running at once, and the
-    rate is the sum of the workers' rates."""
+HOST_SHARE = 16   # CPU threads one GPU's jobs may use on the GPU host
+
+
+def _host_cores() -> int:
+    """Cores of this process's CPU set, at most HOST_SHARE."""
+    return max(1, min(HOST_SHARE, len(os.sched_getaffinity(0))))
+
+
+def _numpy_oracle_decode(seconds: float, seed: int, cores: int) -> dict:
+    """The numpy float64 oracle on whole decode steps of the 256-slot, H=32
+    batch: one core, then the slots split over `cores` worker processes
+    running at once (the rate is the sum of the workers' rates)."""
     import multiprocessing as mp
 
     tok1, t1 = _oracle_decode_slice(0, 256, seed, seconds)
-    single = tok1 / t1
-    _progress(f"cpu baseline: one core {single:.0f} tokens/s")
-    cores = max(1, min(max_workers, len(os.sched_getaffinity(0))))
-    value, used, sample_par = single, 1, ""
+    out = {"single_core_value": tok1 / t1, "value": tok1 / t1, "cores": 1,
+           "steps_single_core": tok1 // 256, "seconds_single_core": t1}
     if cores > 1:
         ctx = mp.get_context("spawn")
         barrier, queue = ctx.Barrier(cores), ctx.Queue()
         bounds = np.linspace(0, 256, cores + 1).astype(int)
         procs = [ctx.Process(target=_oracle_decode_slice,
                              args=(int(bounds[i]), int(bounds[i + 1]), seed,
-                                   seconds * 0.5, barrier, queue))
+                                   seconds, barrier, queue))
                  for i in range(cores)]
         for p in procs:
             p.start()
-        res = [queue.get(timeout=600) for _ in procs]
+        res = []
+        try:
+            for _ in procs:
+                res.append(queue.get(timeout=120))
+        except Exception:            # a worker failed: keep the one-core rate
+            res = []
         for p in procs:
-            p.join(timeout=60)
-        if all(p.exitcode == 0 for p in procs):
-            value, used = sum(t / s for t, s in res), cores
-            sample_par = (f"; all cores: the 256 slots split over {cores} "
-                          f"worker processes running at once, "
-                          f"{seconds * 0.5:.0f} s of compute each")
+            p.join(timeout=30)
+            if p.is_alive():
+                p.terminate()
+                p.join(timeout=10)
+        if len(res) == cores and all(p.exitcode == 0 for p in procs):
+            out["value"] = sum(t / s for t, s in res)
+            out["cores"] = cores
+    return out
+
+
+def _rate(fn, units: float, budget: float):
+    """Run fn() until `budget` seconds have passed (at least once); returns
+    (units per second, calls, seconds)."""
+    n, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        n += 1
+        dt = time.perf_counter() - t0
+        if dt >= budget:
+            return units * n / dt, n, dt
+
+
+def cpu_baseline(seconds: float, seed: int = 1) -> dict:
+    """The CPU oracles, timed on this host in the same run, on bounded
+    samples of every workload.
+
+    Headline: the plain-C float64 oracle (oracle/wkv7_ref.c) on whole decode
+    steps of the 256-slot H=32 batch, independent heads on one thread per
+    core (value), and on one thread (single_core_value). Per workload: the
+    same oracle's tokens per second on a sample of that workload with the
+    workload's own shapes and input recipe. Beside it, the numpy float64
+    oracle on the decode batch, on one core and on one worker process per
+    core. Input generation is not timed."""
+    import torch
+    import wkv7_inputs as G
+    from oracle import wkv7_cref as C
+    from oracle import wkv7_sequence
+
+    cores = _host_cores()
+    budget = max(0.25, seconds / 20.0)
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(seed)
+
+    def draw(T, H):
+        return G.draw_tokens_device(gen, T, H, N, "bf16", "cpu")
+
+    per = {}
+    # small: one sequence of 64 tokens, H=2, fp32 inputs, zero state
+    wl = G.cfg_small(seed=0)
+    x0, x0_64 = wl.batch.inputs, wl.batch.inputs64()
+
+    def small_c():
+        C.run_heads(np.zeros((2, N, N)), x0, 64, 2, N, threads=1)
+
+    def small_np():
+        wkv7_sequence(np.zeros((2, N, N)), **x0_64)
+
+    r_c, n_c, t_c = _rate(small_c, 1, budget)
+    r_n, n_n, t_n = _rate(small_np, 1, budget)
+    per["small_h2_t64_f32in"] = {"us_per_call_1core": 1e6 / r_c,
+                                 "us_per_call_1core_numpy": 1e6 / r_n,
+                                 "tokens_per_s_1core": 64 * r_c}
+    # decode: 256 slots x H=32, one token each, states N(0, 0.1)
+    S1 = np.ascontiguousarray(
+        np.random.default_rng(seed).normal(0, 0.1, (256 * 32, N, N)))
+    xd = draw(256, 32)
+    dec_1, _, _ = _rate(lambda: C.run_heads(S1, xd, 1, 256 * 32, N,
+                                            threads=1), 256, budget)
+    dec_n, n_dec, t_dec = _rate(lambda: C.run_heads(S1, xd, 1, 256 * 32, N,
+                                                    threads=cores),
+                                256, budget)
+    per["decode_b256_h32_bf16in"] = {"tokens_per_s": dec_n,
+                                     "tokens_per_s_1core": dec_1}
+    _progress(f"cpu baseline: decode {dec_1:.0f} tokens/s on one thread, "
+              f"{dec_n:.0f} on {cores}")
+    # prefill: 8 x 4096 tokens, H=32, zero state; a sample of 2 sequences
+    xp = [draw(4096, 32) for _ in range(2)]
+
+    def prefill():
+        for x in xp:
+            C.run_heads(np.zeros((32, N, N)), x, 4096, 32, N, threads=cores)
+
+    r, _, _ = _rate(prefill, 2 * 4096, budget)
+    per["prefill_b8_t4096_h32_bf16in"] = {
+        "tokens_per_s": r, "sample": "2 of the 8 sequences of 4096 tokens"}
+    # mixed stack: one layer (64 decode slots + prefills 512, 1024, 2048,
+    # 2048) at H=12; a 12-layer step is 12 such layers
+    xm_d = draw(64, 12)
+    xm_p = [draw(T, 12) for T in (512, 1024, 2048, 2048)]
+    Sm = np.ascontiguousarray(
+        np.random.default_rng(seed + 1).normal(0, 0.1, (64 * 12, N, N)))
+
+    def mixed_layer():
+        C.run_heads(Sm, xm_d, 1, 64 * 12, N, threads=cores)
+        for x in xm_p:
+            C.run_heads(np.zeros((12, N, N)), x, x["r"].shape[0], 12, N,
+                        threads=cores)
+
+    r, _, _ = _rate(mixed_layer, 5696, budget)
+    per["mixed_12layers_h12_bf16in"] = {"layer_tokens_per_s": r,
+                                        "tokens_per_s": r / 12,
+                                        "sample": "one of the 12 layers"}
+    # large pool decode: 1024 slots x H=64
+    S4 = np.ascontiguousarray(
+        np.random.default_rng(seed + 2).normal(0, 0.1, (1024 * 64, N, N)))
+    x4 = draw(1024, 64)
+    r, _, _ = _rate(lambda: C.run_heads(S4, x4, 1, 1024 * 64, N,
+                                        threads=cores), 1024, budget)
+    per["decode_b1024_h64_bf16in"] = {"tokens_per_s": r}
+    del S4
+    # large pool prefill: 4 of the 32 ragged sequences (lengths from the
+    # same draw as the GPU leg), H=64
+    lens = np.random.default_rng(4).integers(128, 8193, size=32)[:4]
+    x4p = [draw(int(T), 64) for T in lens]
+
+    def ragged():
+        for x in x4p:
+            C.run_heads(np.zeros((64, N, N)), x, x["r"].shape[0], 64, N,
+                        threads=cores)
+
+    r, _, _ = _rate(ragged, float(lens.sum()), budget)
+    per["prefill_32ragged_128to8192_h64_bf16in"] = {
+        "tokens_per_s": r,
+        "sample": f"4 of the 32 sequences ({int(lens.sum())} tokens)"}
+    _progress("cpu baseline: per-workload oracle rates done")
+    npy = _numpy_oracle_decode(budget * 2, seed, cores)
+    _progress(f"cpu baseline: numpy oracle {npy['single_core_value']:.0f} "
+              f"tokens/s on one core")
+    model = _cpu_model()
     return {
-        "value": value, "unit": "tokens/s", "cores": used, "kind": "oracle",
-        "single_core_value": single,
-        "sample": (f"whole decode steps of the 256-slot H=32 batch, numpy "
-                   f"float64, one BLAS thread per process, on "
-                   f"{_cpu_model()}; one core: {tok1 // 256} steps in "
-                   f"{t1:.1f} s{sample_par}"),
+        "value": dec_n, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+        "single_core_value": dec_1,
+        "sample": (f"decode steps of the 256-slot H=32 batch, plain-C "
+                   f"float64 oracle, heads split over {cores} threads; "
+                   f"{n_dec} steps in {t_dec:.1f} s"),
+        "cpu_model": model,
+        "host_cpus_in_affinity": len(os.sched_getaffinity(0)),
+        "per_workload": per,
+        "numpy_oracle": npy,
     }
 
 
 def _cpu_model() -> str:
+    """Model name with family/model/stepping (some hosts report only the
+    vendor line), from /proc/cpuinfo."""
+    info = {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if ":" in line:
+                    k, v = line.split(":", 1)
+                    info.setdefault(k.strip(), v.strip())
+                if not line.strip() and info:
+                    break
     except OSError:
-        pass
-    return "unknown CPU"
+        return "unknown CPU"
+    name = info.get("model name", "unknown CPU")
+    return (f"{name} (family {info.get('cpu family', '?')}, model "
+            f"{info.get('model', '?')}, stepping {info.get('stepping', '?')}"
+            f", {info.get('cpu MHz', '?')} MHz)")
 
 
 def _progress(msg: str) -> None:
@@ -1150,6 +1298,7 @@ def main(argv=None) -> int:
     if not args.no_cpu_baseline:
         _progress("cpu baseline (oracle) running")
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+        _progress("cpu baseline done")
     print(json.dumps(line), flush=True)
     return 0
 
