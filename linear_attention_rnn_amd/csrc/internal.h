@@ -83,6 +83,9 @@ __device__ __forceinline__ void lds_barrier() {
 
 // Sequential kernel: one wavefront per (sequence, head), state in registers.
 hipError_t launch_seq(const SeqArgs& args, hipStream_t stream);
+// The same for items of exactly one token (decode), each state row stored
+// as soon as it is updated; the same bits as launch_seq.
+hipError_t launch_seq1(const SeqArgs& args, hipStream_t stream);
 // The same recurrence with four wavefronts per (sequence, head) (the same
 // bits), for items of more than one token.
 hipError_t launch_seq4(const SeqArgs& args, hipStream_t stream);

@@ -42,6 +42,9 @@ template <> struct In<WKV7_BF16> {
     r.u[1] = reinterpret_cast<const uint4*>(p)[1];
     return r;
   }
+  __device__ static float ld1(const T* p) {
+    return __uint_as_float(static_cast<uint32_t>(*p) << 16);
+  }
   __device__ static void lo_hi(uint32_t x, float& lo, float& hi) {
     lo = __uint_as_float(x << 16);
     hi = __uint_as_float(x & 0xffff0000u);
@@ -74,6 +77,7 @@ template <> struct In<WKV7_F32> {
     for (int q = 0; q < 4; ++q) r.u[q] = reinterpret_cast<const float4*>(p)[q];
     return r;
   }
+  __device__ static float ld1(const T* p) { return *p; }
   __device__ static void cvt4(const R4& r, float f[4]) {
     f[0] = r.u.x; f[1] = r.u.y; f[2] = r.u.z; f[3] = r.u.w;
   }
@@ -125,6 +129,33 @@ __device__ __forceinline__ void store_state(float* p, float4 s) {
   }
 }
 
+// One state row (row 16 g + m of the lane's group, columns 4 c .. 4 c + 3)
+// through one token: the delta-rule sum over the row before this step's
+// decay, the update, and the readout of the updated row. Returns `mine`,
+// replaced by the row's output in the lane (c == m) that stores row 16 g + c.
+__device__ __forceinline__ float row_step(float4& s, const float (&w)[4],
+                                          const float (&a)[4],
+                                          const float (&b)[4],
+                                          const float (&k)[4],
+                                          const float (&r)[4], float vm,
+                                          int c, int m, float mine) {
+  float q = s.x * a[0];
+  q = fmaf(s.y, a[1], q);
+  q = fmaf(s.z, a[2], q);
+  q = fmaf(s.w, a[3], q);
+  const float sa = row_sum16(q);
+  s.x = fmaf(s.x, w[0], fmaf(sa, b[0], vm * k[0]));
+  s.y = fmaf(s.y, w[1], fmaf(sa, b[1], vm * k[1]));
+  s.z = fmaf(s.z, w[2], fmaf(sa, b[2], vm * k[2]));
+  s.w = fmaf(s.w, w[3], fmaf(sa, b[3], vm * k[3]));
+  q = s.x * r[0];
+  q = fmaf(s.y, r[1], q);
+  q = fmaf(s.z, r[2], q);
+  q = fmaf(s.w, r[3], q);
+  const float om = row_sum16(q);
+  return (c == m) ? om : mine;
+}
+
 // The recurrence of work item `it`, head h, on this wavefront (lane = its
 // lane id): the state is read from the pool once, every token of the item
 // is applied in order with its output written, and the state is written
@@ -165,30 +196,82 @@ __device__ __forceinline__ void seq_wave(const SeqArgs& p, const WorkItem it,
     // 169 with all 16 sums and outputs held, three wavefronts per SIMD).
     float mine = 0.f;
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
-      float q = s[m].x * a[0];
-      q = fmaf(s[m].y, a[1], q);
-      q = fmaf(s[m].z, a[2], q);
-      q = fmaf(s[m].w, a[3], q);
-      const float sa = row_sum16(q);
-      s[m].x = fmaf(s[m].x, w[0], fmaf(sa, b[0], v[m] * k[0]));
-      s[m].y = fmaf(s[m].y, w[1], fmaf(sa, b[1], v[m] * k[1]));
-      s[m].z = fmaf(s[m].z, w[2], fmaf(sa, b[2], v[m] * k[2]));
-      s[m].w = fmaf(s[m].w, w[3], fmaf(sa, b[3], v[m] * k[3]));
-      q = s[m].x * r[0];
-      q = fmaf(s[m].y, r[1], q);
-      q = fmaf(s[m].z, r[2], q);
-      q = fmaf(s[m].w, r[3], q);
-      // lane c of group g keeps row 16 g + c for one coalesced 256-byte store
-      const float om = row_sum16(q);
-      mine = (c == m) ? om : mine;
-    }
+    for (int m = 0; m < 16; ++m)
+      mine = row_step(s[m], w, a, b, k, r, v[m], c, m, mine);
     p.o[off + 16 * g + c] = mine;
     off += tstride;
   }
 
 #pragma unroll
   for (int m = 0; m < 16; ++m) store_state<NT>(sbase + m * kN, s[m]);
+}
+
+// Lane m's value to every lane of its row of 16 (DPP row_newbcast).
+template <int M>
+__device__ __forceinline__ float row_bcast_t(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+      0, __builtin_bit_cast(int, x), 0x150 + M, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row_bcast(float x, int m) {
+  switch (m) {   // m is a constant once the caller's loop is unrolled
+    case 0: return row_bcast_t<0>(x);   case 1: return row_bcast_t<1>(x);
+    case 2: return row_bcast_t<2>(x);   case 3: return row_bcast_t<3>(x);
+    case 4: return row_bcast_t<4>(x);   case 5: return row_bcast_t<5>(x);
+    case 6: return row_bcast_t<6>(x);   case 7: return row_bcast_t<7>(x);
+    case 8: return row_bcast_t<8>(x);   case 9: return row_bcast_t<9>(x);
+    case 10: return row_bcast_t<10>(x); case 11: return row_bcast_t<11>(x);
+    case 12: return row_bcast_t<12>(x); case 13: return row_bcast_t<13>(x);
+    case 14: return row_bcast_t<14>(x); default: return row_bcast_t<15>(x);
+  }
+}
+
+// A one-token work item (decode) whose state streams from HBM: the same
+// row steps as seq_wave, with lane 16 g + c owning rows 4 m + g (m < 16),
+// so each state access of the wavefront covers four consecutive rows (1 KB
+// contiguous); the inputs are requested first and the state rows after
+// them, and row m is computed as soon as it has arrived and stored at once
+// while later rows are still in flight. Lane 16 g + c loads v[4 c + g]; row
+// 4 m + g takes v from lane m of its row of 16. Each row's arithmetic is
+// seq_wave's, so the results are the same bits.
+template <int DT, bool NT>
+__device__ __forceinline__ void seq1_wave(const SeqArgs& p, const WorkItem it,
+                                          int h, int lane) {
+  using I = In<DT>;
+  using T = typename I::T;
+  const int g = lane >> 4;
+  const int c = lane & 15;
+  const T* src[6] = {static_cast<const T*>(p.r), static_cast<const T*>(p.w),
+                     static_cast<const T*>(p.k), static_cast<const T*>(p.v),
+                     static_cast<const T*>(p.a), static_cast<const T*>(p.b)};
+  const size_t off = (static_cast<size_t>(it.tok0) * p.H + h) * kN;
+  const typename I::R4 rr = I::ld4(src[0] + off + 4 * c);
+  const typename I::R4 ww = I::ld4(src[1] + off + 4 * c);
+  const typename I::R4 kk = I::ld4(src[2] + off + 4 * c);
+  const typename I::R4 aa = I::ld4(src[4] + off + 4 * c);
+  const typename I::R4 bb = I::ld4(src[5] + off + 4 * c);
+  const float vmine = I::ld1(src[3] + off + 4 * c + g);
+  float* sbase = p.pool + (static_cast<size_t>(it.slot) * p.H + h) * (kN * kN)
+                 + g * kN + 4 * c;
+  // every load is issued before the first use and in row order (the
+  // scheduler would otherwise hold later rows back behind the stores, or
+  // reorder them so that the first rows' waits cover later loads too)
+  float4 s[16];
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    s[m] = load_state<NT>(sbase + 4 * m * kN);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  float w[4], a[4], b[4], k[4], r[4];
+  I::cvt4(ww, w); I::cvt4(aa, a); I::cvt4(bb, b);
+  I::cvt4(kk, k); I::cvt4(rr, r);
+  float mine = 0.f;
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    mine = row_step(s[m], w, a, b, k, r, row_bcast(vmine, m), c, m, mine);
+    store_state<NT>(sbase + 4 * m * kN, s[m]);
+  }
+  // lane c of group g holds the output of row 4 c + g
+  p.o[off + 4 * c + g] = mine;
 }
 
 }  // namespace seqw

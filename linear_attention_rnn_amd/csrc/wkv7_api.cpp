@@ -420,7 +420,7 @@ wkv7_status launch_batch(const wkv7_pool* p, const wkv7::Launch& L,
   if (n_single > 0 && !fuse) {
     args.items = L.seq;
     args.n_items = n_single;
-    hipError_t e = wkv7::launch_seq(args, hs);
+    hipError_t e = wkv7::launch_seq1(args, hs);
     if (e != hipSuccess) return fail_hip(e, "sequential kernel launch");
   }
   if (n_multi > 0) {
