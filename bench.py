@@ -38,10 +38,15 @@ def decode_bytes_per_token_head(in_bytes: int = 2) -> int:
     return 2 * 4 * N * N + 6 * N * in_bytes + N * 4
 
 
-def kernel_sha(name: str) -> str:
-    p = os.path.join(ROOT, "linear_attention_rnn_amd", "csrc", name)
-    with open(p, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def kernel_sha(names) -> str:
+    """Digest of the kernel's source files (a name or a list of names under
+    csrc/, in order)."""
+    h = hashlib.sha256()
+    for name in ([names] if isinstance(names, str) else names):
+        with open(os.path.join(ROOT, "linear_attention_rnn_amd", "csrc",
+                               name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic(kind: str, bytes_alg: float):
@@ -55,6 +60,63 @@ def load_traffic(kind: str, bytes_alg: float):
     if t.get("kernel_sha") != kernel_sha(t["kernel_src"]):
         return None
     return float(t["hbm_bytes_per_launch"])
+
+
+# Raw TCC read-request counts by size and write-request counts: the bytes a
+# kernel moves between the L2 and the memory side, with no fitted factor.
+RAW_READ = ("TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_32B_sum",
+            "TCC_EA0_RDREQ_64B_sum", "TCC_EA0_RDREQ_128B_sum")
+RAW_WRITE = ("TCC_EA0_WRREQ_sum", "TCC_EA0_WRREQ_64B_sum")
+
+
+def pmc_summary(paths, kernel: str) -> dict:
+    """Means per dispatch of the counters in rocprofv3 counter-collection
+    CSVs (one or more passes) for kernels whose name contains `kernel`,
+    grouped by grid size; with the raw request counts present, the bytes
+    read (32/64/128-byte requests) and written (64-byte requests and the
+    rest as 32-byte ones) per dispatch."""
+    import csv
+    import collections
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    grids = {}
+    for path in paths:
+        with open(path, newline="") as f:
+            for row in csv.DictReader(f):
+                if kernel not in row["Kernel_Name"]:
+                    continue
+                key = (path, int(row["Dispatch_Id"]))
+                per[key][row["Counter_Name"]] += float(row["Counter_Value"])
+                grids[key] = int(row["Grid_Size"])
+    groups = collections.defaultdict(lambda: collections.defaultdict(list))
+    distinct = collections.defaultdict(collections.Counter)
+    for key, cs in per.items():
+        for c, v in cs.items():
+            groups[grids[key]][c].append(v)
+        if all(c in cs for c in RAW_READ):
+            rb = (128 * cs["TCC_EA0_RDREQ_128B_sum"] +
+                  64 * cs["TCC_EA0_RDREQ_64B_sum"] +
+                  32 * cs["TCC_EA0_RDREQ_32B_sum"])
+            distinct[grids[key]][f"read {rb / 2**20:.2f} MiB"] += 1
+        if all(c in cs for c in RAW_WRITE):
+            wb = (64 * cs["TCC_EA0_WRREQ_64B_sum"] + 32 *
+                  (cs["TCC_EA0_WRREQ_sum"] - cs["TCC_EA0_WRREQ_64B_sum"]))
+            distinct[grids[key]][f"write {wb / 2**20:.2f} MiB"] += 1
+    out = {}
+    for g, cs in sorted(groups.items()):
+        m = {c: sum(v) / len(v) for c, v in cs.items()}
+        m["dispatches"] = max(len(v) for v in cs.values())
+        if distinct[g]:
+            m["per_dispatch_values"] = dict(distinct[g])
+        if all(c in m for c in RAW_READ):
+            m["read_bytes"] = (128 * m["TCC_EA0_RDREQ_128B_sum"] +
+                               64 * m["TCC_EA0_RDREQ_64B_sum"] +
+                               32 * m["TCC_EA0_RDREQ_32B_sum"])
+        if all(c in m for c in RAW_WRITE):
+            m["write_bytes"] = (64 * m["TCC_EA0_WRREQ_64B_sum"] + 32 *
+                                (m["TCC_EA0_WRREQ_sum"] -
+                                 m["TCC_EA0_WRREQ_64B_sum"]))
+        out[f"grid{g}"] = m
+    return out
 
 
 def run_decode(steps: int, warmup: int, seed: int = 1):
@@ -547,7 +609,8 @@ def run_decode_large(steps: int = 20, warmup: int = 3, seed: int = 4):
         "workload": "decode_b1024_h64_pool4096_bf16in_f32state",
         "tokens_per_s": n_active / (k_ms * 1e-3), "kernel_ms": k_ms,
         "hbm": {"achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": gbs / HBM_PEAK_GBS, "bytes_per_launch": bytes_launch},
+                "frac": gbs / HBM_PEAK_GBS, "bytes_per_launch": bytes_launch,
+                "traffic": load_traffic("decode_large", bytes_launch)},
         "steps": steps, "warmup": warmup,
     }
 
@@ -1168,7 +1231,32 @@ def main(argv=None) -> int:
                             "q8_proj,small,short,ceilings",
                     help="comma list of legs to run (profiling one kernel)")
     ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--pmc-summary", nargs="+", metavar="CSV",
+                    help="summarise rocprofv3 counter CSVs (no GPU use) for "
+                         "--kernel and exit; with --traffic-out, write the "
+                         "traffic record the bench reports for --grid")
+    ap.add_argument("--kernel", default="seq_kernel")
+    ap.add_argument("--grid", type=int, default=0)
+    ap.add_argument("--src", default="",
+                    help="comma list of the kernel's source files (csrc/)")
+    ap.add_argument("--workload", default="")
+    ap.add_argument("--traffic-out", default="")
     args = ap.parse_args(argv)
+    if args.pmc_summary:
+        summ = pmc_summary(args.pmc_summary, args.kernel)
+        print(json.dumps(summ, indent=1))
+        if args.traffic_out:
+            m = summ[f"grid{args.grid}"]
+            src = args.src.split(",")
+            rec = {"kernel": args.kernel, "kernel_src": src,
+                   "kernel_sha": kernel_sha(src), "workload": args.workload,
+                   "grid": args.grid, "counters_per_dispatch": m,
+                   "read_bytes_per_launch": m["read_bytes"],
+                   "write_bytes_per_launch": m["write_bytes"],
+                   "hbm_bytes_per_launch": m["read_bytes"] + m["write_bytes"]}
+            with open(args.traffic_out, "w") as f:
+                json.dump(rec, f, indent=1)
+        return 0
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not "
               "supported (slots shard across GPUs with no exchange, but no "

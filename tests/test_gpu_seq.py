@@ -288,3 +288,36 @@ def test_decode_streams_large_state_nontemporally(dtype):
             assert err < tol_for(dtype)
     finally:
         W.wkv7_pool_destroy(pool)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_streaming_form(dtype):
+    """A decode step whose active state exceeds the 256 MB Infinity Cache
+    (520 slots x H=32 = 272 MB) takes the streaming form of the row steps
+    (contiguous rows, each stored as it is updated): every slot and head
+    against the float64 oracle, and untouched slots bit-identical."""
+    from oracle import wkv7_cref as C
+    n_active, H = 520, 32
+    rng = np.random.default_rng(31)
+    ids = rng.permutation(600)[:n_active].astype(np.int32)
+    say(f"streaming decode, {n_active} slots x H={H}, dtype={dtype}")
+    b = G.make_batch(rng, ids, [1] * n_active, H, 64, dtype)
+    init = G.draw_states(rng, n_active, H, 64)
+    others = np.setdiff1d(np.arange(600), ids).astype(np.int32)
+    other_states = G.draw_states(rng, len(others), H, 64, std=1.0)
+    pool = _pool(600, H)
+    try:
+        set_states(pool, others, other_states)
+        set_states(pool, ids, init)
+        o = run_forward(pool, b)
+        S = get_states(pool, ids)
+        after = get_states(pool, others)
+    finally:
+        W.wkv7_pool_destroy(pool)
+    S_ref = np.ascontiguousarray(G.as_f64(init).reshape(n_active * H, 64, 64))
+    o_ref = C.run_heads(S_ref, b.inputs, 1, n_active * H, 64)
+    e_o = rel_err(o, o_ref.reshape(n_active, H, 64))
+    e_s = rel_err(S, S_ref.reshape(n_active, H, 64, 64))
+    say(f"  o err {e_o:.3e}  S err {e_s:.3e}")
+    assert e_o < 1e-5 and e_s < 1e-5
+    assert torch.equal(after.view(torch.int32), other_states.view(torch.int32))
