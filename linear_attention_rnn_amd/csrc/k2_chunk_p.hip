@@ -89,6 +89,8 @@ static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 constexpr float kHalfSafe = 32768.f;            // fp16 operand bound
 constexpr float kMinLamL = 7.88860905e-31f;     // 2^-100
 
+template <int V> struct IntC { static constexpr int value = V; };
+
 struct F8 { bf16x8 h, l; };
 struct F4 { bf16x4 h, l; };
 
@@ -518,7 +520,7 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
   float w0[4], w1[4], P0[4], P1[4];
   auto prep = [&](int c) {
     x = nxt;
-    pad_raw(x, min(kL, len - c * kL), rg);
+    if (len - c * kL < kL) pad_raw(x, len - c * kL, rg);   // the last chunk
     if (zero_v) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) x.v[e] = 0u;
@@ -541,7 +543,11 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
   // in the same order (two per step; all waves of the workgroup reach each
   // one), so each role's registers hold only its own state.
   const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-  if (is_key) {
+  // The key loop is instantiated once per key wavefront W (= wv): which
+  // row groups, Gram matrix and LDS destination a wavefront owns are then
+  // constants, not per-step selects.
+  auto key_loop = [&](auto Wc) {
+    constexpr int W = decltype(Wc)::value;
     for (int step = 0; step <= nch; ++step) {
       const int cK = step;          // chunk whose operands and Grams are built
       const bool k_on = cK < nch;
@@ -560,13 +566,8 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
   #pragma unroll
         for (int q = 0; q < 8; ++q) { g0[q] = TOT[q * 64 + j0]; g1[q] = TOT[q * 64 + j0 + 1]; }
         float lo0, lo1, hi0, hi1;      // products below and above the pair
-        switch (wv & 3) {
-          case 0: outer_products<0>(g0, g1, lo0, lo1, hi0, hi1); break;
-          case 1: outer_products<1>(g0, g1, lo0, lo1, hi0, hi1); break;
-          case 2: outer_products<2>(g0, g1, lo0, lo1, hi0, hi1); break;
-          default: outer_products<3>(g0, g1, lo0, lo1, hi0, hi1); break;
-        }
-        const int wq = 2 * (wv & 3);
+        outer_products<W>(g0, g1, lo0, lo1, hi0, hi1);
+        constexpr int wq = 2 * W;
         const bool second = (lane >> 5) != 0;   // group wq + 1
         const float ga0 = g0[wq], ga1 = g1[wq], gb0 = g0[wq + 1], gb1 = g1[wq + 1];
         const float pre0 = second ? lo0 * ga0 : lo0, pre1 = second ? lo1 * ga1 : lo1;
@@ -633,9 +634,9 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
       float gmax = 0.f;
       if (k_on) {
         // key: Gram matrix wv, tiles (tt, st) = (0,0), (1,0), (1,1) as C[s][t]
-        const __bf16* Pm = (wv & 1) ? Kbar : Bbar;
-        const __bf16* Qm = (wv >= 2) ? Rhat : Ahat;
-        const bool strict = wv < 2;
+        const __bf16* Pm = (W & 1) ? Kbar : Bbar;
+        const __bf16* Qm = (W >= 2) ? Rhat : Ahat;
+        constexpr bool strict = W < 2;
         f32x4 gt[3];
         int ti = 0;
   #pragma unroll
@@ -648,16 +649,18 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
               c = mm3(ldp8(Pm, kM64, kP64, 16 * st + n16, 32 * kc, g),
                       ldp8(Qm, kM64, kP64, 16 * tt + n16, 32 * kc, g), c);
             const int t = 16 * tt + n16;
+            if (st == tt) {            // tile (1, 0) lies wholly below the diagonal
   #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int s = 16 * st + 4 * g + r;
-              const bool keep = strict ? (s < t) : (s <= t);
-              c[r] = keep ? c[r] : 0.f;
+              for (int r = 0; r < 4; ++r) {
+                const int s = 16 * st + 4 * g + r;
+                const bool keep = strict ? (s < t) : (s <= t);
+                c[r] = keep ? c[r] : 0.f;
+              }
             }
             gt[ti++] = c;
           }
         }
-        if (wv == 0) {
+        if (W == 0) {
           // A_ab in fp16 as [t][s] rows and as [s][t] rows (tile ti holds
           // C[s][t] = A_ab[t][s])
           _Float16* ABr = AB;
@@ -676,7 +679,7 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
             }
           }
         } else {
-          _Float16* dst = LLk + (wv - 1) * kM32;
+          _Float16* dst = LLk + (W - 1) * kM32;
           ti = 0;
   #pragma unroll
           for (int tt = 0; tt < 2; ++tt) {
@@ -692,6 +695,14 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
       if (cK + 1 < nch) prep(cK + 1);   // the next chunk
       (void)barrier_or2(FLG + 8, wv, lane, k_on && bad_k,
                         k_on && !(gmax < kHalfSafe));             // B3
+    }
+  };
+  if (is_key) {
+    switch (wv) {
+      case 0: key_loop(IntC<0>{}); break;
+      case 1: key_loop(IntC<1>{}); break;
+      case 2: key_loop(IntC<2>{}); break;
+      default: key_loop(IntC<3>{}); break;
     }
   } else {
     // fallback flags of chunk step - 1, known from the end of the step
