@@ -510,16 +510,18 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
     }
   }
 
-  // Key side: a chunk's raw inputs are loaded two steps before its operands
-  // are built (nxt) and prepared one step before (x: padded; running
-  // products of w over the thread's 4 rows in P0/P1; the rows' totals in
-  // TOT), in the previous step's second interval, where the key wavefronts
-  // wait on the value side anyway. The third barrier then orders the TOT
-  // writes before their reads, and no barrier precedes the operand build.
-  Raw nxt, x;
+  // Key side: a chunk's raw inputs are loaded into x right after the
+  // operands of the chunk before have been built from it (the loads are
+  // issued after those reads, so one buffer serves both and no copy is
+  // made at the back edge), and prepared one step before their operands are
+  // built (padded; running products of w over the thread's 4 rows in P0/P1;
+  // the rows' totals in TOT), in the previous step's second interval, where
+  // the key wavefronts wait on the value side anyway. The third barrier then
+  // orders the TOT writes before their reads, and no barrier precedes the
+  // operand build.
+  Raw x;
   float w0[4], w1[4], P0[4], P1[4];
   auto prep = [&](int c) {
-    x = nxt;
     if (len - c * kL < kL) pad_raw(x, len - c * kL, rg);   // the last chunk
     if (zero_v) {
 #pragma unroll
@@ -534,7 +536,7 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
     TOT[rg * 64 + j0 + 1] = P1[3];
   };
   if (is_key) {
-    load_raw(nxt, p, tok0, min(kL, len), h, rg, jp);
+    load_raw(x, p, tok0, min(kL, len), h, rg, jp);
     if (nch > 0) prep(0);
   }
   __syncthreads();                                                // TOT of chunk 0
@@ -624,7 +626,7 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
         put4h(Vt, kP32, j0 + 1, 4 * rg, f32x4{vt1[0], vt1[1], vt1[2], vt1[3]});
         // next chunk's inputs, in flight from here on
         if (cK + 1 < nch)
-          load_raw(nxt, p, t0K + kL, min(kL, len - (cK + 1) * kL), h, rg, jp);
+          load_raw(x, p, t0K + kL, min(kL, len - (cK + 1) * kL), h, rg, jp);
       }
       // B2. The range flags of chunk cK travel with B3: its Grams are built
       // either way, and the value side reads them only if no flag was
