@@ -217,6 +217,15 @@ __device__ __forceinline__ uint32_t dpp_umax16(uint32_t x) {
 // max over the wavefront of x >= 0 (or NaN): rows of 16 by DPP (every lane
 // of a row then holds the row's maximum), then the four rows through scalar
 // registers (no LDS round trip). The result is wavefront-uniform.
+// max(m, |x_r|) as floats, for the power-of-two scale of an operand: one
+// max3 with |x| source modifiers per two values, no sign masking. A NaN
+// among the x_r is skipped (its row stays NaN after scaling); an infinity
+// makes the scale 1, as in pow2_scale.
+__device__ __forceinline__ float scale_max4(f32x4 x, float m) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) m = fmaxf(m, fabsf(x[r]));
+  return m;
+}
 __device__ __forceinline__ float wave_max(float x) {
   const uint32_t u = dpp_umax16(__float_as_uint(x));
   const uint32_t r0 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(u), 0));
@@ -737,7 +746,7 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
           const _Float16* Aak = LLv;
           float m = 0.f;
   #pragma unroll
-          for (int jt = 0; jt < 4; ++jt) m = abs_max4(S[jt], m);
+          for (int jt = 0; jt < 4; ++jt) m = scale_max4(S[jt], m);
           const float sS = pow2_scale(wave_max(m), &inv_s);
           Sf0 = frag8h(S[0], S[1], sS);
           Sf1 = frag8h(S[2], S[3], sS);
@@ -795,13 +804,13 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
         const _Float16* Mrk = LLv + 2 * kM32;
         const float* lam = LAMb + bV * 64;
         float inv_x;
-        const float sX = pow2_scale(wave_max(abs_max4(X[1], abs_max4(X[0], 0.f))), &inv_x);
+        const float sX = pow2_scale(wave_max(scale_max4(X[1], scale_max4(X[0], 0.f))), &inv_x);
         const f16x8 Xf = frag8h(X[0], X[1], sX);
         f32x4 U[2];
         U[0] = mmah(Tf0, Xf, z);
         U[1] = mmah(Tf1, Xf, z);
         float inv_u;
-        const float sU = pow2_scale(wave_max(abs_max4(U[1], abs_max4(U[0], 0.f))), &inv_u);
+        const float sU = pow2_scale(wave_max(scale_max4(U[1], scale_max4(U[0], 0.f))), &inv_u);
         const float inv_ux = inv_u * inv_x;
         const f16x8 Uf = frag8h(U[0], U[1], sU);
   #pragma unroll
