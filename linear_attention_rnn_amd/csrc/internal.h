@@ -105,10 +105,14 @@ hipError_t launch_chunked_p(const SeqArgs& args, hipStream_t stream,
 hipError_t launch_chunked_p_seg(const SeqArgs& args, const SegItem* segs,
                                 hipStream_t stream, const WorkItem* dec = nullptr,
                                 int32_t n_dec = 0);
+// Wavefronts per workgroup of the bf16 chunked kernel.
+constexpr int kChunkPWaves = 12;
 // Trailing workgroups of a chunked-kernel launch that run n_dec decode
-// items (eight (item, head) pairs each).
+// items (one (item, head) pair per wavefront).
 inline int64_t chunk_decode_blocks(int32_t n_dec, int32_t H) {
-  return n_dec > 0 ? (static_cast<int64_t>(n_dec) * H + 7) / 8 : 0;
+  return n_dec > 0
+             ? (static_cast<int64_t>(n_dec) * H + kChunkPWaves - 1) / kChunkPWaves
+             : 0;
 }
 // Carry scan of split sequences: one workgroup per (sequence, head).
 hipError_t launch_seg_scan(const ScanItem* items, int32_t n_items, int32_t H,

@@ -82,8 +82,9 @@ constexpr int kOffVO = kOffTOT + 8 * 64 * 4;               // 2 buffers
 constexpr int kLLBytes = 3 * kM32 * 2;
 constexpr int kOffLL = kOffVO + 2 * kVOBytes;              // 2 buffers
 constexpr int kOffLAM = kOffLL + 2 * kLLBytes;             // fp32 [2][64]
-constexpr int kOffFLG = kOffLAM + 2 * 64 * 4;              // u32 [2][8]
-constexpr int kLdsBytes = kOffFLG + 2 * 8 * 4;
+constexpr int kOffTT = kOffLAM + 2 * 64 * 4;               // fp16 T [32][32], 2 buffers
+constexpr int kOffFLG = kOffTT + 2 * kM32 * 2;             // u32 [16]
+constexpr int kLdsBytes = kOffFLG + 16 * 4;
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 
 constexpr float kHalfSafe = 32768.f;            // fp16 operand bound
@@ -263,54 +264,73 @@ __device__ __forceinline__ bool any_half_ge(uint32_t m, uint32_t limit) {
   return (m & 0xffffu) >= limit || (m >> 16) >= limit;
 }
 
-// raw inputs of a key thread: rows 4 rg + e (e < 4), channels 2 jp, 2 jp + 1
-struct Raw { uint32_t r[4], w[4], k[4], a[4], b[4], v[4]; };
+// raw inputs of a key thread, rows 4 rg + e (e < 4), channels 2 jp, 2 jp + 1:
+// a t wavefront holds r, a and w, an s wavefront k, b, v and w
+struct RawT { uint32_t r[4], a[4], w[4]; };
+struct RawS { uint32_t k[4], b[4], v[4], w[4]; };
 
 // Loads through buffer resources based at the chunk's first row, with a
 // 32-bit lane offset and no branch: a row past the chunk's end re-reads the
 // last valid row (always in bounds). The caller replaces such rows by
 // padding (pad_raw) when it consumes them, so nothing waits on the loads
 // here.
-__device__ __forceinline__ void load_raw(Raw& x, const SeqArgs& p, int t0,
-                                         int n, int h, int rg, int jp) {
+template <int NA>
+__device__ __forceinline__ void load_rows(uint32_t (*const dst[NA])[4],
+                                          const void* const src[NA],
+                                          const SeqArgs& p, int t0, int n,
+                                          int h, int rg, int jp) {
   const size_t row0 = (static_cast<size_t>(t0) * p.H + h) * (kN * 2);  // bytes
   const uint32_t rowb = static_cast<uint32_t>(p.H) * (kN * 2);
   const int bytes = static_cast<int>(static_cast<uint32_t>(n) * rowb);
-  const char* base[6] = {static_cast<const char*>(p.r), static_cast<const char*>(p.w),
-                         static_cast<const char*>(p.k), static_cast<const char*>(p.a),
-                         static_cast<const char*>(p.b), static_cast<const char*>(p.v)};
-  __amdgpu_buffer_rsrc_t rs[6];
+  __amdgpu_buffer_rsrc_t rs[NA];
 #pragma unroll
-  for (int u = 0; u < 6; ++u)
-    rs[u] = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base[u] + row0),
-                                              0, bytes, 0x00020000);
+  for (int u = 0; u < NA; ++u)
+    rs[u] = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(static_cast<const char*>(src[u]) + row0), 0, bytes,
+        0x00020000);
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int voff = static_cast<int>(
         static_cast<uint32_t>(min(4 * rg + e, n - 1)) * rowb + 4 * jp);
-    x.r[e] = __builtin_amdgcn_raw_buffer_load_b32(rs[0], voff, 0, 0);
-    x.w[e] = __builtin_amdgcn_raw_buffer_load_b32(rs[1], voff, 0, 0);
-    x.k[e] = __builtin_amdgcn_raw_buffer_load_b32(rs[2], voff, 0, 0);
-    x.a[e] = __builtin_amdgcn_raw_buffer_load_b32(rs[3], voff, 0, 0);
-    x.b[e] = __builtin_amdgcn_raw_buffer_load_b32(rs[4], voff, 0, 0);
-    x.v[e] = __builtin_amdgcn_raw_buffer_load_b32(rs[5], voff, 0, 0);
+#pragma unroll
+    for (int u = 0; u < NA; ++u)
+      (*dst[u])[e] = __builtin_amdgcn_raw_buffer_load_b32(rs[u], voff, 0, 0);
   }
 }
+__device__ __forceinline__ void load_raw(RawT& x, const SeqArgs& p, int t0,
+                                         int n, int h, int rg, int jp) {
+  uint32_t (*const dst[3])[4] = {&x.r, &x.a, &x.w};
+  const void* const src[3] = {p.r, p.a, p.w};
+  load_rows<3>(dst, src, p, t0, n, h, rg, jp);
+}
+__device__ __forceinline__ void load_raw(RawS& x, const SeqArgs& p, int t0,
+                                         int n, int h, int rg, int jp) {
+  uint32_t (*const dst[4])[4] = {&x.k, &x.b, &x.v, &x.w};
+  const void* const src[4] = {p.k, p.b, p.v, p.w};
+  load_rows<4>(dst, src, p, t0, n, h, rg, jp);
+}
 // rows 4 rg + e >= n become padding: w = 1, everything else 0 (state unchanged)
-__device__ __forceinline__ void pad_raw(Raw& x, int n, int rg) {
+__device__ __forceinline__ void pad_raw(RawT& x, int n, int rg) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const bool pad = 4 * rg + e >= n;
     x.r[e] = pad ? 0u : x.r[e];
-    x.w[e] = pad ? 0x3f803f80u : x.w[e];
-    x.k[e] = pad ? 0u : x.k[e];
     x.a[e] = pad ? 0u : x.a[e];
+    x.w[e] = pad ? 0x3f803f80u : x.w[e];
+  }
+}
+__device__ __forceinline__ void pad_raw(RawS& x, int n, int rg) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const bool pad = 4 * rg + e >= n;
+    x.k[e] = pad ? 0u : x.k[e];
     x.b[e] = pad ? 0u : x.b[e];
     x.v[e] = pad ? 0u : x.v[e];
+    x.w[e] = pad ? 0x3f803f80u : x.w[e];
   }
 }
 
-// ---- T = (I - A_ab)^-1 on a value wavefront, all in registers ----
+// ---- T = (I - A_ab)^-1 on the key wavefront that computes A_ab ----
 // A 16x16 matrix M is held as two fp16 operand fragments and their fp32
 // values:
 //   row(M): lane (g, n) holds M[n][4g + e]   (left operand of a product)
@@ -371,7 +391,8 @@ __device__ __forceinline__ f16x4 ldh4(const _Float16* m, int pitch, int row,
 }
 
 // Workgroup OR of two flag bits with one barrier: lane 0 of every wave
-// posts its wave's bits; all threads read the eight posts after the barrier.
+// posts its wave's bits; all threads read the twelve posts after the
+// barrier.
 __device__ __forceinline__ uint32_t barrier_or2(uint32_t* slot, int wv,
                                                 int lane, bool b0, bool b1) {
   const uint32_t m0 = __builtin_amdgcn_ballot_w64(b0) != 0 ? 1u : 0u;
@@ -380,7 +401,7 @@ __device__ __forceinline__ uint32_t barrier_or2(uint32_t* slot, int wv,
   __syncthreads();
   uint32_t r = 0;
 #pragma unroll
-  for (int w = 0; w < 8; ++w) r |= slot[w];
+  for (int w = 0; w < kChunkPWaves; ++w) r |= slot[w];
   return r;
 }
 
@@ -438,12 +459,12 @@ __device__ __forceinline__ void exact_chunk(const SeqArgs& p, f32x4* S, int t0,
 // SEG = false: items are pool slots (p.items); true: segments (segs) with
 // their own state buffers and flags.
 // Workgroups past the (item, head) grid run the decode work items `dec` of
-// the same call, eight (item, head) pairs per workgroup, one per
+// the same call, twelve (item, head) pairs per workgroup, one per
 // wavefront, with the sequential recurrence (the same bits as the
 // sequential kernel): a batch's decode tokens then fill CUs that its
 // prefills leave idle, in the same launch.
 template <bool SEG>
-__global__ __launch_bounds__(512, 1)
+__global__ __launch_bounds__(64 * kChunkPWaves, 1)
 void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
                     int32_t n_dec) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
@@ -462,13 +483,14 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t n_main = static_cast<int64_t>(p.n_items) * p.H;
   if (static_cast<int64_t>(blockIdx.x) >= n_main) {
-    const int64_t q = (static_cast<int64_t>(blockIdx.x) - n_main) * 8 + wv;
+    const int64_t q = (static_cast<int64_t>(blockIdx.x) - n_main) * kChunkPWaves + wv;
     const int di = static_cast<int>(q / p.H);
     const int dh = static_cast<int>(q - static_cast<int64_t>(di) * p.H);
     if (di < n_dec) seqw::seq_wave<WKV7_BF16, false>(p, dec[di], dh, lane);
     return;
   }
-  const bool is_key = wv < 4;
+  // roles: t wavefronts 0-3, s wavefronts 4-7, value wavefronts 8-11
+  const int role = wv >> 2;
   const int g = lane >> 4;
   const int n16 = lane & 15;
   const int item = blockIdx.x / p.H;
@@ -496,155 +518,117 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
   const int nch = (len + kL - 1) / kL;
   const size_t rowstride = static_cast<size_t>(p.H) * kN;
 
-  // key-thread ownership: channel pair jp, rows 4 rg .. 4 rg + 3
+  // key-thread ownership (t and s wavefronts alike): channel pair jp, rows
+  // 4 rg .. 4 rg + 3
   const int jp = lane & 31;
   const int j0 = 2 * jp;
   const int rg = 2 * (wv & 3) + (lane >> 5);
   // value-wavefront ownership: state rows i in [16 vb, 16 vb + 16)
   const int vb = wv & 3;
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
 
-  const size_t soff = static_cast<size_t>(16 * vb + n16) * kN + 4 * g;
-  f32x4 S[4] = {};   // S[jt][r] = S[i = 16 vb + n16][j = 16 jt + 4 g + r]
-  if (!is_key) {
-    if (flags & kSegIdentity) {
-#pragma unroll
-      for (int jt = 0; jt < 4; ++jt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          S[jt][r] = (16 * vb + n16 == 16 * jt + 4 * g + r) ? 1.f : 0.f;
-    } else if (s_in) {
-#pragma unroll
-      for (int jt = 0; jt < 4; ++jt)   // global accesses (see gf32x4)
-        S[jt] = *(const gf32x4*)(s_in + soff + 16 * jt);
-    }
-  }
-
-  // Key side: a chunk's raw inputs are loaded into x right after the
-  // operands of the chunk before have been built from it (the loads are
-  // issued after those reads, so one buffer serves both and no copy is
-  // made at the back edge), and prepared one step before their operands are
-  // built (padded; running products of w over the thread's 4 rows in P0/P1;
-  // the rows' totals in TOT), in the previous step's second interval, where
-  // the key wavefronts wait on the value side anyway. The third barrier then
-  // orders the TOT writes before their reads, and no barrier precedes the
-  // operand build.
-  Raw x;
+  // Key side, split over two roles that own the same rows and channels:
+  // the t wavefronts build the operands made from r and a (and then the
+  // Gram matrices and T), the s wavefronts those made from k, b and v and
+  // the chunk's decay totals. A chunk's raw inputs are loaded right after
+  // the operands of the chunk before have been built from the same
+  // registers, and prepared one step before their operands are built
+  // (padded; running products of w over the thread's 4 rows in P0/P1; the
+  // s wavefronts post the rows' totals in TOT), in the previous step's
+  // second interval. The third barrier orders the TOT writes before their
+  // reads. Each loop is instantiated once per wavefront W (= wv & 3): its
+  // row groups, Gram matrix and LDS destinations are then constants.
   float w0[4], w1[4], P0[4], P1[4];
-  auto prep = [&](int c) {
-    if (len - c * kL < kL) pad_raw(x, len - c * kL, rg);   // the last chunk
-    if (zero_v) {
+  auto decays = [&](const uint32_t (&wr)[4]) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) x.v[e] = 0u;
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) { w0[e] = bf_lo(x.w[e]); w1[e] = bf_hi(x.w[e]); }
+    for (int e = 0; e < 4; ++e) { w0[e] = bf_lo(wr[e]); w1[e] = bf_hi(wr[e]); }
     P0[0] = w0[0]; P1[0] = w1[0];
 #pragma unroll
     for (int e = 1; e < 4; ++e) { P0[e] = P0[e - 1] * w0[e]; P1[e] = P1[e - 1] * w1[e]; }
-    TOT[rg * 64 + j0] = P0[3];
-    TOT[rg * 64 + j0 + 1] = P1[3];
   };
-  if (is_key) {
-    load_raw(x, p, tok0, min(kL, len), h, rg, jp);
-    if (nch > 0) prep(0);
-  }
-  __syncthreads();                                                // TOT of chunk 0
-
-  // The key and value wavefronts run separate loops with the same barriers
-  // in the same order (two per step; all waves of the workgroup reach each
-  // one), so each role's registers hold only its own state.
-  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-  // The key loop is instantiated once per key wavefront W (= wv): which
-  // row groups, Gram matrix and LDS destination a wavefront owns are then
-  // constants, not per-step selects.
-  auto key_loop = [&](auto Wc) {
+  // Decay over the row groups before the thread's group (pre), after it
+  // (suf) and over the whole chunk (lam), from the group totals in TOT. A
+  // wavefront's two groups are 2 W and 2 W + 1, so the products outside
+  // them have wavefront-uniform bounds.
+  struct Dec { float pre0, pre1, suf0, suf1, lam0, lam1; };
+  auto chunk_decays = [&](auto Wc) {
     constexpr int W = decltype(Wc)::value;
+    float g0[8], g1[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) { g0[q] = TOT[q * 64 + j0]; g1[q] = TOT[q * 64 + j0 + 1]; }
+    float lo0, lo1, hi0, hi1;      // products below and above the pair
+    outer_products<W>(g0, g1, lo0, lo1, hi0, hi1);
+    constexpr int wq = 2 * W;
+    const bool second = (lane >> 5) != 0;   // group wq + 1
+    const float ga0 = g0[wq], ga1 = g1[wq], gb0 = g0[wq + 1], gb1 = g1[wq + 1];
+    Dec d;
+    d.pre0 = second ? lo0 * ga0 : lo0;
+    d.pre1 = second ? lo1 * ga1 : lo1;
+    d.suf0 = second ? hi0 : gb0 * hi0;
+    d.suf1 = second ? hi1 : gb1 * hi1;
+    d.lam0 = (lo0 * ga0) * (gb0 * hi0);
+    d.lam1 = (lo1 * ga1) * (gb1 * hi1);
+    return d;
+  };
+
+  auto t_loop = [&](auto Wc) {
+    constexpr int W = decltype(Wc)::value;
+    RawT x;
+    auto prep = [&](int c) {
+      if (len - c * kL < kL) pad_raw(x, len - c * kL, rg);   // the last chunk
+      decays(x.w);
+    };
+    load_raw(x, p, tok0, min(kL, len), h, rg, jp);
+    prep(0);
+    __syncthreads();                                              // TOT of chunk 0
     for (int step = 0; step <= nch; ++step) {
       const int cK = step;          // chunk whose operands and Grams are built
       const bool k_on = cK < nch;
       const int bK = cK & 1;
       _Float16* VOk = reinterpret_cast<_Float16*>(lds + kOffVO + bK * kVOBytes);
       _Float16* LLk = reinterpret_cast<_Float16*>(lds + kOffLL + bK * kLLBytes);
+      _Float16* TTk = reinterpret_cast<_Float16*>(lds + kOffTT) + bK * kM32;
       const int t0K = tok0 + cK * kL;
       // ===== interval 1 =====
       bool bad_k = false;
       if (k_on) {
-        // key: operands of chunk cK. Decay over the row groups before the
-        // thread's group (pre), after it (suf) and over the whole chunk (lam).
-        // The wavefront's two groups are 2 (wv & 3) and the one after, so the
-        // products outside them have wavefront-uniform bounds.
-        float g0[8], g1[8];
-  #pragma unroll
-        for (int q = 0; q < 8; ++q) { g0[q] = TOT[q * 64 + j0]; g1[q] = TOT[q * 64 + j0 + 1]; }
-        float lo0, lo1, hi0, hi1;      // products below and above the pair
-        outer_products<W>(g0, g1, lo0, lo1, hi0, hi1);
-        constexpr int wq = 2 * W;
-        const bool second = (lane >> 5) != 0;   // group wq + 1
-        const float ga0 = g0[wq], ga1 = g1[wq], gb0 = g0[wq + 1], gb1 = g1[wq + 1];
-        const float pre0 = second ? lo0 * ga0 : lo0, pre1 = second ? lo1 * ga1 : lo1;
-        const float suf0 = second ? hi0 : gb0 * hi0, suf1 = second ? hi1 : gb1 * hi1;
-        const float lam0 = (lo0 * ga0) * (gb0 * hi0), lam1 = (lo1 * ga1) * (gb1 * hi1);
-        if (rg == 0) { LAMb[bK * 64 + j0] = lam0; LAMb[bK * 64 + j0 + 1] = lam1; }
+        const Dec d = chunk_decays(Wc);
         // hardware reciprocal (1 ulp): the scaled Gram operands are split into
         // bf16 pairs, far coarser; a lam below the fast path's range takes the
         // token-by-token path, which does not use these operands
-        const float inv0 = __builtin_amdgcn_rcpf(lam0), inv1 = __builtin_amdgcn_rcpf(lam1);
+        const float inv0 = __builtin_amdgcn_rcpf(d.lam0), inv1 = __builtin_amdgcn_rcpf(d.lam1);
         _Float16* Abar = VOk;
         _Float16* Rbar = VOk + kM64;
-        _Float16* BbT = VOk + 2 * kM64;
-        _Float16* KbT = BbT + kMT;
-        _Float16* Vt = KbT + kMT;
-        // range of the raw inputs (|Abar| <= |a| etc. when every |w| <= 1)
-        uint32_t mx = 0u, mw = 0u;
+        // range of the raw inputs (|Abar| <= |a| etc. when every |w| <= 1;
+        // w and lam are checked on the s side)
+        uint32_t mx = 0u;
   #pragma unroll
         for (int e = 0; e < 4; ++e) {
           mx = absmax_bits(mx, x.a[e]); mx = absmax_bits(mx, x.r[e]);
-          mx = absmax_bits(mx, x.b[e]); mx = absmax_bits(mx, x.k[e]);
-          mx = absmax_bits(mx, x.v[e]); mw = absmax_bits(mw, x.w[e]);
         }
-        bad_k = !(lam0 >= kMinLamL) || !(lam1 >= kMinLamL) ||
-                any_half_ge(mx, 0x4700u) ||     // |x| >= 2^15 (or NaN/Inf)
-                any_half_ge(mw, 0x3f81u);       // |w| > 1 (or NaN)
-        float sfx0 = suf0, sfx1 = suf1;
-        float bt0[4], bt1[4], kt0[4], kt1[4], vt0[4], vt1[4];
+        bad_k = any_half_ge(mx, 0x4700u);     // |x| >= 2^15 (or NaN/Inf)
   #pragma unroll
         for (int e = 3; e >= 0; --e) {
           const int t = 4 * rg + e;
-          const float lp0 = e == 0 ? pre0 : pre0 * P0[e - 1];
-          const float lp1 = e == 0 ? pre1 : pre1 * P1[e - 1];
-          const float lt0 = pre0 * P0[e], lt1 = pre1 * P1[e];
+          const float lp0 = e == 0 ? d.pre0 : d.pre0 * P0[e - 1];
+          const float lp1 = e == 0 ? d.pre1 : d.pre1 * P1[e - 1];
+          const float lt0 = d.pre0 * P0[e], lt1 = d.pre1 * P1[e];
           const float ab0 = bf_lo(x.a[e]) * lp0, ab1 = bf_hi(x.a[e]) * lp1;
           const float rb0 = bf_lo(x.r[e]) * lt0, rb1 = bf_hi(x.r[e]) * lt1;
-          const float bb0 = bf_lo(x.b[e]) * sfx0, bb1 = bf_hi(x.b[e]) * sfx1;
-          const float kb0 = bf_lo(x.k[e]) * sfx0, kb1 = bf_hi(x.k[e]) * sfx1;
           put2p(Ahat, kM64, kP64, t, j0, ab0 * inv0, ab1 * inv1);
           put2p(Rhat, kM64, kP64, t, j0, rb0 * inv0, rb1 * inv1);
-          put2p(Bbar, kM64, kP64, t, j0, bb0, bb1);
-          put2p(Kbar, kM64, kP64, t, j0, kb0, kb1);
           put2h(Abar, kP64, t, j0, ab0, ab1);
           put2h(Rbar, kP64, t, j0, rb0, rb1);
-          bt0[e] = bb0; bt1[e] = bb1; kt0[e] = kb0; kt1[e] = kb1;
-          vt0[e] = bf_lo(x.v[e]); vt1[e] = bf_hi(x.v[e]);
-          sfx0 *= w0[e]; sfx1 *= w1[e];
         }
-        put4h(BbT, kP32, j0, 4 * rg, f32x4{bt0[0], bt0[1], bt0[2], bt0[3]});
-        put4h(BbT, kP32, j0 + 1, 4 * rg, f32x4{bt1[0], bt1[1], bt1[2], bt1[3]});
-        put4h(KbT, kP32, j0, 4 * rg, f32x4{kt0[0], kt0[1], kt0[2], kt0[3]});
-        put4h(KbT, kP32, j0 + 1, 4 * rg, f32x4{kt1[0], kt1[1], kt1[2], kt1[3]});
-        put4h(Vt, kP32, j0, 4 * rg, f32x4{vt0[0], vt0[1], vt0[2], vt0[3]});
-        put4h(Vt, kP32, j0 + 1, 4 * rg, f32x4{vt1[0], vt1[1], vt1[2], vt1[3]});
         // next chunk's inputs, in flight from here on
         if (cK + 1 < nch)
           load_raw(x, p, t0K + kL, min(kL, len - (cK + 1) * kL), h, rg, jp);
       }
-      // B2. The range flags of chunk cK travel with B3: its Grams are built
-      // either way, and the value side reads them only if no flag was
-      // raised.
       __syncthreads();                                            // B2
       // ===== interval 2 =====
       float gmax = 0.f;
       if (k_on) {
-        // key: Gram matrix wv, tiles (tt, st) = (0,0), (1,0), (1,1) as C[s][t]
+        // Gram matrix W, tiles (tt, st) = (0,0), (1,0), (1,1) as C[s][t]
         const __bf16* Pm = (W & 1) ? Kbar : Bbar;
         const __bf16* Qm = (W >= 2) ? Rhat : Ahat;
         constexpr bool strict = W < 2;
@@ -673,7 +657,7 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
         }
         if (W == 0) {
           // A_ab in fp16 as [t][s] rows and as [s][t] rows (tile ti holds
-          // C[s][t] = A_ab[t][s])
+          // C[s][t] = A_ab[t][s]), read back below as T's operand fragments
           _Float16* ABr = AB;
           _Float16* ABt = ABr + kM32;
           ti = 0;
@@ -689,6 +673,29 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
                     static_cast<_Float16>(gt[ti][r]);
             }
           }
+          // T = [[D_0, 0], [T_10, D_1]], D_p = (I - A_pp)^-1, T_10 = D_1 A_10 D_0
+          const Frag D0 = inverse_unit_lower(ldh4(ABr, kP32, n16, 4 * g),
+                                             ldh4(ABt, kP32, n16, 4 * g), g, n16);
+          const Frag D1 = inverse_unit_lower(ldh4(ABr, kP32, 16 + n16, 16 + 4 * g),
+                                             ldh4(ABt, kP32, 16 + n16, 16 + 4 * g), g, n16);
+          // Y = A_10 D_0 needs row(A_10) and col(D_0) only
+          const f16x4 a10 = ldh4(ABr, kP32, 16 + n16, 4 * g);
+          Frag Y;
+          Y.fcol = mmh16(a10, D0.col, z);
+          Y.frow = mmh16(D0.col, a10, z);
+          Y.row = h4(Y.frow);
+          Y.col = h4(Y.fcol);
+          const Frag T10 = product(D1, Y);
+          // T out of the fp16 range takes the token-by-token path, as a
+          // Gram matrix out of range does
+          gmax = abs_max4(D0.frow, gmax);
+          gmax = abs_max4(D1.frow, gmax);
+          gmax = abs_max4(T10.frow, gmax);
+          // T as fp16 [t][s] rows, the operand fragments of its row tiles
+          put4h(TTk, kP32, n16, 4 * g, D0.frow);
+          put4h(TTk, kP32, n16, 16 + 4 * g, z);
+          put4h(TTk, kP32, 16 + n16, 4 * g, T10.frow);
+          put4h(TTk, kP32, 16 + n16, 16 + 4 * g, D1.frow);
         } else {
           _Float16* dst = LLk + (W - 1) * kM32;
           ti = 0;
@@ -704,28 +711,119 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
         }
       }
       if (cK + 1 < nch) prep(cK + 1);   // the next chunk
-      (void)barrier_or2(FLG + 8, wv, lane, k_on && bad_k,
+      (void)barrier_or2(FLG, wv, lane, k_on && bad_k,
                         k_on && !(gmax < kHalfSafe));             // B3
     }
   };
-  if (is_key) {
+
+  auto s_loop = [&](auto Wc) {
+    RawS x;
+    auto prep = [&](int c) {
+      if (len - c * kL < kL) pad_raw(x, len - c * kL, rg);   // the last chunk
+      if (zero_v) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x.v[e] = 0u;
+      }
+      decays(x.w);
+      TOT[rg * 64 + j0] = P0[3];
+      TOT[rg * 64 + j0 + 1] = P1[3];
+    };
+    load_raw(x, p, tok0, min(kL, len), h, rg, jp);
+    prep(0);
+    __syncthreads();                                              // TOT of chunk 0
+    for (int step = 0; step <= nch; ++step) {
+      const int cK = step;          // chunk whose operands are built
+      const bool k_on = cK < nch;
+      const int bK = cK & 1;
+      _Float16* VOk = reinterpret_cast<_Float16*>(lds + kOffVO + bK * kVOBytes);
+      const int t0K = tok0 + cK * kL;
+      // ===== interval 1 =====
+      bool bad_k = false;
+      if (k_on) {
+        const Dec d = chunk_decays(Wc);
+        if (rg == 0) { LAMb[bK * 64 + j0] = d.lam0; LAMb[bK * 64 + j0 + 1] = d.lam1; }
+        _Float16* BbT = VOk + 2 * kM64;
+        _Float16* KbT = BbT + kMT;
+        _Float16* Vt = KbT + kMT;
+        // range of the raw inputs (|Bbar| <= |b| etc. when every |w| <= 1)
+        uint32_t mx = 0u, mw = 0u;
+  #pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          mx = absmax_bits(mx, x.b[e]); mx = absmax_bits(mx, x.k[e]);
+          mx = absmax_bits(mx, x.v[e]); mw = absmax_bits(mw, x.w[e]);
+        }
+        bad_k = !(d.lam0 >= kMinLamL) || !(d.lam1 >= kMinLamL) ||
+                any_half_ge(mx, 0x4700u) ||     // |x| >= 2^15 (or NaN/Inf)
+                any_half_ge(mw, 0x3f81u);       // |w| > 1 (or NaN)
+        float sfx0 = d.suf0, sfx1 = d.suf1;
+        float bt0[4], bt1[4], kt0[4], kt1[4], vt0[4], vt1[4];
+  #pragma unroll
+        for (int e = 3; e >= 0; --e) {
+          const int t = 4 * rg + e;
+          const float bb0 = bf_lo(x.b[e]) * sfx0, bb1 = bf_hi(x.b[e]) * sfx1;
+          const float kb0 = bf_lo(x.k[e]) * sfx0, kb1 = bf_hi(x.k[e]) * sfx1;
+          put2p(Bbar, kM64, kP64, t, j0, bb0, bb1);
+          put2p(Kbar, kM64, kP64, t, j0, kb0, kb1);
+          bt0[e] = bb0; bt1[e] = bb1; kt0[e] = kb0; kt1[e] = kb1;
+          vt0[e] = bf_lo(x.v[e]); vt1[e] = bf_hi(x.v[e]);
+          sfx0 *= w0[e]; sfx1 *= w1[e];
+        }
+        put4h(BbT, kP32, j0, 4 * rg, f32x4{bt0[0], bt0[1], bt0[2], bt0[3]});
+        put4h(BbT, kP32, j0 + 1, 4 * rg, f32x4{bt1[0], bt1[1], bt1[2], bt1[3]});
+        put4h(KbT, kP32, j0, 4 * rg, f32x4{kt0[0], kt0[1], kt0[2], kt0[3]});
+        put4h(KbT, kP32, j0 + 1, 4 * rg, f32x4{kt1[0], kt1[1], kt1[2], kt1[3]});
+        put4h(Vt, kP32, j0, 4 * rg, f32x4{vt0[0], vt0[1], vt0[2], vt0[3]});
+        put4h(Vt, kP32, j0 + 1, 4 * rg, f32x4{vt1[0], vt1[1], vt1[2], vt1[3]});
+        // next chunk's inputs, in flight from here on
+        if (cK + 1 < nch)
+          load_raw(x, p, t0K + kL, min(kL, len - (cK + 1) * kL), h, rg, jp);
+      }
+      __syncthreads();                                            // B2
+      // ===== interval 2 =====
+      if (cK + 1 < nch) prep(cK + 1);   // the next chunk
+      (void)barrier_or2(FLG, wv, lane, k_on && bad_k, false);     // B3
+    }
+  };
+
+  if (role == 0) {
     switch (wv) {
-      case 0: key_loop(IntC<0>{}); break;
-      case 1: key_loop(IntC<1>{}); break;
-      case 2: key_loop(IntC<2>{}); break;
-      default: key_loop(IntC<3>{}); break;
+      case 0: t_loop(IntC<0>{}); break;
+      case 1: t_loop(IntC<1>{}); break;
+      case 2: t_loop(IntC<2>{}); break;
+      default: t_loop(IntC<3>{}); break;
+    }
+  } else if (role == 1) {
+    switch (wv) {
+      case 4: s_loop(IntC<0>{}); break;
+      case 5: s_loop(IntC<1>{}); break;
+      case 6: s_loop(IntC<2>{}); break;
+      default: s_loop(IntC<3>{}); break;
     }
   } else {
+    const size_t soff = static_cast<size_t>(16 * vb + n16) * kN + 4 * g;
+    f32x4 S[4] = {};   // S[jt][r] = S[i = 16 vb + n16][j = 16 jt + 4 g + r]
+    if (flags & kSegIdentity) {
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          S[jt][r] = (16 * vb + n16 == 16 * jt + 4 * g + r) ? 1.f : 0.f;
+    } else if (s_in) {
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt)   // global accesses (see gf32x4)
+        S[jt] = *(const gf32x4*)(s_in + soff + 16 * jt);
+    }
+    __syncthreads();                                              // TOT of chunk 0
     // fallback flags of chunk step - 1, known from the end of the step
     // before: early (its inputs or decays out of the fast path's range)
-    // and gram (its Gram matrices out of the fp16 range)
+    // and gram (its Gram matrices or T out of the fp16 range)
     bool early_prev = false, gram_prev = false;
     // The start state has arrived before the loop: without this wait the
     // compiler keeps S's registers pending from these loads and, at every
     // state update, waits for the step's output stores as well.
     __builtin_amdgcn_s_waitcnt(0x0F70);                // vmcnt(0)
     for (int step = 0; step <= nch; ++step) {
-      const int cV = step - 1;      // chunk whose T is built and value side run
+      const int cV = step - 1;      // chunk whose value side is run
       const bool v_on = cV >= 0;
       const int bV = cV & 1;
       const _Float16* VOv = reinterpret_cast<const _Float16*>(lds + kOffVO + bV * kVOBytes);
@@ -733,13 +831,13 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
       const int nV = min(kL, len - cV * kL);
       const int t0V = tok0 + cV * kL;
       // ===== interval 1 =====
-      // value side, first half: X and T of chunk cV (or the whole chunk exactly)
+      // value side, first half: X of chunk cV (or the whole chunk exactly)
       bool v_exact_done = false;
       float inv_s = 1.f;
-      f16x8 Sf0 = {}, Sf1 = {}, Vf = {}, Tf0 = {}, Tf1 = {};
+      f16x8 Sf0 = {}, Sf1 = {}, Vf = {};
       f32x4 X[2] = {z, z};
       if (v_on) {
-        bool exact = early_prev || gram_prev;
+        const bool exact = early_prev || gram_prev;
         if (!exact) {
           const _Float16* Abar = VOv;
           const _Float16* Vt = VOv + 2 * kM64 + 2 * kMT;
@@ -759,33 +857,6 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
   #pragma unroll
             for (int r = 0; r < 4; ++r) X[tt][r] = fmaf(cs[r], inv_s, cv[r]);
           }
-          // T = [[D_0, 0], [T_10, D_1]], D_p = (I - A_pp)^-1, T_10 = D_1 A_10 D_0
-          const _Float16* ABr = AB;
-          const _Float16* ABt = ABr + kM32;
-          const Frag D0 = inverse_unit_lower(ldh4(ABr, kP32, n16, 4 * g),
-                                             ldh4(ABt, kP32, n16, 4 * g), g, n16);
-          const Frag D1 = inverse_unit_lower(ldh4(ABr, kP32, 16 + n16, 16 + 4 * g),
-                                             ldh4(ABt, kP32, 16 + n16, 16 + 4 * g), g, n16);
-          // Y = A_10 D_0 needs row(A_10) and col(D_0) only
-          const f16x4 a10 = ldh4(ABr, kP32, 16 + n16, 4 * g);
-          Frag Y;
-          Y.fcol = mmh16(a10, D0.col, z);
-          Y.frow = mmh16(D0.col, a10, z);
-          Y.row = h4(Y.frow);
-          Y.col = h4(Y.fcol);
-          const Frag T10 = product(D1, Y);
-          float tm = abs_max4(D0.frow, 0.f);
-          tm = abs_max4(D1.frow, tm);
-          tm = abs_max4(T10.frow, tm);
-          // operand fragments of T's row tiles: k in [0,16) then [16,32)
-  #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            Tf0[r] = static_cast<_Float16>(D0.frow[r]);
-            Tf0[4 + r] = static_cast<_Float16>(0.f);
-            Tf1[r] = static_cast<_Float16>(T10.frow[r]);
-            Tf1[4 + r] = static_cast<_Float16>(D1.frow[r]);
-          }
-          exact = !(wave_max(tm) < kHalfSafe);   // T out of fp16 range
         }
         if (exact) {
           // the whole chunk token by token
@@ -803,6 +874,39 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
         const _Float16* Mrb = LLv + kM32;
         const _Float16* Mrk = LLv + 2 * kM32;
         const float* lam = LAMb + bV * 64;
+        const _Float16* TTv = reinterpret_cast<const _Float16*>(lds + kOffTT) + bV * kM32;
+        // Every LDS operand of the step's products is read first, and the
+        // products that do not involve U are issued before X and U are
+        // scaled, so that the LDS reads and those products overlap the two
+        // wavefront reductions instead of waiting one by one. Each sum is
+        // formed in the same order as when computed term by term.
+        f16x8 rb[2][2], mb[2], mk[2], bt[4], kt[4];
+        f32x4 lm[4];
+        // operand fragments of T's row tiles: k in [0,16) then [16,32)
+        const f16x8 Tf0 = ldh8(TTv, kP32, n16, 0, g);
+        const f16x8 Tf1 = ldh8(TTv, kP32, 16 + n16, 0, g);
+  #pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          rb[tt][0] = ldh8(Rbar, kP64, 16 * tt + n16, 0, g);
+          rb[tt][1] = ldh8(Rbar, kP64, 16 * tt + n16, 32, g);
+          mk[tt] = ldh8(Mrk, kP32, 16 * tt + n16, 0, g);
+          mb[tt] = ldh8(Mrb, kP32, 16 * tt + n16, 0, g);
+        }
+  #pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+          kt[jt] = ldh8(KbT, kP32, 16 * jt + n16, 0, g);
+          bt[jt] = ldh8(BbT, kP32, 16 * jt + n16, 0, g);
+          lm[jt] = *reinterpret_cast<const f32x4*>(lam + 16 * jt + 4 * g);
+        }
+        f32x4 cs[2], cvo[2], cvs[4];
+  #pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          cs[tt] = mmah(Sf0, rb[tt][0], z);
+          cs[tt] = mmah(Sf1, rb[tt][1], cs[tt]);
+          cvo[tt] = mmah(Vf, mk[tt], z);
+        }
+  #pragma unroll
+        for (int jt = 0; jt < 4; ++jt) cvs[jt] = mmah(kt[jt], Vf, z);
         float inv_x;
         const float sX = pow2_scale(wave_max(scale_max4(X[1], scale_max4(X[0], 0.f))), &inv_x);
         const f16x8 Xf = frag8h(X[0], X[1], sX);
@@ -815,32 +919,27 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
         const f16x8 Uf = frag8h(U[0], U[1], sU);
   #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-          f32x4 cs = mmah(Sf0, ldh8(Rbar, kP64, 16 * tt + n16, 0, g), z);
-          cs = mmah(Sf1, ldh8(Rbar, kP64, 16 * tt + n16, 32, g), cs);
-          const f32x4 cu = mmah(Uf, ldh8(Mrb, kP32, 16 * tt + n16, 0, g), z);
-          const f32x4 cv = mmah(Vf, ldh8(Mrk, kP32, 16 * tt + n16, 0, g), z);
+          const f32x4 cu = mmah(Uf, mb[tt], z);
           const int t = 16 * tt + n16;
           if (t < nV && !no_out) {
             float4 ov;
-            ov.x = fmaf(cs[0], inv_s, fmaf(cu[0], inv_ux, cv[0]));
-            ov.y = fmaf(cs[1], inv_s, fmaf(cu[1], inv_ux, cv[1]));
-            ov.z = fmaf(cs[2], inv_s, fmaf(cu[2], inv_ux, cv[2]));
-            ov.w = fmaf(cs[3], inv_s, fmaf(cu[3], inv_ux, cv[3]));
+            ov.x = fmaf(cs[tt][0], inv_s, fmaf(cu[0], inv_ux, cvo[tt][0]));
+            ov.y = fmaf(cs[tt][1], inv_s, fmaf(cu[1], inv_ux, cvo[tt][1]));
+            ov.z = fmaf(cs[tt][2], inv_s, fmaf(cu[2], inv_ux, cvo[tt][2]));
+            ov.w = fmaf(cs[tt][3], inv_s, fmaf(cu[3], inv_ux, cvo[tt][3]));
             *reinterpret_cast<float4*>(p.o + static_cast<size_t>(t0V + t) * rowstride
                                        + static_cast<size_t>(h) * kN + 16 * vb + 4 * g) = ov;
           }
         }
   #pragma unroll
         for (int jt = 0; jt < 4; ++jt) {
-          const f32x4 cu = mmah(ldh8(BbT, kP32, 16 * jt + n16, 0, g), Uf, z);
-          const f32x4 cv = mmah(ldh8(KbT, kP32, 16 * jt + n16, 0, g), Vf, z);
+          const f32x4 cu = mmah(bt[jt], Uf, z);
   #pragma unroll
           for (int r = 0; r < 4; ++r)
-            S[jt][r] = fmaf(lam[16 * jt + 4 * g + r], S[jt][r],
-                            fmaf(cu[r], inv_ux, cv[r]));
+            S[jt][r] = fmaf(lm[jt][r], S[jt][r], fmaf(cu[r], inv_ux, cvs[jt][r]));
         }
       }
-      const uint32_t f3 = barrier_or2(FLG + 8, wv, lane, false, false);  // B3
+      const uint32_t f3 = barrier_or2(FLG, wv, lane, false, false);  // B3
       early_prev = (f3 & 1u) != 0;
       gram_prev = (f3 & 2u) != 0;
     }
@@ -861,7 +960,7 @@ hipError_t launch_chunked_p(const SeqArgs& args, hipStream_t stream,
                          chunk_decode_blocks(n_dec, args.H);
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(chunk_p_kernel<false>, dim3(static_cast<unsigned>(blocks)),
-                     dim3(512), 0, stream, args, nullptr, dec, n_dec);
+                     dim3(64 * kChunkPWaves), 0, stream, args, nullptr, dec, n_dec);
   return hipGetLastError();
 }
 
@@ -873,7 +972,7 @@ hipError_t launch_chunked_p_seg(const SeqArgs& args, const SegItem* segs,
                          chunk_decode_blocks(n_dec, args.H);
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(chunk_p_kernel<true>, dim3(static_cast<unsigned>(blocks)),
-                     dim3(512), 0, stream, args, segs, dec, n_dec);
+                     dim3(64 * kChunkPWaves), 0, stream, args, segs, dec, n_dec);
   return hipGetLastError();
 }
 
