@@ -82,8 +82,11 @@ constexpr int kOffVO = kOffTOT + 8 * 64 * 4;               // 2 buffers
 constexpr int kLLBytes = 3 * kM32 * 2;
 constexpr int kOffLL = kOffVO + 2 * kVOBytes;              // 2 buffers
 constexpr int kOffLAM = kOffLL + 2 * kLLBytes;             // fp32 [2][64]
-constexpr int kOffTT = kOffLAM + 2 * 64 * 4;               // fp16 T [32][32], 2 buffers
-constexpr int kOffFLG = kOffTT + 2 * kM32 * 2;             // u32 [16]
+constexpr int kOffTT = kOffLAM + 2 * 64 * 4;               // fp16 T [32][32]
+constexpr int kOffYC = kOffTT + kM32 * 2;                  // fp16x4 [64]: col(Y)
+constexpr int kOffD1R = kOffYC + 64 * 8;                   // fp16x4 [64]: row(D_1)
+constexpr int kOffTFL = kOffD1R + 64 * 8;                  // u32 [2]: D_0, D_1 range
+constexpr int kOffFLG = kOffTFL + 2 * 4;                   // u32 [16]
 constexpr int kLdsBytes = kOffFLG + 16 * 4;
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 
@@ -477,6 +480,10 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
   float* TOT = reinterpret_cast<float*>(lds + kOffTOT);
   float* LAMb = reinterpret_cast<float*>(lds + kOffLAM);
   uint32_t* FLG = reinterpret_cast<uint32_t*>(lds + kOffFLG);
+  _Float16* TT = reinterpret_cast<_Float16*>(lds + kOffTT);       // T [t][s]
+  _Float16* YC = reinterpret_cast<_Float16*>(lds + kOffYC);
+  _Float16* D1R = reinterpret_cast<_Float16*>(lds + kOffD1R);
+  uint32_t* TFL = reinterpret_cast<uint32_t*>(lds + kOffTFL);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -587,7 +594,6 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
       const int bK = cK & 1;
       _Float16* VOk = reinterpret_cast<_Float16*>(lds + kOffVO + bK * kVOBytes);
       _Float16* LLk = reinterpret_cast<_Float16*>(lds + kOffLL + bK * kLLBytes);
-      _Float16* TTk = reinterpret_cast<_Float16*>(lds + kOffTT) + bK * kM32;
       const int t0K = tok0 + cK * kL;
       // ===== interval 1 =====
       bool bad_k = false;
@@ -657,7 +663,8 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
         }
         if (W == 0) {
           // A_ab in fp16 as [t][s] rows and as [s][t] rows (tile ti holds
-          // C[s][t] = A_ab[t][s]), read back below as T's operand fragments
+          // C[s][t] = A_ab[t][s]): T's operand fragments, read by the value
+          // side in the next step
           _Float16* ABr = AB;
           _Float16* ABt = ABr + kM32;
           ti = 0;
@@ -673,29 +680,6 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
                     static_cast<_Float16>(gt[ti][r]);
             }
           }
-          // T = [[D_0, 0], [T_10, D_1]], D_p = (I - A_pp)^-1, T_10 = D_1 A_10 D_0
-          const Frag D0 = inverse_unit_lower(ldh4(ABr, kP32, n16, 4 * g),
-                                             ldh4(ABt, kP32, n16, 4 * g), g, n16);
-          const Frag D1 = inverse_unit_lower(ldh4(ABr, kP32, 16 + n16, 16 + 4 * g),
-                                             ldh4(ABt, kP32, 16 + n16, 16 + 4 * g), g, n16);
-          // Y = A_10 D_0 needs row(A_10) and col(D_0) only
-          const f16x4 a10 = ldh4(ABr, kP32, 16 + n16, 4 * g);
-          Frag Y;
-          Y.fcol = mmh16(a10, D0.col, z);
-          Y.frow = mmh16(D0.col, a10, z);
-          Y.row = h4(Y.frow);
-          Y.col = h4(Y.fcol);
-          const Frag T10 = product(D1, Y);
-          // T out of the fp16 range takes the token-by-token path, as a
-          // Gram matrix out of range does
-          gmax = abs_max4(D0.frow, gmax);
-          gmax = abs_max4(D1.frow, gmax);
-          gmax = abs_max4(T10.frow, gmax);
-          // T as fp16 [t][s] rows, the operand fragments of its row tiles
-          put4h(TTk, kP32, n16, 4 * g, D0.frow);
-          put4h(TTk, kP32, n16, 16 + 4 * g, z);
-          put4h(TTk, kP32, 16 + n16, 4 * g, T10.frow);
-          put4h(TTk, kP32, 16 + n16, 16 + 4 * g, D1.frow);
         } else {
           _Float16* dst = LLk + (W - 1) * kM32;
           ti = 0;
@@ -774,13 +758,18 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
         put4h(KbT, kP32, j0 + 1, 4 * rg, f32x4{kt1[0], kt1[1], kt1[2], kt1[3]});
         put4h(Vt, kP32, j0, 4 * rg, f32x4{vt0[0], vt0[1], vt0[2], vt0[3]});
         put4h(Vt, kP32, j0 + 1, 4 * rg, f32x4{vt1[0], vt1[1], vt1[2], vt1[3]});
-        // next chunk's inputs, in flight from here on
-        if (cK + 1 < nch)
-          load_raw(x, p, t0K + kL, min(kL, len - (cK + 1) * kL), h, rg, jp);
       }
       __syncthreads();                                            // B2
       // ===== interval 2 =====
-      if (cK + 1 < nch) prep(cK + 1);   // the next chunk
+      // The next chunk's inputs are loaded here rather than with the t
+      // wavefronts' at the end of the first interval, so that the two
+      // roles' loads do not queue at once and the first interval, which
+      // this role sets, is shorter; the second interval, set by the value
+      // side, leaves them time.
+      if (cK + 1 < nch) {
+        load_raw(x, p, t0K + kL, min(kL, len - (cK + 1) * kL), h, rg, jp);
+        prep(cK + 1);
+      }
       (void)barrier_or2(FLG, wv, lane, k_on && bad_k, false);     // B3
     }
   };
@@ -800,6 +789,10 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
       default: s_loop(IntC<3>{}); break;
     }
   } else {
+    // The value wavefronts carry the chunk-to-chunk chain; the key
+    // wavefronts on the same SIMDs have slack at the barriers. Issue
+    // priority goes to the value wavefronts.
+    __builtin_amdgcn_s_setprio(3);
     const size_t soff = static_cast<size_t>(16 * vb + n16) * kN + 4 * g;
     f32x4 S[4] = {};   // S[jt][r] = S[i = 16 vb + n16][j = 16 jt + 4 g + r]
     if (flags & kSegIdentity) {
@@ -857,6 +850,31 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
   #pragma unroll
             for (int r = 0; r < 4; ++r) X[tt][r] = fmaf(cs[r], inv_s, cv[r]);
           }
+          // T = [[D_0, 0], [T_10, D_1]], D_p = (I - A_pp)^-1, T_10 = D_1 A_10 D_0,
+          // from A_ab of chunk cV: value wavefront 0 computes D_0 and
+          // Y = A_10 D_0, wavefront 1 computes D_1, each value wavefront then
+          // T_10 = D_1 Y in the second interval. Each posts whether its
+          // part left the fp16 range.
+          const _Float16* ABr = AB;
+          const _Float16* ABt = ABr + kM32;
+          if (vb == 0) {
+            const Frag D0 = inverse_unit_lower(ldh4(ABr, kP32, n16, 4 * g),
+                                               ldh4(ABt, kP32, n16, 4 * g), g, n16);
+            // col(Y) = A_10 D_0 from row(A_10) and col(D_0)
+            const f16x4 ycol = h4(mmh16(ldh4(ABr, kP32, 16 + n16, 4 * g), D0.col, z));
+            put4h(TT, kP32, n16, 4 * g, D0.frow);
+            put4h(TT, kP32, n16, 16 + 4 * g, z);
+            *reinterpret_cast<f16x4*>(YC + 4 * lane) = ycol;
+            const bool out = __builtin_amdgcn_ballot_w64(!(abs_max4(D0.frow, 0.f) < kHalfSafe)) != 0;
+            if (lane == 0) TFL[0] = out ? 1u : 0u;
+          } else if (vb == 1) {
+            const Frag D1 = inverse_unit_lower(ldh4(ABr, kP32, 16 + n16, 16 + 4 * g),
+                                               ldh4(ABt, kP32, 16 + n16, 16 + 4 * g), g, n16);
+            put4h(TT, kP32, 16 + n16, 16 + 4 * g, D1.frow);
+            *reinterpret_cast<f16x4*>(D1R + 4 * lane) = D1.row;
+            const bool out = __builtin_amdgcn_ballot_w64(!(abs_max4(D1.frow, 0.f) < kHalfSafe)) != 0;
+            if (lane == 0) TFL[1] = out ? 1u : 0u;
+          }
         }
         if (exact) {
           // the whole chunk token by token
@@ -866,7 +884,19 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
       }
       __syncthreads();                                            // B2
       // ===== interval 2 =====
+      bool t_exact = false;
+      f32x4 t10 = z;
       if (v_on && !v_exact_done) {
+        t10 = mmh16(*reinterpret_cast<const f16x4*>(YC + 4 * lane),
+                    *reinterpret_cast<const f16x4*>(D1R + 4 * lane), z);
+        t_exact = (TFL[0] | TFL[1]) != 0 ||
+                  __builtin_amdgcn_ballot_w64(!(abs_max4(t10, 0.f) < kHalfSafe)) != 0;
+        if (t_exact) {
+          // T out of the fp16 range: the whole chunk token by token
+          exact_chunk(p, S, t0V, nV, h, vb, g, n16, zero_v, no_out);
+        }
+      }
+      if (v_on && !v_exact_done && !t_exact) {
         // value side, second half: U, O, state update of chunk cV
         const _Float16* Rbar = VOv + kM64;
         const _Float16* BbT = VOv + 2 * kM64;
@@ -874,7 +904,6 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
         const _Float16* Mrb = LLv + kM32;
         const _Float16* Mrk = LLv + 2 * kM32;
         const float* lam = LAMb + bV * 64;
-        const _Float16* TTv = reinterpret_cast<const _Float16*>(lds + kOffTT) + bV * kM32;
         // Every LDS operand of the step's products is read first, and the
         // products that do not involve U are issued before X and U are
         // scaled, so that the LDS reads and those products overlap the two
@@ -883,8 +912,14 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
         f16x8 rb[2][2], mb[2], mk[2], bt[4], kt[4];
         f32x4 lm[4];
         // operand fragments of T's row tiles: k in [0,16) then [16,32)
-        const f16x8 Tf0 = ldh8(TTv, kP32, n16, 0, g);
-        const f16x8 Tf1 = ldh8(TTv, kP32, 16 + n16, 0, g);
+        const f16x8 Tf0 = ldh8(TT, kP32, n16, 0, g);
+        f16x8 Tf1;
+        {
+          const f16x4 t10h = h4(t10);
+          const f16x4 d1 = ldh4(TT, kP32, 16 + n16, 16 + 4 * g);
+  #pragma unroll
+          for (int r = 0; r < 4; ++r) { Tf1[r] = t10h[r]; Tf1[4 + r] = d1[r]; }
+        }
   #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
           rb[tt][0] = ldh8(Rbar, kP64, 16 * tt + n16, 0, g);
