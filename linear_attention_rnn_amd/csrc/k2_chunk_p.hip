@@ -257,14 +257,25 @@ __device__ __forceinline__ float abs_max4(f32x4 x, float m) {
 }
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-// per-half max of |bf16| bit patterns (sign cleared); NaN/Inf sort highest
-__device__ __forceinline__ uint32_t absmax_bits(uint32_t m, uint32_t x) {
-  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(
-      __builtin_bit_cast(u16x2, m), __builtin_bit_cast(u16x2, x & 0x7fff7fffu)));
+// per-half max of |bf16| bit patterns (sign cleared; NaN/Inf sort highest)
+// over n words, as a tree of depth log2(n): the masked words are
+// independent
+template <int n>
+__device__ __forceinline__ uint32_t absmax_tree(const uint32_t* x) {
+  uint32_t m[n];
+#pragma unroll
+  for (int u = 0; u < n; ++u) m[u] = x[u] & 0x7fff7fffu;
+#pragma unroll
+  for (int w = 1; w < n; w *= 2)
+#pragma unroll
+    for (int u = 0; u + w < n; u += 2 * w)
+      m[u] = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(
+          __builtin_bit_cast(u16x2, m[u]), __builtin_bit_cast(u16x2, m[u + w])));
+  return m[0];
 }
 // true if either half of a per-half max of bf16 bit patterns is >= limit
 __device__ __forceinline__ bool any_half_ge(uint32_t m, uint32_t limit) {
-  return (m & 0xffffu) >= limit || (m >> 16) >= limit;
+  return ((m & 0xffffu) >= limit) | ((m >> 16) >= limit);
 }
 
 // raw inputs of a key thread, rows 4 rg + e (e < 4), channels 2 jp, 2 jp + 1:
@@ -520,6 +531,9 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
     s_out = p.pool + (static_cast<size_t>(it.slot) * p.H + h) * (kN * kN);
     s_in = s_out;
   }
+  // Every item holds at least one token (the host drops empty sequences,
+  // and segments are never empty); the clamped loads rely on it.
+  if (len <= 0) return;
   const bool zero_v = (flags & kSegZeroV) != 0;
   const bool no_out = (flags & kSegNoOut) != 0;
   const int nch = (len + kL - 1) / kL;
@@ -545,6 +559,14 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
   // second interval. The third barrier orders the TOT writes before their
   // reads. Each loop is instantiated once per wavefront W (= wv & 3): its
   // row groups, Gram matrix and LDS destinations are then constants.
+  // The next chunk's loads and preparation happen on every path, with the
+  // chunk index clamped to the last one (whose totals no step then reads):
+  // a load under a branch leaves the raw registers to be merged at its
+  // end, and the copies that merge them wait for the loads.
+  auto load_next = [&](auto& x, int c) {
+    const int cl = min(c + 1, nch - 1);
+    load_raw(x, p, tok0 + cl * kL, min(kL, len - cl * kL), h, rg, jp);
+  };
   float w0[4], w1[4], P0[4], P1[4];
   auto decays = [&](const uint32_t (&wr)[4]) {
 #pragma unroll
@@ -607,12 +629,9 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
         _Float16* Rbar = VOk + kM64;
         // range of the raw inputs (|Abar| <= |a| etc. when every |w| <= 1;
         // w and lam are checked on the s side)
-        uint32_t mx = 0u;
-  #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          mx = absmax_bits(mx, x.a[e]); mx = absmax_bits(mx, x.r[e]);
-        }
-        bad_k = any_half_ge(mx, 0x4700u);     // |x| >= 2^15 (or NaN/Inf)
+        const uint32_t xs[8] = {x.a[0], x.a[1], x.a[2], x.a[3],
+                                x.r[0], x.r[1], x.r[2], x.r[3]};
+        bad_k = any_half_ge(absmax_tree<8>(xs), 0x4700u);   // |x| >= 2^15 (or NaN/Inf)
   #pragma unroll
         for (int e = 3; e >= 0; --e) {
           const int t = 4 * rg + e;
@@ -626,11 +645,14 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
           put2h(Abar, kP64, t, j0, ab0, ab1);
           put2h(Rbar, kP64, t, j0, rb0, rb1);
         }
-        // next chunk's inputs, in flight from here on
-        if (cK + 1 < nch)
-          load_raw(x, p, t0K + kL, min(kL, len - (cK + 1) * kL), h, rg, jp);
       }
+      // next chunk's inputs, in flight from here on
+      load_next(x, cK);
+      // no code moves across: work of the second interval hoisted above
+      // the barrier would wait there for the loads just issued
+      __builtin_amdgcn_sched_barrier(0);
       __syncthreads();                                            // B2
+      __builtin_amdgcn_sched_barrier(0);
       // ===== interval 2 =====
       float gmax = 0.f;
       if (k_on) {
@@ -694,7 +716,7 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
           put4h(dst, kP32, n16, 16 + 4 * g, z);
         }
       }
-      if (cK + 1 < nch) prep(cK + 1);   // the next chunk
+      prep(min(cK + 1, nch - 1));   // the next chunk
       (void)barrier_or2(FLG, wv, lane, k_on && bad_k,
                         k_on && !(gmax < kHalfSafe));             // B3
     }
@@ -730,15 +752,12 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
         _Float16* KbT = BbT + kMT;
         _Float16* Vt = KbT + kMT;
         // range of the raw inputs (|Bbar| <= |b| etc. when every |w| <= 1)
-        uint32_t mx = 0u, mw = 0u;
-  #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          mx = absmax_bits(mx, x.b[e]); mx = absmax_bits(mx, x.k[e]);
-          mx = absmax_bits(mx, x.v[e]); mw = absmax_bits(mw, x.w[e]);
-        }
-        bad_k = !(d.lam0 >= kMinLamL) || !(d.lam1 >= kMinLamL) ||
-                any_half_ge(mx, 0x4700u) ||     // |x| >= 2^15 (or NaN/Inf)
-                any_half_ge(mw, 0x3f81u);       // |w| > 1 (or NaN)
+        const uint32_t xs[12] = {x.b[0], x.b[1], x.b[2], x.b[3], x.k[0], x.k[1],
+                                 x.k[2], x.k[3], x.v[0], x.v[1], x.v[2], x.v[3]};
+        // bitwise, not short-circuit: no branches
+        bad_k = !(d.lam0 >= kMinLamL) | !(d.lam1 >= kMinLamL) |
+                any_half_ge(absmax_tree<12>(xs), 0x4700u) |   // |x| >= 2^15 (or NaN/Inf)
+                any_half_ge(absmax_tree<4>(x.w), 0x3f81u);    // |w| > 1 (or NaN)
         float sfx0 = d.suf0, sfx1 = d.suf1;
         float bt0[4], bt1[4], kt0[4], kt1[4], vt0[4], vt1[4];
   #pragma unroll
@@ -759,17 +778,19 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
         put4h(Vt, kP32, j0, 4 * rg, f32x4{vt0[0], vt0[1], vt0[2], vt0[3]});
         put4h(Vt, kP32, j0 + 1, 4 * rg, f32x4{vt1[0], vt1[1], vt1[2], vt1[3]});
       }
+      // no code moves across: work of the second interval hoisted above
+      // the barrier would wait there for the loads just issued
+      __builtin_amdgcn_sched_barrier(0);
       __syncthreads();                                            // B2
+      __builtin_amdgcn_sched_barrier(0);
       // ===== interval 2 =====
       // The next chunk's inputs are loaded here rather than with the t
       // wavefronts' at the end of the first interval, so that the two
       // roles' loads do not queue at once and the first interval, which
       // this role sets, is shorter; the second interval, set by the value
       // side, leaves them time.
-      if (cK + 1 < nch) {
-        load_raw(x, p, t0K + kL, min(kL, len - (cK + 1) * kL), h, rg, jp);
-        prep(cK + 1);
-      }
+      load_next(x, cK);
+      prep(min(cK + 1, nch - 1));
       (void)barrier_or2(FLG, wv, lane, k_on && bad_k, false);     // B3
     }
   };
