@@ -724,17 +724,33 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
 
   auto s_loop = [&](auto Wc) {
     RawS x;
+    // The s wavefronts load a chunk's w at the start of the first interval
+    // of the step before its preparation (the build uses the decays
+    // prepared from it, not x.w), and its k, b and v at the start of the
+    // second interval: the preparation, which waits for w only, then needs
+    // no load issued in the same interval.
+    auto load_w = [&](int c) {
+      const int cl = min(c, nch - 1);
+      uint32_t (*const dst[1])[4] = {&x.w};
+      const void* const src[1] = {p.w};
+      load_rows<1>(dst, src, p, tok0 + cl * kL, min(kL, len - cl * kL), h, rg, jp);
+    };
+    auto load_kbv = [&](int c) {
+      const int cl = min(c, nch - 1);
+      uint32_t (*const dst[3])[4] = {&x.k, &x.b, &x.v};
+      const void* const src[3] = {p.k, p.b, p.v};
+      load_rows<3>(dst, src, p, tok0 + cl * kL, min(kL, len - cl * kL), h, rg, jp);
+    };
+    bool bad_w = false;   // |w| > 1 (or NaN) in the prepared chunk
     auto prep = [&](int c) {
       if (len - c * kL < kL) pad_raw(x, len - c * kL, rg);   // the last chunk
-      if (zero_v) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x.v[e] = 0u;
-      }
+      bad_w = any_half_ge(absmax_tree<4>(x.w), 0x3f81u);
       decays(x.w);
       TOT[rg * 64 + j0] = P0[3];
       TOT[rg * 64 + j0 + 1] = P1[3];
     };
-    load_raw(x, p, tok0, min(kL, len), h, rg, jp);
+    load_w(0);
+    load_kbv(0);
     prep(0);
     __syncthreads();                                              // TOT of chunk 0
     for (int step = 0; step <= nch; ++step) {
@@ -742,33 +758,56 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
       const bool k_on = cK < nch;
       const int bK = cK & 1;
       _Float16* VOk = reinterpret_cast<_Float16*>(lds + kOffVO + bK * kVOBytes);
-      const int t0K = tok0 + cK * kL;
       // ===== interval 1 =====
+      load_w(cK + 1);
       bool bad_k = false;
+      float suf0 = 0.f, suf1 = 0.f;
       if (k_on) {
         const Dec d = chunk_decays(Wc);
+        suf0 = d.suf0;
+        suf1 = d.suf1;
         if (rg == 0) { LAMb[bK * 64 + j0] = d.lam0; LAMb[bK * 64 + j0 + 1] = d.lam1; }
-        _Float16* BbT = VOk + 2 * kM64;
-        _Float16* KbT = BbT + kMT;
-        _Float16* Vt = KbT + kMT;
-        // range of the raw inputs (|Bbar| <= |b| etc. when every |w| <= 1)
+        // range of the raw inputs (|Bbar| <= |b| etc. when every |w| <= 1);
+        // v is zero on a run with kSegZeroV
+        const uint32_t v0m = zero_v ? 0u : x.v[0], v1m = zero_v ? 0u : x.v[1];
+        const uint32_t v2m = zero_v ? 0u : x.v[2], v3m = zero_v ? 0u : x.v[3];
         const uint32_t xs[12] = {x.b[0], x.b[1], x.b[2], x.b[3], x.k[0], x.k[1],
-                                 x.k[2], x.k[3], x.v[0], x.v[1], x.v[2], x.v[3]};
+                                 x.k[2], x.k[3], v0m, v1m, v2m, v3m};
         // bitwise, not short-circuit: no branches
         bad_k = !(d.lam0 >= kMinLamL) | !(d.lam1 >= kMinLamL) |
                 any_half_ge(absmax_tree<12>(xs), 0x4700u) |   // |x| >= 2^15 (or NaN/Inf)
-                any_half_ge(absmax_tree<4>(x.w), 0x3f81u);    // |w| > 1 (or NaN)
+                bad_w;
+        // the Gram operands, read after the second barrier
         float sfx0 = d.suf0, sfx1 = d.suf1;
-        float bt0[4], bt1[4], kt0[4], kt1[4], vt0[4], vt1[4];
   #pragma unroll
         for (int e = 3; e >= 0; --e) {
           const int t = 4 * rg + e;
-          const float bb0 = bf_lo(x.b[e]) * sfx0, bb1 = bf_hi(x.b[e]) * sfx1;
-          const float kb0 = bf_lo(x.k[e]) * sfx0, kb1 = bf_hi(x.k[e]) * sfx1;
-          put2p(Bbar, kM64, kP64, t, j0, bb0, bb1);
-          put2p(Kbar, kM64, kP64, t, j0, kb0, kb1);
-          bt0[e] = bb0; bt1[e] = bb1; kt0[e] = kb0; kt1[e] = kb1;
-          vt0[e] = bf_lo(x.v[e]); vt1[e] = bf_hi(x.v[e]);
+          put2p(Bbar, kM64, kP64, t, j0, bf_lo(x.b[e]) * sfx0, bf_hi(x.b[e]) * sfx1);
+          put2p(Kbar, kM64, kP64, t, j0, bf_lo(x.k[e]) * sfx0, bf_hi(x.k[e]) * sfx1);
+          sfx0 *= w0[e]; sfx1 *= w1[e];
+        }
+      }
+      // no code moves across: work of the second interval hoisted above
+      // the barrier would wait there for loads
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();                                            // B2
+      __builtin_amdgcn_sched_barrier(0);
+      // ===== interval 2 =====
+      if (k_on) {
+        // the value side's operands, read in the next step: built here,
+        // where this role waits on the value side anyway, from the same
+        // products as the Gram operands (the same values)
+        _Float16* BbT = VOk + 2 * kM64;
+        _Float16* KbT = BbT + kMT;
+        _Float16* Vt = KbT + kMT;
+        float sfx0 = suf0, sfx1 = suf1;
+        float bt0[4], bt1[4], kt0[4], kt1[4], vt0[4], vt1[4];
+  #pragma unroll
+        for (int e = 3; e >= 0; --e) {
+          bt0[e] = bf_lo(x.b[e]) * sfx0; bt1[e] = bf_hi(x.b[e]) * sfx1;
+          kt0[e] = bf_lo(x.k[e]) * sfx0; kt1[e] = bf_hi(x.k[e]) * sfx1;
+          vt0[e] = zero_v ? 0.f : bf_lo(x.v[e]);
+          vt1[e] = zero_v ? 0.f : bf_hi(x.v[e]);
           sfx0 *= w0[e]; sfx1 *= w1[e];
         }
         put4h(BbT, kP32, j0, 4 * rg, f32x4{bt0[0], bt0[1], bt0[2], bt0[3]});
@@ -778,19 +817,8 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
         put4h(Vt, kP32, j0, 4 * rg, f32x4{vt0[0], vt0[1], vt0[2], vt0[3]});
         put4h(Vt, kP32, j0 + 1, 4 * rg, f32x4{vt1[0], vt1[1], vt1[2], vt1[3]});
       }
-      // no code moves across: work of the second interval hoisted above
-      // the barrier would wait there for the loads just issued
-      __builtin_amdgcn_sched_barrier(0);
-      __syncthreads();                                            // B2
-      __builtin_amdgcn_sched_barrier(0);
-      // ===== interval 2 =====
-      // The next chunk's inputs are loaded here rather than with the t
-      // wavefronts' at the end of the first interval, so that the two
-      // roles' loads do not queue at once and the first interval, which
-      // this role sets, is shorter; the second interval, set by the value
-      // side, leaves them time.
-      load_next(x, cK);
-      prep(min(cK + 1, nch - 1));
+      load_kbv(cK + 1);
+      prep(min(cK + 1, nch - 1));   // the next chunk
       (void)barrier_or2(FLG, wv, lane, k_on && bad_k, false);     // B3
     }
   };
@@ -848,11 +876,12 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
       // value side, first half: X of chunk cV (or the whole chunk exactly)
       bool v_exact_done = false;
       float inv_s = 1.f;
-      f16x8 Sf0 = {}, Sf1 = {}, Vf = {};
-      f32x4 X[2] = {z, z};
+      f16x8 Sf0 = {}, Sf1 = {}, Vf = {}, Xf = {};
+      float inv_x = 1.f;
       if (v_on) {
         const bool exact = early_prev || gram_prev;
         if (!exact) {
+          f32x4 X[2];
           const _Float16* Abar = VOv;
           const _Float16* Vt = VOv + 2 * kM64 + 2 * kMT;
           const _Float16* Aak = LLv;
@@ -871,6 +900,10 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
   #pragma unroll
             for (int r = 0; r < 4; ++r) X[tt][r] = fmaf(cs[r], inv_s, cv[r]);
           }
+          // X scaled into the fp16 range here, where the value side has
+          // slack, so that the second interval starts with U
+          const float sX = pow2_scale(wave_max(scale_max4(X[1], scale_max4(X[0], 0.f))), &inv_x);
+          Xf = frag8h(X[0], X[1], sX);
           // T = [[D_0, 0], [T_10, D_1]], D_p = (I - A_pp)^-1, T_10 = D_1 A_10 D_0,
           // from A_ab of chunk cV: value wavefront 0 computes D_0 and
           // Y = A_10 D_0, wavefront 1 computes D_1, each value wavefront then
@@ -963,9 +996,6 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
         }
   #pragma unroll
         for (int jt = 0; jt < 4; ++jt) cvs[jt] = mmah(kt[jt], Vf, z);
-        float inv_x;
-        const float sX = pow2_scale(wave_max(scale_max4(X[1], scale_max4(X[0], 0.f))), &inv_x);
-        const f16x8 Xf = frag8h(X[0], X[1], sX);
         f32x4 U[2];
         U[0] = mmah(Tf0, Xf, z);
         U[1] = mmah(Tf1, Xf, z);
