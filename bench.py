@@ -197,10 +197,12 @@ def run_decode(steps: int, warmup: int, seed: int = 1):
 def chunk_mfma_flops_per_chunk_head() -> int:
     """MFMA flops the bf16 chunked-prefill kernel issues per 32-token chunk
     and head, from the instructions in its compiled loop body: each of the
-    4 key wavefronts issues 18 v_mfma_f32_16x16x32_bf16, each of the 4 value
-    wavefronts 24 v_mfma_f32_16x16x32_f16 and 21 v_mfma_f32_16x16x16_f16
-    (16384 and 8192 flops per instruction)."""
-    return 4 * 18 * 16384 + 4 * (24 * 16384 + 21 * 8192)
+    4 t wavefronts issues 18 v_mfma_f32_16x16x32_bf16 (its Gram matrix),
+    each of the 4 value wavefronts 24 v_mfma_f32_16x16x32_f16 and one
+    v_mfma_f32_16x16x16_f16 (T_10), and the two value wavefronts that build
+    T's diagonal blocks 20 v_mfma_f32_16x16x16_f16 between them (16384 and
+    8192 flops per instruction)."""
+    return 4 * 18 * 16384 + 4 * 24 * 16384 + (4 + 20) * 8192
 
 
 CHUNK_L = 32        # chunk length of the bf16 chunked-prefill kernel
