@@ -19,12 +19,14 @@ GUARD = {("f32", 0): 5e-4, ("f32", 1): 5e-4, ("bf16", 1): 5e-4,
 
 
 def _run(ids, lens, H, dtype, n_slots, init=None, min_len=None, seed=0,
-         precise=0, scale=None, **draw):
+         precise=0, scale=None, edit=None, **draw):
     rng = np.random.default_rng(seed)
     b = G.make_batch(rng, ids, lens, H, 64, dtype, **draw)
     if scale is not None:
         for name, f in scale.items():
             b.inputs[name] = (b.inputs[name].double() * f).to(b.inputs[name].dtype)
+    if edit is not None:
+        edit(b.inputs)      # in place, on the rounded inputs both sides use
     pool = W.wkv7_pool_create(n_slots, H, 64)
     try:
         W.wkv7_pool_set_option(pool, W.WKV7_OPT_CHUNK_PRECISE, precise)
@@ -116,6 +118,54 @@ def test_out_of_fp16_range_runs_exactly(name, factor):
     say(f"large {name} x{factor:g}: o err {e_o:.3e}  S err {e_s:.3e}")
     assert np.all(np.isfinite(o.numpy())) and np.all(np.isfinite(S.numpy()))
     assert e_o < 1e-4 and e_s < 1e-4
+
+
+@pytest.mark.parametrize("name", ["a", "b", "r"])
+def test_single_large_input_runs_exactly(name):
+    """One element of a, b or r at 4e4 (beyond the fp16 operand range, one
+    token): its chunk runs token by token (the raw-input range flags of
+    both key roles), the others on the fast path."""
+    def edit(x):
+        x[name][5, 1, 3] = 4.0e4
+    e_o, e_s, o, S = _run(np.array([0], np.int32), [100], 2, "bf16", 1,
+                          seed=7, edit=edit)
+    say(f"large single {name}: o err {e_o:.3e}  S err {e_s:.3e}")
+    assert np.all(np.isfinite(o.numpy())) and np.all(np.isfinite(S.numpy()))
+    assert e_o < GUARD["bf16", 0] and e_s < GUARD["bf16", 0]
+
+
+def test_growing_decay_runs_exactly():
+    """w above 1 (1.0625 on every channel): outside the fast path's range
+    (its check runs when a chunk's inputs are prepared), so every chunk
+    runs token by token."""
+    e_o, e_s, o, S = _run(np.array([0], np.int32), [130], 2, "bf16", 1,
+                          seed=8, w_override=1.0625)
+    say(f"w = 1.0625: o err {e_o:.3e}  S err {e_s:.3e}")
+    assert np.all(np.isfinite(o.numpy())) and np.all(np.isfinite(S.numpy()))
+    assert e_o < 1e-4 and e_s < 1e-4
+
+
+@pytest.mark.parametrize("c", [1.0, 2.0])
+def test_t_out_of_fp16_range_runs_exactly(c):
+    """a = b = u with |u|^2 = c and w = 1 make A_ab = c below the
+    diagonal, so T = (I - A_ab)^-1 grows like (1 + c)^(t - s) within the
+    first 32-token chunk: with c = 1 only the off-diagonal block T_10
+    leaves the fp16 range (checked on every value wavefront), with c = 2
+    the diagonal blocks D_0 and D_1 too (checked where they are built).
+    The chunk runs token by token; the 8-token tail chunk on the fast path."""
+    u = torch.zeros(64, dtype=torch.float64)
+    u[0] = 1.0
+    u[1] = (c - 1.0) ** 0.5
+
+    def edit(x):
+        for name in ("a", "b"):
+            x[name][:] = u.to(x[name].dtype)
+        x["w"][:] = 1.0
+    e_o, e_s, o, S = _run(np.array([0], np.int32), [40], 2, "bf16", 1,
+                          seed=9, edit=edit)
+    say(f"T out of range, c = {c}: o err {e_o:.3e}  S err {e_s:.3e}")
+    assert np.all(np.isfinite(o.numpy())) and np.all(np.isfinite(S.numpy()))
+    assert e_o < GUARD["bf16", 0] and e_s < GUARD["bf16", 0]
 
 
 def test_chunked_matches_sequential_within_rounding():
