@@ -281,10 +281,10 @@ def run_prefill(steps: int, warmup: int, seed: int = 2):
 
 
 def run_prefill_f32(steps: int = 5, warmup: int = 3, seed: int = 2):
-    """The 8 x 4096 x H=32 prefill with fp32 inputs, which take the precise
-    chunked kernel (chunks of 64, every product in split-bf16 operands); one
-    step = reset the 8 slots + one plan forward, timed with an event pair
-    around the forward."""
+    """The 8 x 4096 x H=32 prefill with fp32 inputs, which take the chunked
+    kernel's precise plan (chunks of 32, every product from split-bf16
+    operands); one step = reset the 8 slots + one plan forward, timed with an
+    event pair around the forward."""
     import torch
     import wkv7_inputs as G
     from linear_attention_rnn_amd import wkv7 as W
@@ -320,8 +320,8 @@ def run_prefill_f32(steps: int = 5, warmup: int = 3, seed: int = 2):
     tokens = n_seq * T
     bytes_alg = tokens * H * (6 * N * 4 + N * 4) + n_seq * H * 2 * 4 * N * N
     return {"workload": "prefill_b8_t4096_h32_f32in_f32state",
-            "kernel": "chunk_kernel (fp32 inputs, chunks of 64, split-bf16 "
-                      "products)",
+            "kernel": "chunk_p_kernel<fp32, precise> (chunks of 32, "
+                      "split-bf16 products)",
             "tokens_per_s": tokens / (k_ms * 1e-3), "kernel_ms": k_ms,
             "hbm": {"achieved": bytes_alg / (k_ms * 1e-3) / 1e9,
                     "peak": HBM_PEAK_GBS, "unit": "GB/s",

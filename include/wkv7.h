@@ -106,15 +106,15 @@ enum {
   /* Segment-parallel prefill, for batches with few long sequences (the
    * chunked kernel runs one workgroup per (sequence, head), so a handful of
    * sequences leaves most of the GPU idle). 0 (default): off. s > 0 (a
-   * multiple of 32, at least 64): on the bf16 fast chunked path, every
-   * sequence of at least 2 s tokens is cut into segments of s tokens that
+   * multiple of 32, at least 64): every sequence of at least 2 s tokens
+   * (any input type and CHUNK_PRECISE) is cut into segments of s tokens that
    * run in parallel: each segment's transition and zero-start state, a
    * short scan chaining the segments' states (the recurrence is affine in
    * the state), then every segment again from its true initial state. About
    * three times the arithmetic, so it pays only while the (sequence, head)
    * count is well below the CU count. The split depends on the sequence's
    * own length only; results agree with the unsplit run to rounding, not
-   * bit for bit. Other chunked paths ignore it. */
+   * bit for bit. */
   WKV7_OPT_SEGMENT_LEN = 3
 };
 

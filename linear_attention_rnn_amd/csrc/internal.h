@@ -90,22 +90,20 @@ hipError_t launch_seq1(const SeqArgs& args, hipStream_t stream);
 // bits), for items of more than one token.
 hipError_t launch_seq4(const SeqArgs& args, hipStream_t stream);
 
-// Chunked-prefill kernel for sequences of at least one chunk. bf16 inputs
-// take the fp16-value-side kernel unless `precise`; fp32 inputs always take
-// the split-bf16 kernel.
-hipError_t launch_chunked(const SeqArgs& args, bool precise,
-                          hipStream_t stream);
-
-// Pipelined chunked-prefill kernel for bf16 inputs with an fp16 value side
-// (32-token chunks), over pool slots (args.items) or over segments
-// (launch_chunked_p_seg: `segs`, n_items of them; args.items unused).
-hipError_t launch_chunked_p(const SeqArgs& args, hipStream_t stream,
-                            const WorkItem* dec = nullptr, int32_t n_dec = 0);
-// Segment items (SegItem) instead of pool slots; same kernel code.
-hipError_t launch_chunked_p_seg(const SeqArgs& args, const SegItem* segs,
-                                hipStream_t stream, const WorkItem* dec = nullptr,
-                                int32_t n_dec = 0);
-// Wavefronts per workgroup of the bf16 chunked kernel.
+// Pipelined chunked-prefill kernel (32-token chunks) for sequences of at
+// least one chunk, over pool slots (args.items). bf16 inputs take the plan
+// with an fp16 value side unless `precise`; fp32 inputs, and bf16 inputs
+// with `precise`, the plan with split bf16 operands throughout. n_dec
+// decode items `dec` run in trailing workgroups of the same launch.
+hipError_t launch_chunked_p(const SeqArgs& args, bool precise,
+                            hipStream_t stream, const WorkItem* dec = nullptr,
+                            int32_t n_dec = 0);
+// Segment items (SegItem, n_items of them; args.items unused) instead of
+// pool slots; same kernel code.
+hipError_t launch_chunked_p_seg(const SeqArgs& args, bool precise,
+                                const SegItem* segs, hipStream_t stream,
+                                const WorkItem* dec = nullptr, int32_t n_dec = 0);
+// Wavefronts per workgroup of the chunked kernel.
 constexpr int kChunkPWaves = 12;
 // Trailing workgroups of a chunked-kernel launch that run n_dec decode
 // items (one (item, head) pair per wavefront).

@@ -1,4 +1,4 @@
-// Pipelined chunked-prefill WKV-7 kernel for bf16 inputs on gfx950.
+// Pipelined chunked-prefill WKV-7 kernel on gfx950.
 //
 // Same operation as the other kernels (page "RWKV-X Architecture", section
 // "WKV-7 Kernel (Generalized Delta Rule)", product-form reading
@@ -16,29 +16,34 @@
 // Every Gram term <., .> is the exact decay between s and t (<= 1) times
 // the inputs; only the operands Abar / Lambda_L, Rbar / Lambda_L are large.
 //
-// Organisation: one 512-thread workgroup (8 wavefronts, two per SIMD) per
-// (sequence, head), as a pipeline over chunks. In step c:
-//   * key wavefronts 0-3 build chunk c's scaled operands (into one of two
-//     LDS buffers) from its decay products, then the four Gram matrices
-//     (wavefront w computes matrix w), then prepare chunk c + 1 (its
-//     running-product decays and per-row-group totals), which fills the
-//     time they would otherwise wait for the value side;
-//   * value wavefronts 4-7 consume chunk c - 1: wavefront 4 + w owns state
-//     rows i in [16 w, 16 w + 16), kept in registers as MFMA accumulator
-//     tiles of S^T, and computes X and T (in registers, fp16 MFMA products),
-//     then U, O (written to HBM) and the state update.
-// Two workgroup barriers per step, after the operands and at the end; the
-// fallback flags of chunk c travel with the second (a ballot per
-// wavefront, posted to LDS).
+// Organisation: one 768-thread workgroup (12 wavefronts, three per SIMD:
+// wavefront w runs on SIMD w mod 4) per (sequence, head), as a two-stage
+// pipeline over chunks. In step c the key side builds chunk c while the
+// value side runs chunk c - 1:
+//   * t wavefronts 0-3 build the operands made from r and a, then (after
+//     the mid-step barrier) t wavefront W computes Gram matrix W;
+//   * s wavefronts 4-7 build the operands made from k, b and v and prepare
+//     the next chunk's decay products;
+//   * value wavefronts 8-11: wavefront 8 + w owns state rows
+//     i in [16 w, 16 w + 16), kept in registers as MFMA accumulator tiles of
+//     S^T; value wavefronts 0 and 1 also form T from A_ab.
+// Two workgroup barriers per step (mid-step and end); the fallback flags of
+// a chunk travel with the end-of-step barrier (a ballot per wavefront,
+// posted to LDS).
 //
-// Precision: Gram products use split bf16 (hi + lo) operands, three MFMAs
-// with fp32 accumulation; the diagonal blocks of T are fp32; every
-// value-side product uses single fp16 operands, with the state, X and U
-// scaled by powers of two (exact) before conversion. About 3e-3 of
-// max|err|/rms against the float64 oracle on the workloads' inputs (bf16
-// bar: 2e-2). A chunk whose Lambda_L falls below 2^-100 in some channel, or
-// whose fp16 operands would leave the fp16 range, runs token by token on the
-// value wavefronts instead (exact for any w in (0, 1]).
+// Precision, two plans (template parameter PRE):
+//   * fast (bf16 inputs): Gram products from split bf16 (hi + lo) operands,
+//     three MFMAs with fp32 accumulation; T from fp16 A_ab by products on
+//     the matrix cores; every value-side product with single fp16 operands,
+//     the state, X and U scaled by powers of two (exact) before conversion.
+//     About 3e-3 of max|err|/rms against the float64 oracle on the
+//     workloads' inputs (bf16 bar: 2e-2).
+//   * precise (fp32 inputs, or bf16 inputs on request): the same Gram
+//     products and T; every value-side product from split bf16 operands as
+//     well (three MFMAs), no scaling. About 1e-4 (fp32 bar: 1e-3).
+// A chunk whose Lambda_L falls below 2^-100 in some channel, whose inputs
+// reach 2^15, or whose Gram matrices or T leave the fp16 range runs token by
+// token on the value wavefronts instead (exact for any w in (0, 1]).
 //
 // MFMA fragments (verified lane layout of v_mfma_f32_16x16x32_{bf16,f16}
 // and 16x16x16): lane l = 16 g + n holds operand row n and, for a 32-wide k
@@ -61,6 +66,8 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 // The state pointers of segment items come from memory; accessed as plain
 // pointers they would compile to flat instructions, which also count
 // against the LDS wait counter.
@@ -73,22 +80,35 @@ constexpr int kM64 = kL * kP64;          // [32][64] matrix, elements
 constexpr int kM32 = kL * kP32;          // [32][32] matrix
 constexpr int kMT = 64 * kP32;           // [64][32] matrix
 
-// LDS map (bytes)
-constexpr int kOffGR = 0;                                  // 4 pairs [32][64]
-constexpr int kOffAB = kOffGR + 4 * 2 * kM64 * 2;          // fp16 A_ab, A_ab^T
-constexpr int kOffTOT = kOffAB + 2 * kM32 * 2;             // fp32 [8][64]
-constexpr int kVOBytes = (2 * kM64 + 3 * kMT) * 2;         // per buffer
-constexpr int kOffVO = kOffTOT + 8 * 64 * 4;               // 2 buffers
-constexpr int kLLBytes = 3 * kM32 * 2;
-constexpr int kOffLL = kOffVO + 2 * kVOBytes;              // 2 buffers
-constexpr int kOffLAM = kOffLL + 2 * kLLBytes;             // fp32 [2][64]
-constexpr int kOffTT = kOffLAM + 2 * 64 * 4;               // fp16 T [32][32]
-constexpr int kOffYC = kOffTT + kM32 * 2;                  // fp16x4 [64]: col(Y)
-constexpr int kOffD1R = kOffYC + 64 * 8;                   // fp16x4 [64]: row(D_1)
-constexpr int kOffTFL = kOffD1R + 64 * 8;                  // u32 [2]: D_0, D_1 range
-constexpr int kOffFLG = kOffTFL + 2 * 4;                   // u32 [16]
-constexpr int kLdsBytes = kOffFLG + 16 * 4;
-static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+// LDS map (bytes). The value side's operands (VO: Abar, Rbar [32][64],
+// Bbar^T, Kbar^T, V^T [64][32]; LL: A_ak, M_rb, M_rk [32][32]) are single
+// fp16 matrices in the fast plan and split bf16 pairs (hi matrix, lo matrix
+// after it) in the precise plan; everything else is common.
+template <bool PRE> struct Map {
+  static constexpr int kVO = PRE ? 2 : 1;                  // matrices per operand
+  static constexpr int GR = 0;                             // 4 pairs [32][64]
+  static constexpr int AB = GR + 4 * 2 * kM64 * 2;         // fp16 A_ab, A_ab^T
+  static constexpr int TOT = AB + 2 * kM32 * 2;            // fp32 [8][64]
+  static constexpr int VOBytes = kVO * (2 * kM64 + 3 * kMT) * 2;  // per buffer
+  static constexpr int VO = TOT + 8 * 64 * 4;              // 2 buffers
+  static constexpr int LLBytes = kVO * 3 * kM32 * 2;
+  static constexpr int LL = VO + 2 * VOBytes;              // 2 buffers
+  static constexpr int LAM = LL + 2 * LLBytes;             // fp32 [2][64]
+  static constexpr int TT = LAM + 2 * 64 * 4;              // fp16 T [32][32]
+  static constexpr int YC = TT + kM32 * 2;                 // fp16x4 [64]: col(Y)
+  static constexpr int D1R = YC + 64 * 8;                  // fp16x4 [64]: row(D_1)
+  static constexpr int TFL = D1R + 64 * 8;                 // u32 [2]: D_0, D_1 range
+  static constexpr int FLG = TFL + 2 * 4;                  // u32 [16]
+  static constexpr int Bytes = FLG + 16 * 4;
+  static_assert(Bytes <= 160 * 1024, "LDS budget");
+  // element offsets of the operands within a VO / LL buffer
+  static constexpr int Abar = 0, Rbar = kVO * kM64, BbT = 2 * kVO * kM64,
+                       KbT = BbT + kVO * kMT, Vt = KbT + kVO * kMT;
+  static constexpr int Aak = 0, Mrb = kVO * kM32, Mrk = 2 * kVO * kM32;
+};
+// element type of the value side's LDS operands
+template <bool PRE> struct VOElem { typedef _Float16 T; };
+template <> struct VOElem<true> { typedef __bf16 T; };
 
 constexpr float kHalfSafe = 32768.f;            // fp16 operand bound
 constexpr float kMinLamL = 7.88860905e-31f;     // 2^-100
@@ -184,16 +204,56 @@ __device__ __forceinline__ void outer_products(const float (&g0)[8], const float
 // Two channels at once: one packed conversion for the high parts, the
 // residuals from the packed bits (exact), one packed conversion for them.
 // The same values as split() per channel.
-__device__ __forceinline__ void put2p(__bf16* pair, int mat, int pitch,
-                                      int row, int col, float x0, float x1) {
-  typedef float f32x2 __attribute__((ext_vector_type(2)));
-  const bf16x2 h = __builtin_convertvector(f32x2{x0, x1}, bf16x2);
+__device__ __forceinline__ void split2(float x0, float x1, bf16x2& h, bf16x2& l) {
+  h = __builtin_convertvector(f32x2{x0, x1}, bf16x2);
   const uint32_t hb = __builtin_bit_cast(uint32_t, h);
   const float h0 = __uint_as_float(hb << 16);
   const float h1 = __uint_as_float(hb & 0xffff0000u);
-  const bf16x2 l = __builtin_convertvector(f32x2{x0 - h0, x1 - h1}, bf16x2);
+  l = __builtin_convertvector(f32x2{x0 - h0, x1 - h1}, bf16x2);
+}
+__device__ __forceinline__ void put2p(__bf16* pair, int mat, int pitch,
+                                      int row, int col, float x0, float x1) {
+  bf16x2 h, l;
+  split2(x0, x1, h, l);
   *reinterpret_cast<bf16x2*>(pair + row * pitch + col) = h;
   *reinterpret_cast<bf16x2*>(pair + mat + row * pitch + col) = l;
+}
+// four consecutive elements of a pair-matrix row, split
+__device__ __forceinline__ void put4p(__bf16* pair, int mat, int pitch,
+                                      int row, int col, f32x4 x) {
+  bf16x2 h0, l0, h1, l1;
+  split2(x[0], x[1], h0, l0);
+  split2(x[2], x[3], h1, l1);
+  *reinterpret_cast<bf16x4*>(pair + row * pitch + col) =
+      __builtin_shufflevector(h0, h1, 0, 1, 2, 3);
+  *reinterpret_cast<bf16x4*>(pair + mat + row * pitch + col) =
+      __builtin_shufflevector(l0, l1, 0, 1, 2, 3);
+}
+// operand fragment of two result tiles (k = 4g + r, then 16 + 4g + r), split
+__device__ __forceinline__ F8 frag8p(f32x4 t0, f32x4 t1) {
+  bf16x2 h[4], l[4];
+  split2(t0[0], t0[1], h[0], l[0]);
+  split2(t0[2], t0[3], h[1], l[1]);
+  split2(t1[0], t1[1], h[2], l[2]);
+  split2(t1[2], t1[3], h[3], l[3]);
+  F8 f;
+  f.h = __builtin_shufflevector(__builtin_shufflevector(h[0], h[1], 0, 1, 2, 3),
+                                __builtin_shufflevector(h[2], h[3], 0, 1, 2, 3),
+                                0, 1, 2, 3, 4, 5, 6, 7);
+  f.l = __builtin_shufflevector(__builtin_shufflevector(l[0], l[1], 0, 1, 2, 3),
+                                __builtin_shufflevector(l[2], l[3], 0, 1, 2, 3),
+                                0, 1, 2, 3, 4, 5, 6, 7);
+  return f;
+}
+// fp16 values as split bf16 pairs: exact (11 significant bits = 8 + 3)
+__device__ __forceinline__ F8 split_f16(f16x8 x) {
+  f32x4 a, b;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    a[r] = static_cast<float>(x[r]);
+    b[r] = static_cast<float>(x[4 + r]);
+  }
+  return frag8p(a, b);
 }
 __device__ __forceinline__ void put2h(_Float16* m, int pitch, int row, int col,
                                       float x0, float x1) {
@@ -278,23 +338,78 @@ __device__ __forceinline__ bool any_half_ge(uint32_t m, uint32_t limit) {
   return ((m & 0xffffu) >= limit) | ((m >> 16) >= limit);
 }
 
-// raw inputs of a key thread, rows 4 rg + e (e < 4), channels 2 jp, 2 jp + 1:
-// a t wavefront holds r, a and w, an s wavefront k, b, v and w
-struct RawT { uint32_t r[4], a[4], w[4]; };
-struct RawS { uint32_t k[4], b[4], v[4], w[4]; };
+// max of |x| over n pairs of floats, as bit patterns (sign cleared; NaN and
+// Inf sort highest), a tree of depth log2(2 n)
+template <int n>
+__device__ __forceinline__ uint32_t absmax_tree(const u32x2* x) {
+  uint32_t m[n];
+#pragma unroll
+  for (int u = 0; u < n; ++u) m[u] = umax(x[u][0] & 0x7fffffffu, x[u][1] & 0x7fffffffu);
+#pragma unroll
+  for (int w = 1; w < n; w *= 2)
+#pragma unroll
+    for (int u = 0; u + w < n; u += 2 * w) m[u] = umax(m[u], m[u + w]);
+  return m[0];
+}
+
+// Raw inputs of a key thread: for each of its rows, the bits of channels
+// 2 jp and 2 jp + 1, a bf16 pair (bf16 inputs) or two floats (fp32 inputs).
+template <int DT> struct Raw;
+template <> struct Raw<WKV7_BF16> {
+  typedef uint32_t W;
+  static constexpr int kElem = 2;                       // bytes per element
+  __device__ static float c0(W x) { return bf_lo(x); }
+  __device__ static float c1(W x) { return bf_hi(x); }
+  __device__ static W zero() { return 0u; }
+  __device__ static W one() { return 0x3f803f80u; }
+  __device__ static W load(__amdgpu_buffer_rsrc_t rs, int voff) {
+    return __builtin_amdgcn_raw_buffer_load_b32(rs, voff, 0, 0);
+  }
+  // some |x| >= 2^15 (or NaN/Inf)
+  template <int n> __device__ static bool big(const W (&x)[n]) {
+    return any_half_ge(absmax_tree<n>(x), 0x4700u);
+  }
+  // some |x| > 1 (or NaN)
+  template <int n> __device__ static bool above_one(const W (&x)[n]) {
+    return any_half_ge(absmax_tree<n>(x), 0x3f81u);
+  }
+};
+template <> struct Raw<WKV7_F32> {
+  typedef u32x2 W;
+  static constexpr int kElem = 4;
+  __device__ static float c0(W x) { return __uint_as_float(x[0]); }
+  __device__ static float c1(W x) { return __uint_as_float(x[1]); }
+  __device__ static W zero() { return W{0u, 0u}; }
+  __device__ static W one() { return W{0x3f800000u, 0x3f800000u}; }
+  __device__ static W load(__amdgpu_buffer_rsrc_t rs, int voff) {
+    return __builtin_amdgcn_raw_buffer_load_b64(rs, voff, 0, 0);
+  }
+  template <int n> __device__ static bool big(const W (&x)[n]) {
+    return absmax_tree<n>(x) >= 0x47000000u;
+  }
+  template <int n> __device__ static bool above_one(const W (&x)[n]) {
+    return absmax_tree<n>(x) > 0x3f800000u;
+  }
+};
+
+// rows 4 rg + e (e < 4): a t wavefront holds r, a and w, an s wavefront k,
+// b, v and w
+template <int DT> struct RawT { typename Raw<DT>::W r[4], a[4], w[4]; };
+template <int DT> struct RawS { typename Raw<DT>::W k[4], b[4], v[4], w[4]; };
 
 // Loads through buffer resources based at the chunk's first row, with a
 // 32-bit lane offset and no branch: a row past the chunk's end re-reads the
 // last valid row (always in bounds). The caller replaces such rows by
 // padding (pad_raw) when it consumes them, so nothing waits on the loads
 // here.
-template <int NA>
-__device__ __forceinline__ void load_rows(uint32_t (*const dst[NA])[4],
+template <int DT, int NA>
+__device__ __forceinline__ void load_rows(typename Raw<DT>::W (*const dst[NA])[4],
                                           const void* const src[NA],
                                           const SeqArgs& p, int t0, int n,
                                           int h, int rg, int jp) {
-  const size_t row0 = (static_cast<size_t>(t0) * p.H + h) * (kN * 2);  // bytes
-  const uint32_t rowb = static_cast<uint32_t>(p.H) * (kN * 2);
+  constexpr int es = Raw<DT>::kElem;
+  const size_t row0 = (static_cast<size_t>(t0) * p.H + h) * (kN * es);  // bytes
+  const uint32_t rowb = static_cast<uint32_t>(p.H) * (kN * es);
   const int bytes = static_cast<int>(static_cast<uint32_t>(n) * rowb);
   __amdgpu_buffer_rsrc_t rs[NA];
 #pragma unroll
@@ -305,42 +420,40 @@ __device__ __forceinline__ void load_rows(uint32_t (*const dst[NA])[4],
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int voff = static_cast<int>(
-        static_cast<uint32_t>(min(4 * rg + e, n - 1)) * rowb + 4 * jp);
+        static_cast<uint32_t>(min(4 * rg + e, n - 1)) * rowb + 2 * es * jp);
 #pragma unroll
-    for (int u = 0; u < NA; ++u)
-      (*dst[u])[e] = __builtin_amdgcn_raw_buffer_load_b32(rs[u], voff, 0, 0);
+    for (int u = 0; u < NA; ++u) (*dst[u])[e] = Raw<DT>::load(rs[u], voff);
   }
 }
-__device__ __forceinline__ void load_raw(RawT& x, const SeqArgs& p, int t0,
+template <int DT>
+__device__ __forceinline__ void load_raw(RawT<DT>& x, const SeqArgs& p, int t0,
                                          int n, int h, int rg, int jp) {
-  uint32_t (*const dst[3])[4] = {&x.r, &x.a, &x.w};
+  typename Raw<DT>::W (*const dst[3])[4] = {&x.r, &x.a, &x.w};
   const void* const src[3] = {p.r, p.a, p.w};
-  load_rows<3>(dst, src, p, t0, n, h, rg, jp);
-}
-__device__ __forceinline__ void load_raw(RawS& x, const SeqArgs& p, int t0,
-                                         int n, int h, int rg, int jp) {
-  uint32_t (*const dst[4])[4] = {&x.k, &x.b, &x.v, &x.w};
-  const void* const src[4] = {p.k, p.b, p.v, p.w};
-  load_rows<4>(dst, src, p, t0, n, h, rg, jp);
+  load_rows<DT, 3>(dst, src, p, t0, n, h, rg, jp);
 }
 // rows 4 rg + e >= n become padding: w = 1, everything else 0 (state unchanged)
-__device__ __forceinline__ void pad_raw(RawT& x, int n, int rg) {
+template <int DT>
+__device__ __forceinline__ void pad_raw(RawT<DT>& x, int n, int rg) {
+  typedef Raw<DT> R;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const bool pad = 4 * rg + e >= n;
-    x.r[e] = pad ? 0u : x.r[e];
-    x.a[e] = pad ? 0u : x.a[e];
-    x.w[e] = pad ? 0x3f803f80u : x.w[e];
+    x.r[e] = pad ? R::zero() : x.r[e];
+    x.a[e] = pad ? R::zero() : x.a[e];
+    x.w[e] = pad ? R::one() : x.w[e];
   }
 }
-__device__ __forceinline__ void pad_raw(RawS& x, int n, int rg) {
+template <int DT>
+__device__ __forceinline__ void pad_raw(RawS<DT>& x, int n, int rg) {
+  typedef Raw<DT> R;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const bool pad = 4 * rg + e >= n;
-    x.k[e] = pad ? 0u : x.k[e];
-    x.b[e] = pad ? 0u : x.b[e];
-    x.v[e] = pad ? 0u : x.v[e];
-    x.w[e] = pad ? 0x3f803f80u : x.w[e];
+    x.k[e] = pad ? R::zero() : x.k[e];
+    x.b[e] = pad ? R::zero() : x.b[e];
+    x.v[e] = pad ? R::zero() : x.v[e];
+    x.w[e] = pad ? R::one() : x.w[e];
   }
 }
 
@@ -419,17 +532,21 @@ __device__ __forceinline__ uint32_t barrier_or2(uint32_t* slot, int wv,
   return r;
 }
 
+// one input element as float
+__device__ __forceinline__ float in_elem(const void* p, size_t i, IntC<WKV7_BF16>) {
+  return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(p)[i]) << 16);
+}
+__device__ __forceinline__ float in_elem(const void* p, size_t i, IntC<WKV7_F32>) {
+  return static_cast<const float*>(p)[i];
+}
+
 // Exact token-by-token recurrence for one chunk on a value wavefront (rows
 // i = 16 vb + n16 of the state, held as S[jt][r] = S[i][16 jt + 4 g + r]).
+template <int DT>
 __device__ __forceinline__ void exact_chunk(const SeqArgs& p, f32x4* S, int t0,
                                          int n, int h, int vb, int g,
                                          int n16, bool zero_v, bool no_out) {
-  const uint16_t* R = static_cast<const uint16_t*>(p.r);
-  const uint16_t* Wp = static_cast<const uint16_t*>(p.w);
-  const uint16_t* K = static_cast<const uint16_t*>(p.k);
-  const uint16_t* A = static_cast<const uint16_t*>(p.a);
-  const uint16_t* B = static_cast<const uint16_t*>(p.b);
-  const uint16_t* V = static_cast<const uint16_t*>(p.v);
+  const IntC<DT> dt;
   const int i = 16 * vb + n16;
   for (int t = 0; t < n; ++t) {
     const size_t base = (static_cast<size_t>(t0 + t) * p.H + h) * kN;
@@ -439,15 +556,14 @@ __device__ __forceinline__ void exact_chunk(const SeqArgs& p, f32x4* S, int t0,
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const size_t o = base + 16 * jt + 4 * g + r;
-        rr[4 * jt + r] = __uint_as_float(static_cast<uint32_t>(R[o]) << 16);
-        ww[4 * jt + r] = __uint_as_float(static_cast<uint32_t>(Wp[o]) << 16);
-        kk[4 * jt + r] = __uint_as_float(static_cast<uint32_t>(K[o]) << 16);
-        aa[4 * jt + r] = __uint_as_float(static_cast<uint32_t>(A[o]) << 16);
-        bb[4 * jt + r] = __uint_as_float(static_cast<uint32_t>(B[o]) << 16);
+        rr[4 * jt + r] = in_elem(p.r, o, dt);
+        ww[4 * jt + r] = in_elem(p.w, o, dt);
+        kk[4 * jt + r] = in_elem(p.k, o, dt);
+        aa[4 * jt + r] = in_elem(p.a, o, dt);
+        bb[4 * jt + r] = in_elem(p.b, o, dt);
       }
     }
-    const float vi = zero_v ? 0.f
-                            : __uint_as_float(static_cast<uint32_t>(V[base + i]) << 16);
+    const float vi = zero_v ? 0.f : in_elem(p.v, base + i, dt);
     float sa = 0.f;
 #pragma unroll
     for (int jt = 0; jt < 4; ++jt)
@@ -477,24 +593,28 @@ __device__ __forceinline__ void exact_chunk(const SeqArgs& p, f32x4* S, int t0,
 // wavefront, with the sequential recurrence (the same bits as the
 // sequential kernel): a batch's decode tokens then fill CUs that its
 // prefills leave idle, in the same launch.
-template <bool SEG>
+// DT: input type (WKV7_BF16 or WKV7_F32); PRE: the precise plan.
+template <bool SEG, int DT, bool PRE>
 __global__ __launch_bounds__(64 * kChunkPWaves, 1)
 void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
                     int32_t n_dec) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
-  __bf16* GR = reinterpret_cast<__bf16*>(lds + kOffGR);
+  typedef Raw<DT> R;
+  typedef Map<PRE> M;
+  typedef typename VOElem<PRE>::T VE;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[M::Bytes];
+  __bf16* GR = reinterpret_cast<__bf16*>(lds + M::GR);
   __bf16* Ahat = GR;                       // pair [t][j]
   __bf16* Rhat = GR + 2 * kM64;            // pair [t][j]
   __bf16* Bbar = GR + 4 * kM64;            // pair [s][j]
   __bf16* Kbar = GR + 6 * kM64;            // pair [s][j]
-  _Float16* AB = reinterpret_cast<_Float16*>(lds + kOffAB);   // A_ab [t][s], then [s][t]
-  float* TOT = reinterpret_cast<float*>(lds + kOffTOT);
-  float* LAMb = reinterpret_cast<float*>(lds + kOffLAM);
-  uint32_t* FLG = reinterpret_cast<uint32_t*>(lds + kOffFLG);
-  _Float16* TT = reinterpret_cast<_Float16*>(lds + kOffTT);       // T [t][s]
-  _Float16* YC = reinterpret_cast<_Float16*>(lds + kOffYC);
-  _Float16* D1R = reinterpret_cast<_Float16*>(lds + kOffD1R);
-  uint32_t* TFL = reinterpret_cast<uint32_t*>(lds + kOffTFL);
+  _Float16* AB = reinterpret_cast<_Float16*>(lds + M::AB);   // A_ab [t][s], then [s][t]
+  float* TOT = reinterpret_cast<float*>(lds + M::TOT);
+  float* LAMb = reinterpret_cast<float*>(lds + M::LAM);
+  uint32_t* FLG = reinterpret_cast<uint32_t*>(lds + M::FLG);
+  _Float16* TT = reinterpret_cast<_Float16*>(lds + M::TT);       // T [t][s]
+  _Float16* YC = reinterpret_cast<_Float16*>(lds + M::YC);
+  _Float16* D1R = reinterpret_cast<_Float16*>(lds + M::D1R);
+  uint32_t* TFL = reinterpret_cast<uint32_t*>(lds + M::TFL);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -504,7 +624,7 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
     const int64_t q = (static_cast<int64_t>(blockIdx.x) - n_main) * kChunkPWaves + wv;
     const int di = static_cast<int>(q / p.H);
     const int dh = static_cast<int>(q - static_cast<int64_t>(di) * p.H);
-    if (di < n_dec) seqw::seq_wave<WKV7_BF16, false>(p, dec[di], dh, lane);
+    if (di < n_dec) seqw::seq_wave<DT, false>(p, dec[di], dh, lane);
     return;
   }
   // roles: t wavefronts 0-3, s wavefronts 4-7, value wavefronts 8-11
@@ -568,9 +688,9 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
     load_raw(x, p, tok0 + cl * kL, min(kL, len - cl * kL), h, rg, jp);
   };
   float w0[4], w1[4], P0[4], P1[4];
-  auto decays = [&](const uint32_t (&wr)[4]) {
+  auto decays = [&](const typename R::W (&wr)[4]) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) { w0[e] = bf_lo(wr[e]); w1[e] = bf_hi(wr[e]); }
+    for (int e = 0; e < 4; ++e) { w0[e] = R::c0(wr[e]); w1[e] = R::c1(wr[e]); }
     P0[0] = w0[0]; P1[0] = w1[0];
 #pragma unroll
     for (int e = 1; e < 4; ++e) { P0[e] = P0[e - 1] * w0[e]; P1[e] = P1[e - 1] * w1[e]; }
@@ -602,7 +722,7 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
 
   auto t_loop = [&](auto Wc) {
     constexpr int W = decltype(Wc)::value;
-    RawT x;
+    RawT<DT> x;
     auto prep = [&](int c) {
       if (len - c * kL < kL) pad_raw(x, len - c * kL, rg);   // the last chunk
       decays(x.w);
@@ -614,8 +734,8 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
       const int cK = step;          // chunk whose operands and Grams are built
       const bool k_on = cK < nch;
       const int bK = cK & 1;
-      _Float16* VOk = reinterpret_cast<_Float16*>(lds + kOffVO + bK * kVOBytes);
-      _Float16* LLk = reinterpret_cast<_Float16*>(lds + kOffLL + bK * kLLBytes);
+      VE* VOk = reinterpret_cast<VE*>(lds + M::VO + bK * M::VOBytes);
+      VE* LLk = reinterpret_cast<VE*>(lds + M::LL + bK * M::LLBytes);
       const int t0K = tok0 + cK * kL;
       // ===== interval 1 =====
       bool bad_k = false;
@@ -625,25 +745,30 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
         // bf16 pairs, far coarser; a lam below the fast path's range takes the
         // token-by-token path, which does not use these operands
         const float inv0 = __builtin_amdgcn_rcpf(d.lam0), inv1 = __builtin_amdgcn_rcpf(d.lam1);
-        _Float16* Abar = VOk;
-        _Float16* Rbar = VOk + kM64;
+        VE* Abar = VOk + M::Abar;
+        VE* Rbar = VOk + M::Rbar;
         // range of the raw inputs (|Abar| <= |a| etc. when every |w| <= 1;
         // w and lam are checked on the s side)
-        const uint32_t xs[8] = {x.a[0], x.a[1], x.a[2], x.a[3],
-                                x.r[0], x.r[1], x.r[2], x.r[3]};
-        bad_k = any_half_ge(absmax_tree<8>(xs), 0x4700u);   // |x| >= 2^15 (or NaN/Inf)
+        const typename R::W xs[8] = {x.a[0], x.a[1], x.a[2], x.a[3],
+                                     x.r[0], x.r[1], x.r[2], x.r[3]};
+        bad_k = R::big(xs);                                  // |x| >= 2^15 (or NaN/Inf)
   #pragma unroll
         for (int e = 3; e >= 0; --e) {
           const int t = 4 * rg + e;
           const float lp0 = e == 0 ? d.pre0 : d.pre0 * P0[e - 1];
           const float lp1 = e == 0 ? d.pre1 : d.pre1 * P1[e - 1];
           const float lt0 = d.pre0 * P0[e], lt1 = d.pre1 * P1[e];
-          const float ab0 = bf_lo(x.a[e]) * lp0, ab1 = bf_hi(x.a[e]) * lp1;
-          const float rb0 = bf_lo(x.r[e]) * lt0, rb1 = bf_hi(x.r[e]) * lt1;
+          const float ab0 = R::c0(x.a[e]) * lp0, ab1 = R::c1(x.a[e]) * lp1;
+          const float rb0 = R::c0(x.r[e]) * lt0, rb1 = R::c1(x.r[e]) * lt1;
           put2p(Ahat, kM64, kP64, t, j0, ab0 * inv0, ab1 * inv1);
           put2p(Rhat, kM64, kP64, t, j0, rb0 * inv0, rb1 * inv1);
-          put2h(Abar, kP64, t, j0, ab0, ab1);
-          put2h(Rbar, kP64, t, j0, rb0, rb1);
+          if constexpr (PRE) {
+            put2p(Abar, kM64, kP64, t, j0, ab0, ab1);
+            put2p(Rbar, kM64, kP64, t, j0, rb0, rb1);
+          } else {
+            put2h(Abar, kP64, t, j0, ab0, ab1);
+            put2h(Rbar, kP64, t, j0, rb0, rb1);
+          }
         }
       }
       // next chunk's inputs, in flight from here on
@@ -703,17 +828,23 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
             }
           }
         } else {
-          _Float16* dst = LLk + (W - 1) * kM32;
+          VE* dst = LLk + (W - 1) * M::kVO * kM32;
           ti = 0;
   #pragma unroll
           for (int tt = 0; tt < 2; ++tt) {
   #pragma unroll
             for (int st = 0; st <= tt; ++st, ++ti) {
               gmax = abs_max4(gt[ti], gmax);
-              put4h(dst, kP32, 16 * tt + n16, 16 * st + 4 * g, gt[ti]);
+              if constexpr (PRE)
+                put4p(dst, kM32, kP32, 16 * tt + n16, 16 * st + 4 * g, gt[ti]);
+              else
+                put4h(dst, kP32, 16 * tt + n16, 16 * st + 4 * g, gt[ti]);
             }
           }
-          put4h(dst, kP32, n16, 16 + 4 * g, z);
+          if constexpr (PRE)
+            put4p(dst, kM32, kP32, n16, 16 + 4 * g, z);
+          else
+            put4h(dst, kP32, n16, 16 + 4 * g, z);
         }
       }
       prep(min(cK + 1, nch - 1));   // the next chunk
@@ -723,7 +854,7 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
   };
 
   auto s_loop = [&](auto Wc) {
-    RawS x;
+    RawS<DT> x;
     // The s wavefronts load a chunk's w at the start of the first interval
     // of the step before its preparation (the build uses the decays
     // prepared from it, not x.w), and its k, b and v at the start of the
@@ -731,20 +862,20 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
     // no load issued in the same interval.
     auto load_w = [&](int c) {
       const int cl = min(c, nch - 1);
-      uint32_t (*const dst[1])[4] = {&x.w};
+      typename R::W (*const dst[1])[4] = {&x.w};
       const void* const src[1] = {p.w};
-      load_rows<1>(dst, src, p, tok0 + cl * kL, min(kL, len - cl * kL), h, rg, jp);
+      load_rows<DT, 1>(dst, src, p, tok0 + cl * kL, min(kL, len - cl * kL), h, rg, jp);
     };
     auto load_kbv = [&](int c) {
       const int cl = min(c, nch - 1);
-      uint32_t (*const dst[3])[4] = {&x.k, &x.b, &x.v};
+      typename R::W (*const dst[3])[4] = {&x.k, &x.b, &x.v};
       const void* const src[3] = {p.k, p.b, p.v};
-      load_rows<3>(dst, src, p, tok0 + cl * kL, min(kL, len - cl * kL), h, rg, jp);
+      load_rows<DT, 3>(dst, src, p, tok0 + cl * kL, min(kL, len - cl * kL), h, rg, jp);
     };
     bool bad_w = false;   // |w| > 1 (or NaN) in the prepared chunk
     auto prep = [&](int c) {
       if (len - c * kL < kL) pad_raw(x, len - c * kL, rg);   // the last chunk
-      bad_w = any_half_ge(absmax_tree<4>(x.w), 0x3f81u);
+      bad_w = R::above_one(x.w);
       decays(x.w);
       TOT[rg * 64 + j0] = P0[3];
       TOT[rg * 64 + j0 + 1] = P1[3];
@@ -757,7 +888,7 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
       const int cK = step;          // chunk whose operands are built
       const bool k_on = cK < nch;
       const int bK = cK & 1;
-      _Float16* VOk = reinterpret_cast<_Float16*>(lds + kOffVO + bK * kVOBytes);
+      VE* VOk = reinterpret_cast<VE*>(lds + M::VO + bK * M::VOBytes);
       // ===== interval 1 =====
       load_w(cK + 1);
       bool bad_k = false;
@@ -769,21 +900,21 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
         if (rg == 0) { LAMb[bK * 64 + j0] = d.lam0; LAMb[bK * 64 + j0 + 1] = d.lam1; }
         // range of the raw inputs (|Bbar| <= |b| etc. when every |w| <= 1);
         // v is zero on a run with kSegZeroV
-        const uint32_t v0m = zero_v ? 0u : x.v[0], v1m = zero_v ? 0u : x.v[1];
-        const uint32_t v2m = zero_v ? 0u : x.v[2], v3m = zero_v ? 0u : x.v[3];
-        const uint32_t xs[12] = {x.b[0], x.b[1], x.b[2], x.b[3], x.k[0], x.k[1],
-                                 x.k[2], x.k[3], v0m, v1m, v2m, v3m};
+        const typename R::W v0m = zero_v ? R::zero() : x.v[0], v1m = zero_v ? R::zero() : x.v[1];
+        const typename R::W v2m = zero_v ? R::zero() : x.v[2], v3m = zero_v ? R::zero() : x.v[3];
+        const typename R::W xs[12] = {x.b[0], x.b[1], x.b[2], x.b[3], x.k[0], x.k[1],
+                                      x.k[2], x.k[3], v0m, v1m, v2m, v3m};
         // bitwise, not short-circuit: no branches
         bad_k = !(d.lam0 >= kMinLamL) | !(d.lam1 >= kMinLamL) |
-                any_half_ge(absmax_tree<12>(xs), 0x4700u) |   // |x| >= 2^15 (or NaN/Inf)
+                R::big(xs) |                                   // |x| >= 2^15 (or NaN/Inf)
                 bad_w;
         // the Gram operands, read after the second barrier
         float sfx0 = d.suf0, sfx1 = d.suf1;
   #pragma unroll
         for (int e = 3; e >= 0; --e) {
           const int t = 4 * rg + e;
-          put2p(Bbar, kM64, kP64, t, j0, bf_lo(x.b[e]) * sfx0, bf_hi(x.b[e]) * sfx1);
-          put2p(Kbar, kM64, kP64, t, j0, bf_lo(x.k[e]) * sfx0, bf_hi(x.k[e]) * sfx1);
+          put2p(Bbar, kM64, kP64, t, j0, R::c0(x.b[e]) * sfx0, R::c1(x.b[e]) * sfx1);
+          put2p(Kbar, kM64, kP64, t, j0, R::c0(x.k[e]) * sfx0, R::c1(x.k[e]) * sfx1);
           sfx0 *= w0[e]; sfx1 *= w1[e];
         }
       }
@@ -797,25 +928,31 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
         // the value side's operands, read in the next step: built here,
         // where this role waits on the value side anyway, from the same
         // products as the Gram operands (the same values)
-        _Float16* BbT = VOk + 2 * kM64;
-        _Float16* KbT = BbT + kMT;
-        _Float16* Vt = KbT + kMT;
+        VE* BbT = VOk + M::BbT;
+        VE* KbT = VOk + M::KbT;
+        VE* Vt = VOk + M::Vt;
         float sfx0 = suf0, sfx1 = suf1;
         float bt0[4], bt1[4], kt0[4], kt1[4], vt0[4], vt1[4];
   #pragma unroll
         for (int e = 3; e >= 0; --e) {
-          bt0[e] = bf_lo(x.b[e]) * sfx0; bt1[e] = bf_hi(x.b[e]) * sfx1;
-          kt0[e] = bf_lo(x.k[e]) * sfx0; kt1[e] = bf_hi(x.k[e]) * sfx1;
-          vt0[e] = zero_v ? 0.f : bf_lo(x.v[e]);
-          vt1[e] = zero_v ? 0.f : bf_hi(x.v[e]);
+          bt0[e] = R::c0(x.b[e]) * sfx0; bt1[e] = R::c1(x.b[e]) * sfx1;
+          kt0[e] = R::c0(x.k[e]) * sfx0; kt1[e] = R::c1(x.k[e]) * sfx1;
+          vt0[e] = zero_v ? 0.f : R::c0(x.v[e]);
+          vt1[e] = zero_v ? 0.f : R::c1(x.v[e]);
           sfx0 *= w0[e]; sfx1 *= w1[e];
         }
-        put4h(BbT, kP32, j0, 4 * rg, f32x4{bt0[0], bt0[1], bt0[2], bt0[3]});
-        put4h(BbT, kP32, j0 + 1, 4 * rg, f32x4{bt1[0], bt1[1], bt1[2], bt1[3]});
-        put4h(KbT, kP32, j0, 4 * rg, f32x4{kt0[0], kt0[1], kt0[2], kt0[3]});
-        put4h(KbT, kP32, j0 + 1, 4 * rg, f32x4{kt1[0], kt1[1], kt1[2], kt1[3]});
-        put4h(Vt, kP32, j0, 4 * rg, f32x4{vt0[0], vt0[1], vt0[2], vt0[3]});
-        put4h(Vt, kP32, j0 + 1, 4 * rg, f32x4{vt1[0], vt1[1], vt1[2], vt1[3]});
+        auto put4 = [&](VE* m, int row, const float (&v)[4]) {
+          if constexpr (PRE)
+            put4p(m, kMT, kP32, row, 4 * rg, f32x4{v[0], v[1], v[2], v[3]});
+          else
+            put4h(m, kP32, row, 4 * rg, f32x4{v[0], v[1], v[2], v[3]});
+        };
+        put4(BbT, j0, bt0);
+        put4(BbT, j0 + 1, bt1);
+        put4(KbT, j0, kt0);
+        put4(KbT, j0 + 1, kt1);
+        put4(Vt, j0, vt0);
+        put4(Vt, j0 + 1, vt1);
       }
       load_kbv(cK + 1);
       prep(min(cK + 1, nch - 1));   // the next chunk
@@ -868,8 +1005,8 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
       const int cV = step - 1;      // chunk whose value side is run
       const bool v_on = cV >= 0;
       const int bV = cV & 1;
-      const _Float16* VOv = reinterpret_cast<const _Float16*>(lds + kOffVO + bV * kVOBytes);
-      const _Float16* LLv = reinterpret_cast<const _Float16*>(lds + kOffLL + bV * kLLBytes);
+      const VE* VOv = reinterpret_cast<const VE*>(lds + M::VO + bV * M::VOBytes);
+      const VE* LLv = reinterpret_cast<const VE*>(lds + M::LL + bV * M::LLBytes);
       const int nV = min(kL, len - cV * kL);
       const int t0V = tok0 + cV * kL;
       // ===== interval 1 =====
@@ -877,33 +1014,51 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
       bool v_exact_done = false;
       float inv_s = 1.f;
       f16x8 Sf0 = {}, Sf1 = {}, Vf = {}, Xf = {};
+      F8 Sp0 = {}, Sp1 = {}, Vp = {}, Xp = {};     // precise plan: split pairs
       float inv_x = 1.f;
       if (v_on) {
         const bool exact = early_prev || gram_prev;
         if (!exact) {
-          f32x4 X[2];
-          const _Float16* Abar = VOv;
-          const _Float16* Vt = VOv + 2 * kM64 + 2 * kMT;
-          const _Float16* Aak = LLv;
-          float m = 0.f;
+          if constexpr (PRE) {
+            const __bf16* Abar = VOv + M::Abar;
+            const __bf16* Vt = VOv + M::Vt;
+            const __bf16* Aak = LLv + M::Aak;
+            Sp0 = frag8p(S[0], S[1]);
+            Sp1 = frag8p(S[2], S[3]);
+            Vp = ldp8(Vt, kMT, kP32, 16 * vb + n16, 0, g);
+            f32x4 X[2];
   #pragma unroll
-          for (int jt = 0; jt < 4; ++jt) m = scale_max4(S[jt], m);
-          const float sS = pow2_scale(wave_max(m), &inv_s);
-          Sf0 = frag8h(S[0], S[1], sS);
-          Sf1 = frag8h(S[2], S[3], sS);
-          Vf = ldh8(Vt, kP32, 16 * vb + n16, 0, g);
+            for (int tt = 0; tt < 2; ++tt) {
+              f32x4 c = mm3(ldp8(Abar, kM64, kP64, 16 * tt + n16, 0, g), Sp0, z);
+              c = mm3(ldp8(Abar, kM64, kP64, 16 * tt + n16, 32, g), Sp1, c);
+              X[tt] = mm3(ldp8(Aak, kM32, kP32, 16 * tt + n16, 0, g), Vp, c);
+            }
+            Xp = frag8p(X[0], X[1]);
+          } else {
+            f32x4 X[2];
+            const _Float16* Abar = VOv + M::Abar;
+            const _Float16* Vt = VOv + M::Vt;
+            const _Float16* Aak = LLv + M::Aak;
+            float m = 0.f;
   #pragma unroll
-          for (int tt = 0; tt < 2; ++tt) {
-            f32x4 cs = mmah(ldh8(Abar, kP64, 16 * tt + n16, 0, g), Sf0, z);
-            cs = mmah(ldh8(Abar, kP64, 16 * tt + n16, 32, g), Sf1, cs);
-            const f32x4 cv = mmah(ldh8(Aak, kP32, 16 * tt + n16, 0, g), Vf, z);
+            for (int jt = 0; jt < 4; ++jt) m = scale_max4(S[jt], m);
+            const float sS = pow2_scale(wave_max(m), &inv_s);
+            Sf0 = frag8h(S[0], S[1], sS);
+            Sf1 = frag8h(S[2], S[3], sS);
+            Vf = ldh8(Vt, kP32, 16 * vb + n16, 0, g);
   #pragma unroll
-            for (int r = 0; r < 4; ++r) X[tt][r] = fmaf(cs[r], inv_s, cv[r]);
+            for (int tt = 0; tt < 2; ++tt) {
+              f32x4 cs = mmah(ldh8(Abar, kP64, 16 * tt + n16, 0, g), Sf0, z);
+              cs = mmah(ldh8(Abar, kP64, 16 * tt + n16, 32, g), Sf1, cs);
+              const f32x4 cv = mmah(ldh8(Aak, kP32, 16 * tt + n16, 0, g), Vf, z);
+  #pragma unroll
+              for (int r = 0; r < 4; ++r) X[tt][r] = fmaf(cs[r], inv_s, cv[r]);
+            }
+            // X scaled into the fp16 range here, where the value side has
+            // slack, so that the second interval starts with U
+            const float sX = pow2_scale(wave_max(scale_max4(X[1], scale_max4(X[0], 0.f))), &inv_x);
+            Xf = frag8h(X[0], X[1], sX);
           }
-          // X scaled into the fp16 range here, where the value side has
-          // slack, so that the second interval starts with U
-          const float sX = pow2_scale(wave_max(scale_max4(X[1], scale_max4(X[0], 0.f))), &inv_x);
-          Xf = frag8h(X[0], X[1], sX);
           // T = [[D_0, 0], [T_10, D_1]], D_p = (I - A_pp)^-1, T_10 = D_1 A_10 D_0,
           // from A_ab of chunk cV: value wavefront 0 computes D_0 and
           // Y = A_10 D_0, wavefront 1 computes D_1, each value wavefront then
@@ -932,7 +1087,7 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
         }
         if (exact) {
           // the whole chunk token by token
-          exact_chunk(p, S, t0V, nV, h, vb, g, n16, zero_v, no_out);
+          exact_chunk<DT>(p, S, t0V, nV, h, vb, g, n16, zero_v, no_out);
           v_exact_done = true;
         }
       }
@@ -947,82 +1102,131 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
                   __builtin_amdgcn_ballot_w64(!(abs_max4(t10, 0.f) < kHalfSafe)) != 0;
         if (t_exact) {
           // T out of the fp16 range: the whole chunk token by token
-          exact_chunk(p, S, t0V, nV, h, vb, g, n16, zero_v, no_out);
+          exact_chunk<DT>(p, S, t0V, nV, h, vb, g, n16, zero_v, no_out);
         }
       }
       if (v_on && !v_exact_done && !t_exact) {
-        // value side, second half: U, O, state update of chunk cV
-        const _Float16* Rbar = VOv + kM64;
-        const _Float16* BbT = VOv + 2 * kM64;
-        const _Float16* KbT = BbT + kMT;
-        const _Float16* Mrb = LLv + kM32;
-        const _Float16* Mrk = LLv + 2 * kM32;
-        const float* lam = LAMb + bV * 64;
-        // Every LDS operand of the step's products is read first, and the
-        // products that do not involve U are issued before X and U are
-        // scaled, so that the LDS reads and those products overlap the two
-        // wavefront reductions instead of waiting one by one. Each sum is
-        // formed in the same order as when computed term by term.
-        f16x8 rb[2][2], mb[2], mk[2], bt[4], kt[4];
-        f32x4 lm[4];
-        // operand fragments of T's row tiles: k in [0,16) then [16,32)
-        const f16x8 Tf0 = ldh8(TT, kP32, n16, 0, g);
-        f16x8 Tf1;
-        {
-          const f16x4 t10h = h4(t10);
-          const f16x4 d1 = ldh4(TT, kP32, 16 + n16, 16 + 4 * g);
+        if constexpr (PRE) {
+          // value side, second half: U, O, state update of chunk cV, every
+          // product from split bf16 operands. The products that do not
+          // involve U are issued first; T's fp16 values split exactly.
+          const __bf16* Rbar = VOv + M::Rbar;
+          const __bf16* BbT = VOv + M::BbT;
+          const __bf16* KbT = VOv + M::KbT;
+          const __bf16* Mrb = LLv + M::Mrb;
+          const __bf16* Mrk = LLv + M::Mrk;
+          const float* lam = LAMb + bV * 64;
+          f32x4 O[2];
   #pragma unroll
-          for (int r = 0; r < 4; ++r) { Tf1[r] = t10h[r]; Tf1[4 + r] = d1[r]; }
-        }
-  #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          rb[tt][0] = ldh8(Rbar, kP64, 16 * tt + n16, 0, g);
-          rb[tt][1] = ldh8(Rbar, kP64, 16 * tt + n16, 32, g);
-          mk[tt] = ldh8(Mrk, kP32, 16 * tt + n16, 0, g);
-          mb[tt] = ldh8(Mrb, kP32, 16 * tt + n16, 0, g);
-        }
-  #pragma unroll
-        for (int jt = 0; jt < 4; ++jt) {
-          kt[jt] = ldh8(KbT, kP32, 16 * jt + n16, 0, g);
-          bt[jt] = ldh8(BbT, kP32, 16 * jt + n16, 0, g);
-          lm[jt] = *reinterpret_cast<const f32x4*>(lam + 16 * jt + 4 * g);
-        }
-        f32x4 cs[2], cvo[2], cvs[4];
-  #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          cs[tt] = mmah(Sf0, rb[tt][0], z);
-          cs[tt] = mmah(Sf1, rb[tt][1], cs[tt]);
-          cvo[tt] = mmah(Vf, mk[tt], z);
-        }
-  #pragma unroll
-        for (int jt = 0; jt < 4; ++jt) cvs[jt] = mmah(kt[jt], Vf, z);
-        f32x4 U[2];
-        U[0] = mmah(Tf0, Xf, z);
-        U[1] = mmah(Tf1, Xf, z);
-        float inv_u;
-        const float sU = pow2_scale(wave_max(scale_max4(U[1], scale_max4(U[0], 0.f))), &inv_u);
-        const float inv_ux = inv_u * inv_x;
-        const f16x8 Uf = frag8h(U[0], U[1], sU);
-  #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          const f32x4 cu = mmah(Uf, mb[tt], z);
-          const int t = 16 * tt + n16;
-          if (t < nV && !no_out) {
-            float4 ov;
-            ov.x = fmaf(cs[tt][0], inv_s, fmaf(cu[0], inv_ux, cvo[tt][0]));
-            ov.y = fmaf(cs[tt][1], inv_s, fmaf(cu[1], inv_ux, cvo[tt][1]));
-            ov.z = fmaf(cs[tt][2], inv_s, fmaf(cu[2], inv_ux, cvo[tt][2]));
-            ov.w = fmaf(cs[tt][3], inv_s, fmaf(cu[3], inv_ux, cvo[tt][3]));
-            *reinterpret_cast<float4*>(p.o + static_cast<size_t>(t0V + t) * rowstride
-                                       + static_cast<size_t>(h) * kN + 16 * vb + 4 * g) = ov;
+          for (int tt = 0; tt < 2; ++tt) {
+            O[tt] = mm3(Sp0, ldp8(Rbar, kM64, kP64, 16 * tt + n16, 0, g), z);
+            O[tt] = mm3(Sp1, ldp8(Rbar, kM64, kP64, 16 * tt + n16, 32, g), O[tt]);
+            O[tt] = mm3(Vp, ldp8(Mrk, kM32, kP32, 16 * tt + n16, 0, g), O[tt]);
           }
-        }
   #pragma unroll
-        for (int jt = 0; jt < 4; ++jt) {
-          const f32x4 cu = mmah(bt[jt], Uf, z);
+          for (int jt = 0; jt < 4; ++jt) {
+            const f32x4 lm = *reinterpret_cast<const f32x4*>(lam + 16 * jt + 4 * g);
+            f32x4 c;
   #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            S[jt][r] = fmaf(lm[jt][r], S[jt][r], fmaf(cu[r], inv_ux, cvs[jt][r]));
+            for (int r = 0; r < 4; ++r) c[r] = lm[r] * S[jt][r];
+            S[jt] = mm3(ldp8(KbT, kMT, kP32, 16 * jt + n16, 0, g), Vp, c);
+          }
+          f16x8 Tf1;
+          {
+            const f16x4 t10h = h4(t10);
+            const f16x4 d1 = ldh4(TT, kP32, 16 + n16, 16 + 4 * g);
+  #pragma unroll
+            for (int r = 0; r < 4; ++r) { Tf1[r] = t10h[r]; Tf1[4 + r] = d1[r]; }
+          }
+          const f32x4 U0 = mm3(split_f16(ldh8(TT, kP32, n16, 0, g)), Xp, z);
+          const f32x4 U1 = mm3(split_f16(Tf1), Xp, z);
+          const F8 Up = frag8p(U0, U1);
+  #pragma unroll
+          for (int tt = 0; tt < 2; ++tt) {
+            const f32x4 c = mm3(Up, ldp8(Mrb, kM32, kP32, 16 * tt + n16, 0, g), O[tt]);
+            const int t = 16 * tt + n16;
+            if (t < nV && !no_out)
+              *reinterpret_cast<float4*>(p.o + static_cast<size_t>(t0V + t) * rowstride
+                                         + static_cast<size_t>(h) * kN + 16 * vb + 4 * g) =
+                  make_float4(c[0], c[1], c[2], c[3]);
+          }
+  #pragma unroll
+          for (int jt = 0; jt < 4; ++jt)
+            S[jt] = mm3(ldp8(BbT, kMT, kP32, 16 * jt + n16, 0, g), Up, S[jt]);
+        } else {
+          // value side, second half: U, O, state update of chunk cV
+          const _Float16* Rbar = VOv + M::Rbar;
+          const _Float16* BbT = VOv + M::BbT;
+          const _Float16* KbT = VOv + M::KbT;
+          const _Float16* Mrb = LLv + M::Mrb;
+          const _Float16* Mrk = LLv + M::Mrk;
+          const float* lam = LAMb + bV * 64;
+          // Every LDS operand of the step's products is read first, and the
+          // products that do not involve U are issued before X and U are
+          // scaled, so that the LDS reads and those products overlap the two
+          // wavefront reductions instead of waiting one by one. Each sum is
+          // formed in the same order as when computed term by term.
+          f16x8 rb[2][2], mb[2], mk[2], bt[4], kt[4];
+          f32x4 lm[4];
+          // operand fragments of T's row tiles: k in [0,16) then [16,32)
+          const f16x8 Tf0 = ldh8(TT, kP32, n16, 0, g);
+          f16x8 Tf1;
+          {
+            const f16x4 t10h = h4(t10);
+            const f16x4 d1 = ldh4(TT, kP32, 16 + n16, 16 + 4 * g);
+  #pragma unroll
+            for (int r = 0; r < 4; ++r) { Tf1[r] = t10h[r]; Tf1[4 + r] = d1[r]; }
+          }
+  #pragma unroll
+          for (int tt = 0; tt < 2; ++tt) {
+            rb[tt][0] = ldh8(Rbar, kP64, 16 * tt + n16, 0, g);
+            rb[tt][1] = ldh8(Rbar, kP64, 16 * tt + n16, 32, g);
+            mk[tt] = ldh8(Mrk, kP32, 16 * tt + n16, 0, g);
+            mb[tt] = ldh8(Mrb, kP32, 16 * tt + n16, 0, g);
+          }
+  #pragma unroll
+          for (int jt = 0; jt < 4; ++jt) {
+            kt[jt] = ldh8(KbT, kP32, 16 * jt + n16, 0, g);
+            bt[jt] = ldh8(BbT, kP32, 16 * jt + n16, 0, g);
+            lm[jt] = *reinterpret_cast<const f32x4*>(lam + 16 * jt + 4 * g);
+          }
+          f32x4 cs[2], cvo[2], cvs[4];
+  #pragma unroll
+          for (int tt = 0; tt < 2; ++tt) {
+            cs[tt] = mmah(Sf0, rb[tt][0], z);
+            cs[tt] = mmah(Sf1, rb[tt][1], cs[tt]);
+            cvo[tt] = mmah(Vf, mk[tt], z);
+          }
+  #pragma unroll
+          for (int jt = 0; jt < 4; ++jt) cvs[jt] = mmah(kt[jt], Vf, z);
+          f32x4 U[2];
+          U[0] = mmah(Tf0, Xf, z);
+          U[1] = mmah(Tf1, Xf, z);
+          float inv_u;
+          const float sU = pow2_scale(wave_max(scale_max4(U[1], scale_max4(U[0], 0.f))), &inv_u);
+          const float inv_ux = inv_u * inv_x;
+          const f16x8 Uf = frag8h(U[0], U[1], sU);
+  #pragma unroll
+          for (int tt = 0; tt < 2; ++tt) {
+            const f32x4 cu = mmah(Uf, mb[tt], z);
+            const int t = 16 * tt + n16;
+            if (t < nV && !no_out) {
+              float4 ov;
+              ov.x = fmaf(cs[tt][0], inv_s, fmaf(cu[0], inv_ux, cvo[tt][0]));
+              ov.y = fmaf(cs[tt][1], inv_s, fmaf(cu[1], inv_ux, cvo[tt][1]));
+              ov.z = fmaf(cs[tt][2], inv_s, fmaf(cu[2], inv_ux, cvo[tt][2]));
+              ov.w = fmaf(cs[tt][3], inv_s, fmaf(cu[3], inv_ux, cvo[tt][3]));
+              *reinterpret_cast<float4*>(p.o + static_cast<size_t>(t0V + t) * rowstride
+                                         + static_cast<size_t>(h) * kN + 16 * vb + 4 * g) = ov;
+            }
+          }
+  #pragma unroll
+          for (int jt = 0; jt < 4; ++jt) {
+            const f32x4 cu = mmah(bt[jt], Uf, z);
+  #pragma unroll
+            for (int r = 0; r < 4; ++r)
+              S[jt][r] = fmaf(lm[jt][r], S[jt][r], fmaf(cu[r], inv_ux, cvs[jt][r]));
+          }
         }
       }
       const uint32_t f3 = barrier_or2(FLG, wv, lane, false, false);  // B3
@@ -1037,29 +1241,39 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
   }
 }
 
-}  // namespace
-
-hipError_t launch_chunked_p(const SeqArgs& args, hipStream_t stream,
-                            const WorkItem* dec, int32_t n_dec) {
+// The kernel instance for an input type and plan: fp32 inputs always take
+// the precise plan.
+template <bool SEG>
+hipError_t launch_p(const SeqArgs& args, bool precise, const SegItem* segs,
+                    hipStream_t stream, const WorkItem* dec, int32_t n_dec) {
   if (args.n_items <= 0) return hipSuccess;
   const int64_t blocks = static_cast<int64_t>(args.n_items) * args.H +
                          chunk_decode_blocks(n_dec, args.H);
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(chunk_p_kernel<false>, dim3(static_cast<unsigned>(blocks)),
-                     dim3(64 * kChunkPWaves), 0, stream, args, nullptr, dec, n_dec);
+  const dim3 grid(static_cast<unsigned>(blocks)), block(64 * kChunkPWaves);
+  if (args.dtype == WKV7_F32)
+    hipLaunchKernelGGL((chunk_p_kernel<SEG, WKV7_F32, true>), grid, block, 0,
+                       stream, args, segs, dec, n_dec);
+  else if (precise)
+    hipLaunchKernelGGL((chunk_p_kernel<SEG, WKV7_BF16, true>), grid, block, 0,
+                       stream, args, segs, dec, n_dec);
+  else
+    hipLaunchKernelGGL((chunk_p_kernel<SEG, WKV7_BF16, false>), grid, block, 0,
+                       stream, args, segs, dec, n_dec);
   return hipGetLastError();
 }
+}  // namespace
 
-hipError_t launch_chunked_p_seg(const SeqArgs& args, const SegItem* segs,
-                                hipStream_t stream, const WorkItem* dec,
-                                int32_t n_dec) {
-  if (args.n_items <= 0) return hipSuccess;
-  const int64_t blocks = static_cast<int64_t>(args.n_items) * args.H +
-                         chunk_decode_blocks(n_dec, args.H);
-  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(chunk_p_kernel<true>, dim3(static_cast<unsigned>(blocks)),
-                     dim3(64 * kChunkPWaves), 0, stream, args, segs, dec, n_dec);
-  return hipGetLastError();
+hipError_t launch_chunked_p(const SeqArgs& args, bool precise,
+                            hipStream_t stream, const WorkItem* dec,
+                            int32_t n_dec) {
+  return launch_p<false>(args, precise, nullptr, stream, dec, n_dec);
+}
+
+hipError_t launch_chunked_p_seg(const SeqArgs& args, bool precise,
+                                const SegItem* segs, hipStream_t stream,
+                                const WorkItem* dec, int32_t n_dec) {
+  return launch_p<true>(args, precise, segs, stream, dec, n_dec);
 }
 
 }  // namespace wkv7

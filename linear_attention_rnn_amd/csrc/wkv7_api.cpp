@@ -389,17 +389,17 @@ wkv7_status check_forward_args(int32_t dtype, int64_t T_tot, const void* r,
 }
 
 // Launches the kernels of a batch whose work description is on the device.
-// Split sequences run segment-parallel on the bf16 fast path (three
-// launches: segment transitions and zero-start states together with the
-// unsplit chunked sequences, the carry scan, the segments' outputs); on the
-// other chunked paths every chunked sequence runs whole.
+// Split sequences run segment-parallel (three launches: segment transitions
+// and zero-start states together with the unsplit chunked sequences, the
+// carry scan, the segments' outputs); otherwise every chunked sequence runs
+// whole. The chunked launches take the precise plan for fp32 inputs and
+// with CHUNK_PRECISE.
 // Decode items (single-token sequences) ride in trailing workgroups of the
 // batch's chunked launch when the two together fit the CUs in one round
 // (the chunked kernel holds one workgroup per CU); with segment-parallel
 // prefill that is the output launch (phase 3: one item per segment, never
 // more than the transition launch, which has two per non-last segment plus
-// the unsplit sequences). Otherwise, or when the chunked work takes another
-// kernel, they get a launch of their own. Short multi-token sequences take
+// the unsplit sequences). Otherwise they get a launch of their own. Short multi-token sequences take
 // the four-wavefront sequential kernel while the batch has few of them.
 // Every route computes the same bits for a sequential item.
 wkv7_status launch_batch(const wkv7_pool* p, const wkv7::Launch& L,
@@ -407,12 +407,12 @@ wkv7_status launch_batch(const wkv7_pool* p, const wkv7::Launch& L,
                          const void* k, const void* v, const void* a,
                          const void* b, float* o, hipStream_t hs) {
   wkv7::SeqArgs args{p->state, nullptr, 0, p->H, dtype, r, w, k, v, a, b, o};
-  const bool fast = dtype == WKV7_BF16 && !p->chunk_precise;
-  const bool segmented = L.n_phase3 > 0 && fast;
+  const bool precise = p->chunk_precise;
+  const bool segmented = L.n_phase3 > 0;
   const int32_t n_single = L.n_seq_single;
   const int32_t n_multi = L.n_seq - L.n_seq_single;
   bool fuse = false;
-  if (n_single > 0 && fast) {
+  if (n_single > 0) {
     const int64_t chunk_items = segmented ? L.n_phase3 : L.n_chunk_all;
     fuse = chunk_items > 0 &&
            chunk_items * p->H + wkv7::chunk_decode_blocks(n_single, p->H) <= p->n_cus;
@@ -440,21 +440,21 @@ wkv7_status launch_batch(const wkv7_pool* p, const wkv7::Launch& L,
     if (L.n_chunk_all > 0) {
       args.items = L.chunk_all;
       args.n_items = L.n_chunk_all;
-      hipError_t e = fuse ? wkv7::launch_chunked_p(args, hs, L.seq, n_single)
-                          : wkv7::launch_chunked(args, p->chunk_precise, hs);
+      hipError_t e = fuse ? wkv7::launch_chunked_p(args, precise, hs, L.seq, n_single)
+                          : wkv7::launch_chunked_p(args, precise, hs);
       if (e != hipSuccess) return fail_hip(e, "chunked kernel launch");
     }
     return WKV7_OK;
   }
   args.items = nullptr;
   args.n_items = L.n_phase1;
-  hipError_t e = wkv7::launch_chunked_p_seg(args, L.phase1, hs);
+  hipError_t e = wkv7::launch_chunked_p_seg(args, precise, L.phase1, hs);
   if (e != hipSuccess) return fail_hip(e, "segment transition launch");
   e = wkv7::launch_seg_scan(L.scan, L.n_scan, p->H, hs);
   if (e != hipSuccess) return fail_hip(e, "segment scan launch");
   args.n_items = L.n_phase3;
-  e = fuse ? wkv7::launch_chunked_p_seg(args, L.phase3, hs, L.seq, n_single)
-           : wkv7::launch_chunked_p_seg(args, L.phase3, hs);
+  e = fuse ? wkv7::launch_chunked_p_seg(args, precise, L.phase3, hs, L.seq, n_single)
+           : wkv7::launch_chunked_p_seg(args, precise, L.phase3, hs);
   if (e != hipSuccess) return fail_hip(e, "segment prefill launch");
   return WKV7_OK;
 }

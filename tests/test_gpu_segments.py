@@ -15,6 +15,11 @@ pytestmark = pytest.mark.gpu
 H = 3
 SEG = 256
 GUARD = 1e-2
+# the chunked plans (input type, precise mode) and their guards: the fast
+# plan for bf16 inputs, the precise plan (split bf16 operands throughout)
+# for fp32 inputs and on request
+PATHS = [(G.BF16, 0), (G.F32, 0), (G.BF16, 1)]
+PATH_GUARD = {(G.BF16, 0): GUARD, (G.F32, 0): 5e-4, (G.BF16, 1): 5e-4}
 
 
 def _bits_equal(a, b):
@@ -49,13 +54,15 @@ def _run(lens, seg=SEG, seed=0, dtype=G.BF16, precise=0, **draw):
     return e, o, S
 
 
+@pytest.mark.parametrize("dtype,precise", PATHS)
 @pytest.mark.parametrize("lens", [[600], [1, 600, 1024, 130, 2065, 3],
                                   [512, 513, 767, 768, 769]])
-def test_segments_match_oracle(lens):
-    e, o, S = _run(lens)
-    say(f"segments of {SEG}, lens {lens}: err {e:.3e}")
+def test_segments_match_oracle(lens, dtype, precise):
+    e, o, S = _run(lens, dtype=dtype, precise=precise)
+    say(f"segments of {SEG}, lens {lens}, {dtype}, precise {precise}: "
+        f"err {e:.3e}")
     assert np.all(np.isfinite(o.numpy())) and np.all(np.isfinite(S.numpy()))
-    assert e < GUARD
+    assert e < PATH_GUARD[dtype, precise]
 
 
 @pytest.mark.parametrize("w", [0.995, 0.9999])
@@ -74,13 +81,14 @@ def test_segments_carry_slowly_decaying_state(w):
     assert 0 < d < GUARD
 
 
-def test_segments_agree_with_unsplit_run():
+@pytest.mark.parametrize("dtype,precise", PATHS)
+def test_segments_agree_with_unsplit_run(dtype, precise):
     lens = [1, 1100, 70, 2048]
-    _, o1, S1 = _run(lens, seg=SEG, seed=5)
-    _, o2, S2 = _run(lens, seg=0, seed=5)
+    _, o1, S1 = _run(lens, seg=SEG, seed=5, dtype=dtype, precise=precise)
+    _, o2, S2 = _run(lens, seg=0, seed=5, dtype=dtype, precise=precise)
     e = max(rel_err(o1, o2.double().numpy()), rel_err(S1, S2.double().numpy()))
-    say(f"split vs unsplit: {e:.3e}")
-    assert e < GUARD
+    say(f"split vs unsplit, {dtype}, precise {precise}: {e:.3e}")
+    assert e < PATH_GUARD[dtype, precise]
 
 
 def test_segment_split_is_batch_invariant():
@@ -161,12 +169,7 @@ def test_segment_plan_and_graph_equal_forward():
             W.wkv7_pool_destroy(p)
 
 
-def test_segment_option_on_other_paths_and_validation():
-    # fp32 inputs and the precise mode take the whole-sequence kernels
-    e, _, _ = _run([700, 1], dtype=G.F32, seed=13)
-    assert e < 1e-3
-    e, _, _ = _run([700, 1], precise=1, seed=14)
-    assert e < 5e-4
+def test_segment_option_validation():
     pool = W.wkv7_pool_create(1, H, 64)
     try:
         for bad in (32, 100, -64, 1 << 31):

@@ -162,13 +162,14 @@ def decode_step_inputs(seed: int, step: int, ids: np.ndarray, H: int,
 
 
 def cfg_prefill(seed: int = 2, n_seq: int = 8, T: int = 4096, H: int = 32,
-                N: int = 64) -> Workload:
-    """Prefill: 8 fresh sequences of T=4096, H=32, bf16 inputs, zero state."""
+                N: int = 64, dtype: str = BF16) -> Workload:
+    """Prefill: 8 fresh sequences of T=4096, H=32, zero state; bf16 inputs
+    (the workload) or fp32 inputs of the same recipe."""
     rng = np.random.default_rng(seed)
     ids = np.arange(n_seq, dtype=np.int32)
-    b = make_batch(rng, ids, [T] * n_seq, H, N, BF16)
-    return Workload(f"prefill_b{n_seq}_t{T}_h{H}_bf16", n_seq, H, N, BF16, b,
-                    np.zeros(0, np.int32), None)
+    b = make_batch(rng, ids, [T] * n_seq, H, N, dtype)
+    return Workload(f"prefill_b{n_seq}_t{T}_h{H}_{dtype}", n_seq, H, N, dtype,
+                    b, np.zeros(0, np.int32), None)
 
 
 @dataclasses.dataclass
