@@ -326,7 +326,8 @@ def run_prefill_f32(steps: int = 5, warmup: int = 3, seed: int = 2):
             "hbm": {"achieved": bytes_alg / (k_ms * 1e-3) / 1e9,
                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": bytes_alg / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                    "bytes_per_launch": bytes_alg},
+                    "bytes_per_launch": bytes_alg,
+                    "traffic": load_traffic("prefill_f32", bytes_alg)},
             "steps": steps, "warmup": warmup}
 
 
