@@ -106,47 +106,58 @@ def test_extreme_decay_chunks(w, dtype, precise):
     assert e_o < 1e-4 and e_s < 1e-4
 
 
+@pytest.mark.parametrize("dtype,precise", PATHS)
 @pytest.mark.parametrize("name,factor", [("v", 1e5), ("k", 3e4)])
-def test_out_of_fp16_range_runs_exactly(name, factor):
-    """Inputs whose scaled operands exceed the fp16 range make the fast
-    chunked kernel run those chunks token by token: still exact."""
+def test_out_of_fp16_range_runs_exactly(name, factor, dtype, precise):
+    """Inputs at 2^15 or beyond make the chunked kernel run their chunks
+    token by token, in either plan (the fast plan's fp16 operands would
+    overflow; the precise plan keeps the same rule): exact, to fp32
+    rounding (about 1e-6 here, against 3e-5 and more for either plan's
+    products, so a chunk left on the MFMA path would fail the bound)."""
     lens = [130]
     H = 2
     ids = np.array([0], np.int32)
-    e_o, e_s, o, S = _run(ids, lens, H, "bf16", 1, seed=6,
-                          scale={name: factor})
-    say(f"large {name} x{factor:g}: o err {e_o:.3e}  S err {e_s:.3e}")
+    e_o, e_s, o, S = _run(ids, lens, H, dtype, 1, seed=6,
+                          scale={name: factor}, precise=precise)
+    say(f"large {name} x{factor:g} {dtype} precise={precise}: o err {e_o:.3e}  "
+        f"S err {e_s:.3e}")
     assert np.all(np.isfinite(o.numpy())) and np.all(np.isfinite(S.numpy()))
-    assert e_o < 1e-4 and e_s < 1e-4
+    assert e_o < 1e-5 and e_s < 1e-5
 
 
+@pytest.mark.parametrize("dtype,precise", PATHS)
 @pytest.mark.parametrize("name", ["a", "b", "r"])
-def test_single_large_input_runs_exactly(name):
+def test_single_large_input_runs_exactly(name, dtype, precise):
     """One element of a, b or r at 4e4 (beyond the fp16 operand range, one
     token): its chunk runs token by token (the raw-input range flags of
-    both key roles), the others on the fast path."""
+    both key roles), the others on the chunked products."""
     def edit(x):
         x[name][5, 1, 3] = 4.0e4
-    e_o, e_s, o, S = _run(np.array([0], np.int32), [100], 2, "bf16", 1,
-                          seed=7, edit=edit)
-    say(f"large single {name}: o err {e_o:.3e}  S err {e_s:.3e}")
+    e_o, e_s, o, S = _run(np.array([0], np.int32), [100], 2, dtype, 1,
+                          seed=7, edit=edit, precise=precise)
+    say(f"large single {name} {dtype} precise={precise}: o err {e_o:.3e}  "
+        f"S err {e_s:.3e}")
     assert np.all(np.isfinite(o.numpy())) and np.all(np.isfinite(S.numpy()))
-    assert e_o < GUARD["bf16", 0] and e_s < GUARD["bf16", 0]
+    assert e_o < GUARD[dtype, precise] and e_s < GUARD[dtype, precise]
 
 
-def test_growing_decay_runs_exactly():
-    """w above 1 (1.0625 on every channel): outside the fast path's range
-    (its check runs when a chunk's inputs are prepared), so every chunk
-    runs token by token."""
-    e_o, e_s, o, S = _run(np.array([0], np.int32), [130], 2, "bf16", 1,
-                          seed=8, w_override=1.0625)
-    say(f"w = 1.0625: o err {e_o:.3e}  S err {e_s:.3e}")
+@pytest.mark.parametrize("dtype,precise", PATHS)
+def test_growing_decay_runs_exactly(dtype, precise):
+    """w above 1 (1.0625 on every channel): outside the chunked form's
+    range (its check runs when a chunk's inputs are prepared), so every
+    chunk runs token by token."""
+    e_o, e_s, o, S = _run(np.array([0], np.int32), [130], 2, dtype, 1,
+                          seed=8, w_override=1.0625, precise=precise)
+    say(f"w = 1.0625 {dtype} precise={precise}: o err {e_o:.3e}  S err {e_s:.3e}")
     assert np.all(np.isfinite(o.numpy())) and np.all(np.isfinite(S.numpy()))
-    assert e_o < 1e-4 and e_s < 1e-4
+    # fp32 rounding of the token-by-token path (about 4e-6 here, against
+    # 3e-5 and more for either plan's products)
+    assert e_o < 1e-5 and e_s < 1e-5
 
 
+@pytest.mark.parametrize("dtype,precise", PATHS)
 @pytest.mark.parametrize("c", [1.0, 2.0])
-def test_t_out_of_fp16_range_runs_exactly(c):
+def test_t_out_of_fp16_range_runs_exactly(c, dtype, precise):
     """a = b = u with |u|^2 = c and w = 1 make A_ab = c below the
     diagonal, so T = (I - A_ab)^-1 grows like (1 + c)^(t - s) within the
     first 32-token chunk: with c = 1 only the off-diagonal block T_10
@@ -161,11 +172,12 @@ def test_t_out_of_fp16_range_runs_exactly(c):
         for name in ("a", "b"):
             x[name][:] = u.to(x[name].dtype)
         x["w"][:] = 1.0
-    e_o, e_s, o, S = _run(np.array([0], np.int32), [40], 2, "bf16", 1,
-                          seed=9, edit=edit)
-    say(f"T out of range, c = {c}: o err {e_o:.3e}  S err {e_s:.3e}")
+    e_o, e_s, o, S = _run(np.array([0], np.int32), [40], 2, dtype, 1,
+                          seed=9, edit=edit, precise=precise)
+    say(f"T out of range, c = {c} {dtype} precise={precise}: o err {e_o:.3e}  "
+        f"S err {e_s:.3e}")
     assert np.all(np.isfinite(o.numpy())) and np.all(np.isfinite(S.numpy()))
-    assert e_o < GUARD["bf16", 0] and e_s < GUARD["bf16", 0]
+    assert e_o < GUARD[dtype, precise] and e_s < GUARD[dtype, precise]
 
 
 def test_chunked_matches_sequential_within_rounding():
