@@ -1,8 +1,9 @@
 """The allocation-free forward (wkv7_forward_noalloc) against wkv7_forward,
 through the C ABI: the same bits for outputs and slot states on two calls in
 a row, the second with a smaller batch, with segment-parallel prefill off
-and on (segment buffers in the static scratch), and the size limits
-rejected before any device work."""
+and on (segment buffers in the static scratch; bf16 inputs, and fp32 inputs,
+whose chunked sequences take the kernel's precise plan), and the size
+limits rejected before any device work."""
 import numpy as np
 import pytest
 import torch
@@ -26,8 +27,15 @@ def _call(fn, pool, ids, cu, x, T, H):
     return o
 
 
-@pytest.mark.parametrize("seg_len", [0, 512])
-def test_noalloc_equals_forward_on_two_calls(seg_len):
+def _as_f32(b):
+    """The same batch with fp32 inputs (the bf16 values, exactly)."""
+    return G.Batch(G.F32, b.H, b.N, b.slot_ids, b.cu_seqlens,
+                   {n: b.inputs[n].to(torch.float32) for n in G.NAMES})
+
+
+@pytest.mark.parametrize("seg_len,dtype", [(0, G.BF16), (512, G.BF16),
+                                           (512, G.F32)])
+def test_noalloc_equals_forward_on_two_calls(seg_len, dtype):
     H, n_slots = 12, 128
     lay = G.cfg_mixed_layers(seed=3, n_layers=1)[0]
     rng = np.random.default_rng(40)
@@ -39,9 +47,11 @@ def test_noalloc_equals_forward_on_two_calls(seg_len):
     pre2 = rng.choice(free, 2, replace=False).astype(np.int32)
     ids2 = np.concatenate([dec2, pre2]).astype(np.int32)
     b2 = G.make_batch(rng, ids2, [1] * 16 + [130, 1100], H, N, G.BF16)
-    calls = [(lay.batch.slot_ids, lay.batch.cu_seqlens, lay.batch),
-             (b2.slot_ids, b2.cu_seqlens, b2)]
-    say(f"noalloc vs forward, segment length {seg_len}: calls of "
+    b1 = lay.batch
+    if dtype == G.F32:
+        b1, b2 = _as_f32(b1), _as_f32(b2)
+    calls = [(b1.slot_ids, b1.cu_seqlens, b1), (b2.slot_ids, b2.cu_seqlens, b2)]
+    say(f"noalloc vs forward, segment length {seg_len}, {dtype}: calls of "
         f"{lay.batch.T_tot} and {b2.T_tot} tokens")
     pools = [W.wkv7_pool_create(n_slots, H, N) for _ in range(2)]
     try:
