@@ -457,7 +457,7 @@ __device__ __forceinline__ void pad_raw(RawS<DT>& x, int n, int rg) {
   }
 }
 
-// ---- T = (I - A_ab)^-1 on the key wavefront that computes A_ab ----
+// ---- T = (I - A_ab)^-1 from fp16 fragments (value wavefronts 0 and 1) ----
 // A 16x16 matrix M is held as two fp16 operand fragments and their fp32
 // values:
 //   row(M): lane (g, n) holds M[n][4g + e]   (left operand of a product)
@@ -465,7 +465,8 @@ __device__ __forceinline__ void pad_raw(RawS<DT>& x, int n, int rg) {
 //                                             result layout of a product)
 // so L*R gives col(LR) = mfma(row(L), col(R)) and row(LR) = col((LR)^T) =
 // mfma(col(R), row(L)): every product yields both fragments of its result.
-// T is consumed as fp16, so fp16 operands with fp32 accumulation suffice.
+// T is kept in fp16 (the precise plan splits its fp16 values exactly into
+// bf16 pairs), so fp16 operands with fp32 accumulation suffice.
 struct Frag { f16x4 row, col; f32x4 frow, fcol; };
 
 __device__ __forceinline__ f32x4 mmh16(f16x4 a, f16x4 b, f32x4 c) {
@@ -676,8 +677,8 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
   // registers, and prepared one step before their operands are built
   // (padded; running products of w over the thread's 4 rows in P0/P1; the
   // s wavefronts post the rows' totals in TOT), in the previous step's
-  // second interval. The third barrier orders the TOT writes before their
-  // reads. Each loop is instantiated once per wavefront W (= wv & 3): its
+  // second interval. The end-of-step barrier orders the TOT writes before
+  // their reads. Each loop is instantiated once per wavefront W (= wv & 3): its
   // row groups, Gram matrix and LDS destinations are then constants.
   // The next chunk's loads and preparation happen on every path, with the
   // chunk index clamped to the last one (whose totals no step then reads):
@@ -736,13 +737,12 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
       const int bK = cK & 1;
       VE* VOk = reinterpret_cast<VE*>(lds + M::VO + bK * M::VOBytes);
       VE* LLk = reinterpret_cast<VE*>(lds + M::LL + bK * M::LLBytes);
-      const int t0K = tok0 + cK * kL;
       // ===== interval 1 =====
       bool bad_k = false;
       if (k_on) {
         const Dec d = chunk_decays(Wc);
         // hardware reciprocal (1 ulp): the scaled Gram operands are split into
-        // bf16 pairs, far coarser; a lam below the fast path's range takes the
+        // bf16 pairs, far coarser; a lam below the chunked form's range takes the
         // token-by-token path, which does not use these operands
         const float inv0 = __builtin_amdgcn_rcpf(d.lam0), inv1 = __builtin_amdgcn_rcpf(d.lam1);
         VE* Abar = VOk + M::Abar;
@@ -776,7 +776,7 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
       // no code moves across: work of the second interval hoisted above
       // the barrier would wait there for the loads just issued
       __builtin_amdgcn_sched_barrier(0);
-      __syncthreads();                                            // B2
+      __syncthreads();                                            // mid-step barrier
       __builtin_amdgcn_sched_barrier(0);
       // ===== interval 2 =====
       float gmax = 0.f;
@@ -849,7 +849,7 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
       }
       prep(min(cK + 1, nch - 1));   // the next chunk
       (void)barrier_or2(FLG, wv, lane, k_on && bad_k,
-                        k_on && !(gmax < kHalfSafe));             // B3
+                        k_on && !(gmax < kHalfSafe));  // end-of-step barrier
     }
   };
 
@@ -908,7 +908,7 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
         bad_k = !(d.lam0 >= kMinLamL) | !(d.lam1 >= kMinLamL) |
                 R::big(xs) |                                   // |x| >= 2^15 (or NaN/Inf)
                 bad_w;
-        // the Gram operands, read after the second barrier
+        // the Gram operands, read after the mid-step barrier
         float sfx0 = d.suf0, sfx1 = d.suf1;
   #pragma unroll
         for (int e = 3; e >= 0; --e) {
@@ -921,7 +921,7 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
       // no code moves across: work of the second interval hoisted above
       // the barrier would wait there for loads
       __builtin_amdgcn_sched_barrier(0);
-      __syncthreads();                                            // B2
+      __syncthreads();                                            // mid-step barrier
       __builtin_amdgcn_sched_barrier(0);
       // ===== interval 2 =====
       if (k_on) {
@@ -956,7 +956,7 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
       }
       load_kbv(cK + 1);
       prep(min(cK + 1, nch - 1));   // the next chunk
-      (void)barrier_or2(FLG, wv, lane, k_on && bad_k, false);     // B3
+      (void)barrier_or2(FLG, wv, lane, k_on && bad_k, false);  // end of step
     }
   };
 
@@ -994,7 +994,7 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
     }
     __syncthreads();                                              // TOT of chunk 0
     // fallback flags of chunk step - 1, known from the end of the step
-    // before: early (its inputs or decays out of the fast path's range)
+    // before: early (its inputs or decays out of the chunked form's range)
     // and gram (its Gram matrices or T out of the fp16 range)
     bool early_prev = false, gram_prev = false;
     // The start state has arrived before the loop: without this wait the
@@ -1091,7 +1091,7 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
           v_exact_done = true;
         }
       }
-      __syncthreads();                                            // B2
+      __syncthreads();                                            // mid-step barrier
       // ===== interval 2 =====
       bool t_exact = false;
       f32x4 t10 = z;
@@ -1229,7 +1229,7 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
           }
         }
       }
-      const uint32_t f3 = barrier_or2(FLG, wv, lane, false, false);  // B3
+      const uint32_t f3 = barrier_or2(FLG, wv, lane, false, false);  // end of step
       early_prev = (f3 & 1u) != 0;
       gram_prev = (f3 & 2u) != 0;
     }
