@@ -19,10 +19,10 @@ from tests import precision_plans as PP
 N = 64
 
 
-def _heads(T, n_heads, seed):
-    """bf16-rounded inputs of the workload recipe, zero start state."""
+def _heads(T, n_heads, seed, dtype=G.BF16):
+    """Inputs of the workload recipe rounded to `dtype`, zero start state."""
     rng = np.random.default_rng(seed)
-    b = G.make_batch(rng, [0], [T], n_heads, N, G.BF16)
+    b = G.make_batch(rng, [0], [T], n_heads, N, dtype)
     x = b.inputs64()
     for h in range(n_heads):
         xh = {n: x[n][:, h] for n in G.NAMES}
@@ -30,9 +30,9 @@ def _heads(T, n_heads, seed):
         yield xh, o_ref, S_ref
 
 
-def _worst(plan, T, n_heads, seed):
+def _worst(plan, T, n_heads, seed, dtype=G.BF16):
     eo = es = 0.0
-    for xh, o_ref, S_ref in _heads(T, n_heads, seed):
+    for xh, o_ref, S_ref in _heads(T, n_heads, seed, dtype):
         o, S = plan(np.zeros((N, N)), **xh)
         eo = max(eo, rel_max_err(o, o_ref))
         es = max(es, rel_max_err(S, S_ref))
@@ -69,6 +69,29 @@ def test_default_bf16_plan_and_its_growth_with_length():
         assert eo > 1e-4          # fp16 rounding is modelled
     assert res[8192][0] < 1.5 * res[4096][0]
     assert res[8192][1] < 1.5 * res[4096][1]
+
+
+@pytest.mark.parametrize("dtype", [G.F32, G.BF16])
+def test_precise_plan(dtype):
+    """The chunked kernel's precise plan (fp32 inputs, bf16 on request):
+    about a tenth of the fp32-input bar of 1e-3 at the prefill length, with
+    T in fp16 as the fast plan forms it, and no material growth from 4096
+    to 8192 tokens."""
+    res = {T: _worst(PP.precise_sequence, T, 2, seed=700 + T, dtype=dtype)
+           for T in (4096, 8192)}
+    for T, (eo, es) in res.items():
+        print(f"precise plan, {dtype} inputs, T={T}: o {eo:.2e}  S {es:.2e}")
+        assert eo < 3e-4 and es < 3e-4
+        assert eo > 1e-6          # the model really rounds
+    assert res[8192][0] < 1.5 * res[4096][0]
+
+
+def test_fast_plan_would_miss_the_fp32_bar():
+    """fp32 inputs take the precise plan because the fast plan's single fp16
+    value-side operands would spend more than the fp32-input bar."""
+    eo, _ = _worst(PP.fast_sequence, 1024, 2, seed=801, dtype=G.F32)
+    print(f"fast plan on fp32 inputs, T=1024: o {eo:.2e}")
+    assert eo > 1e-3
 
 
 def test_single_bf16_operands_would_miss_the_bar():
