@@ -608,7 +608,9 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
   __bf16* Rhat = GR + 2 * kM64;            // pair [t][j]
   __bf16* Bbar = GR + 4 * kM64;            // pair [s][j]
   __bf16* Kbar = GR + 6 * kM64;            // pair [s][j]
-  _Float16* AB = reinterpret_cast<_Float16*>(lds + M::AB);   // A_ab [t][s], then [s][t]
+  // fast plan: A_ab [t][s], then [s][t]; precise plan: T [t][s] of chunks
+  // of even and odd index
+  _Float16* AB = reinterpret_cast<_Float16*>(lds + M::AB);
   float* TOT = reinterpret_cast<float*>(lds + M::TOT);
   float* LAMb = reinterpret_cast<float*>(lds + M::LAM);
   uint32_t* FLG = reinterpret_cast<uint32_t*>(lds + M::FLG);
@@ -808,7 +810,32 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
             gt[ti++] = c;
           }
         }
-        if (W == 0) {
+        if (W == 0 && PRE) {
+          // T = (I - A_ab)^-1 of this chunk, from the Gram tiles in
+          // registers: tile ti holds C[s][t] = A_ab[t][s], so lane (g, n)
+          // holds A_ab[16 tt + n][16 st + 4 g + r], the row fragment of
+          // block (tt, st); a block's column fragment is its product with
+          // the identity. The value side reads T's rows a step later; T's
+          // range joins the Gram flag.
+          f32x4 icol;
+  #pragma unroll
+          for (int r = 0; r < 4; ++r) icol[r] = (4 * g + r == n16) ? 1.f : 0.f;
+          const f16x4 ic = h4(icol);
+          const f16x4 r00 = h4(gt[0]), r10 = h4(gt[1]), r11 = h4(gt[2]);
+          const Frag D0 = inverse_unit_lower(r00, h4(mmh16(r00, ic, z)), g, n16);
+          const Frag D1 = inverse_unit_lower(r11, h4(mmh16(r11, ic, z)), g, n16);
+          // col(Y) = A_10 D_0; row(T_10) = row(D_1 Y) from col(Y) and row(D_1)
+          const f16x4 ycol = h4(mmh16(r10, D0.col, z));
+          const f32x4 t10 = mmh16(ycol, D1.row, z);
+  #pragma unroll
+          for (int ti2 = 0; ti2 < 3; ++ti2) gmax = abs_max4(gt[ti2], gmax);
+          gmax = abs_max4(D0.frow, abs_max4(D1.frow, abs_max4(t10, gmax)));
+          _Float16* Tb = AB + bK * kM32;
+          put4h(Tb, kP32, n16, 4 * g, D0.frow);
+          put4h(Tb, kP32, n16, 16 + 4 * g, z);
+          put4h(Tb, kP32, 16 + n16, 4 * g, t10);
+          put4h(Tb, kP32, 16 + n16, 16 + 4 * g, D1.frow);
+        } else if (W == 0) {
           // A_ab in fp16 as [t][s] rows and as [s][t] rows (tile ti holds
           // C[s][t] = A_ab[t][s]): T's operand fragments, read by the value
           // side in the next step
@@ -1014,17 +1041,25 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
       bool v_exact_done = false;
       float inv_s = 1.f;
       f16x8 Sf0 = {}, Sf1 = {}, Vf = {}, Xf = {};
-      F8 Sp0 = {}, Sp1 = {}, Vp = {}, Xp = {};     // precise plan: split pairs
+      // precise plan: V and X as split pairs, and the part of O that
+      // involves neither U nor the new state
+      F8 Vp = {}, Xp = {};
+      f32x4 Op[2] = {};
       float inv_x = 1.f;
       if (v_on) {
         const bool exact = early_prev || gram_prev;
         if (!exact) {
           if constexpr (PRE) {
+            // X, and O's products with the old state and with V (T was
+            // formed on the key side): the split state is not needed after
+            // this interval
             const __bf16* Abar = VOv + M::Abar;
+            const __bf16* Rbar = VOv + M::Rbar;
             const __bf16* Vt = VOv + M::Vt;
             const __bf16* Aak = LLv + M::Aak;
-            Sp0 = frag8p(S[0], S[1]);
-            Sp1 = frag8p(S[2], S[3]);
+            const __bf16* Mrk = LLv + M::Mrk;
+            const F8 Sp0 = frag8p(S[0], S[1]);
+            const F8 Sp1 = frag8p(S[2], S[3]);
             Vp = ldp8(Vt, kMT, kP32, 16 * vb + n16, 0, g);
             f32x4 X[2];
   #pragma unroll
@@ -1034,6 +1069,12 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
               X[tt] = mm3(ldp8(Aak, kM32, kP32, 16 * tt + n16, 0, g), Vp, c);
             }
             Xp = frag8p(X[0], X[1]);
+  #pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+              Op[tt] = mm3(Sp0, ldp8(Rbar, kM64, kP64, 16 * tt + n16, 0, g), z);
+              Op[tt] = mm3(Sp1, ldp8(Rbar, kM64, kP64, 16 * tt + n16, 32, g), Op[tt]);
+              Op[tt] = mm3(Vp, ldp8(Mrk, kM32, kP32, 16 * tt + n16, 0, g), Op[tt]);
+            }
           } else {
             f32x4 X[2];
             const _Float16* Abar = VOv + M::Abar;
@@ -1058,31 +1099,31 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
             // slack, so that the second interval starts with U
             const float sX = pow2_scale(wave_max(scale_max4(X[1], scale_max4(X[0], 0.f))), &inv_x);
             Xf = frag8h(X[0], X[1], sX);
-          }
-          // T = [[D_0, 0], [T_10, D_1]], D_p = (I - A_pp)^-1, T_10 = D_1 A_10 D_0,
-          // from A_ab of chunk cV: value wavefront 0 computes D_0 and
-          // Y = A_10 D_0, wavefront 1 computes D_1, each value wavefront then
-          // T_10 = D_1 Y in the second interval. Each posts whether its
-          // part left the fp16 range.
-          const _Float16* ABr = AB;
-          const _Float16* ABt = ABr + kM32;
-          if (vb == 0) {
-            const Frag D0 = inverse_unit_lower(ldh4(ABr, kP32, n16, 4 * g),
-                                               ldh4(ABt, kP32, n16, 4 * g), g, n16);
-            // col(Y) = A_10 D_0 from row(A_10) and col(D_0)
-            const f16x4 ycol = h4(mmh16(ldh4(ABr, kP32, 16 + n16, 4 * g), D0.col, z));
-            put4h(TT, kP32, n16, 4 * g, D0.frow);
-            put4h(TT, kP32, n16, 16 + 4 * g, z);
-            *reinterpret_cast<f16x4*>(YC + 4 * lane) = ycol;
-            const bool out = __builtin_amdgcn_ballot_w64(!(abs_max4(D0.frow, 0.f) < kHalfSafe)) != 0;
-            if (lane == 0) TFL[0] = out ? 1u : 0u;
-          } else if (vb == 1) {
-            const Frag D1 = inverse_unit_lower(ldh4(ABr, kP32, 16 + n16, 16 + 4 * g),
-                                               ldh4(ABt, kP32, 16 + n16, 16 + 4 * g), g, n16);
-            put4h(TT, kP32, 16 + n16, 16 + 4 * g, D1.frow);
-            *reinterpret_cast<f16x4*>(D1R + 4 * lane) = D1.row;
-            const bool out = __builtin_amdgcn_ballot_w64(!(abs_max4(D1.frow, 0.f) < kHalfSafe)) != 0;
-            if (lane == 0) TFL[1] = out ? 1u : 0u;
+            // T = [[D_0, 0], [T_10, D_1]], D_p = (I - A_pp)^-1, T_10 = D_1 A_10 D_0,
+            // from A_ab of chunk cV: value wavefront 0 computes D_0 and
+            // Y = A_10 D_0, wavefront 1 computes D_1, each value wavefront then
+            // T_10 = D_1 Y in the second interval. Each posts whether its
+            // part left the fp16 range.
+            const _Float16* ABr = AB;
+            const _Float16* ABt = ABr + kM32;
+            if (vb == 0) {
+              const Frag D0 = inverse_unit_lower(ldh4(ABr, kP32, n16, 4 * g),
+                                                 ldh4(ABt, kP32, n16, 4 * g), g, n16);
+              // col(Y) = A_10 D_0 from row(A_10) and col(D_0)
+              const f16x4 ycol = h4(mmh16(ldh4(ABr, kP32, 16 + n16, 4 * g), D0.col, z));
+              put4h(TT, kP32, n16, 4 * g, D0.frow);
+              put4h(TT, kP32, n16, 16 + 4 * g, z);
+              *reinterpret_cast<f16x4*>(YC + 4 * lane) = ycol;
+              const bool out = __builtin_amdgcn_ballot_w64(!(abs_max4(D0.frow, 0.f) < kHalfSafe)) != 0;
+              if (lane == 0) TFL[0] = out ? 1u : 0u;
+            } else if (vb == 1) {
+              const Frag D1 = inverse_unit_lower(ldh4(ABr, kP32, 16 + n16, 16 + 4 * g),
+                                                 ldh4(ABt, kP32, 16 + n16, 16 + 4 * g), g, n16);
+              put4h(TT, kP32, 16 + n16, 16 + 4 * g, D1.frow);
+              *reinterpret_cast<f16x4*>(D1R + 4 * lane) = D1.row;
+              const bool out = __builtin_amdgcn_ballot_w64(!(abs_max4(D1.frow, 0.f) < kHalfSafe)) != 0;
+              if (lane == 0) TFL[1] = out ? 1u : 0u;
+            }
           }
         }
         if (exact) {
@@ -1095,7 +1136,8 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
       // ===== interval 2 =====
       bool t_exact = false;
       f32x4 t10 = z;
-      if (v_on && !v_exact_done) {
+      // (the precise plan formed T and checked its range on the key side)
+      if (!PRE && v_on && !v_exact_done) {
         t10 = mmh16(*reinterpret_cast<const f16x4*>(YC + 4 * lane),
                     *reinterpret_cast<const f16x4*>(D1R + 4 * lane), z);
         t_exact = (TFL[0] | TFL[1]) != 0 ||
@@ -1107,22 +1149,13 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
       }
       if (v_on && !v_exact_done && !t_exact) {
         if constexpr (PRE) {
-          // value side, second half: U, O, state update of chunk cV, every
-          // product from split bf16 operands. The products that do not
-          // involve U are issued first; T's fp16 values split exactly.
-          const __bf16* Rbar = VOv + M::Rbar;
+          // value side, second half: U, the rest of O, the state update of
+          // chunk cV, every product from split bf16 operands. The state's
+          // products with V are issued first; T's fp16 values split exactly.
           const __bf16* BbT = VOv + M::BbT;
           const __bf16* KbT = VOv + M::KbT;
           const __bf16* Mrb = LLv + M::Mrb;
-          const __bf16* Mrk = LLv + M::Mrk;
           const float* lam = LAMb + bV * 64;
-          f32x4 O[2];
-  #pragma unroll
-          for (int tt = 0; tt < 2; ++tt) {
-            O[tt] = mm3(Sp0, ldp8(Rbar, kM64, kP64, 16 * tt + n16, 0, g), z);
-            O[tt] = mm3(Sp1, ldp8(Rbar, kM64, kP64, 16 * tt + n16, 32, g), O[tt]);
-            O[tt] = mm3(Vp, ldp8(Mrk, kM32, kP32, 16 * tt + n16, 0, g), O[tt]);
-          }
   #pragma unroll
           for (int jt = 0; jt < 4; ++jt) {
             const f32x4 lm = *reinterpret_cast<const f32x4*>(lam + 16 * jt + 4 * g);
@@ -1131,19 +1164,13 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
             for (int r = 0; r < 4; ++r) c[r] = lm[r] * S[jt][r];
             S[jt] = mm3(ldp8(KbT, kMT, kP32, 16 * jt + n16, 0, g), Vp, c);
           }
-          f16x8 Tf1;
-          {
-            const f16x4 t10h = h4(t10);
-            const f16x4 d1 = ldh4(TT, kP32, 16 + n16, 16 + 4 * g);
-  #pragma unroll
-            for (int r = 0; r < 4; ++r) { Tf1[r] = t10h[r]; Tf1[4 + r] = d1[r]; }
-          }
-          const f32x4 U0 = mm3(split_f16(ldh8(TT, kP32, n16, 0, g)), Xp, z);
-          const f32x4 U1 = mm3(split_f16(Tf1), Xp, z);
+          const _Float16* Tb = AB + bV * kM32;
+          const f32x4 U0 = mm3(split_f16(ldh8(Tb, kP32, n16, 0, g)), Xp, z);
+          const f32x4 U1 = mm3(split_f16(ldh8(Tb, kP32, 16 + n16, 0, g)), Xp, z);
           const F8 Up = frag8p(U0, U1);
   #pragma unroll
           for (int tt = 0; tt < 2; ++tt) {
-            const f32x4 c = mm3(Up, ldp8(Mrb, kM32, kP32, 16 * tt + n16, 0, g), O[tt]);
+            const f32x4 c = mm3(Up, ldp8(Mrb, kM32, kP32, 16 * tt + n16, 0, g), Op[tt]);
             const int t = 16 * tt + n16;
             if (t < nV && !no_out)
               *reinterpret_cast<float4*>(p.o + static_cast<size_t>(t0V + t) * rowstride
