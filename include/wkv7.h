@@ -101,7 +101,8 @@ enum {
    * value-side products single fp16 operands (the state and intermediates
    * scaled by powers of two), about 3e-3 of max|err|/rms(o) on the
    * workloads' inputs. 1: every product uses split bf16 operands, about
-   * 1e-4, roughly twice the work. fp32 inputs always use 1. */
+   * 1e-4, in about 1.5 times the time (the value-side products take three
+   * matrix-core operations each). fp32 inputs always use 1. */
   WKV7_OPT_CHUNK_PRECISE = 2,
   /* Segment-parallel prefill, for batches with few long sequences (the
    * chunked kernel runs one workgroup per (sequence, head), so a handful of
