@@ -195,8 +195,9 @@ def run_decode(steps: int, warmup: int, seed: int = 1):
 
 
 def chunk_mfma_flops_per_chunk_head() -> int:
-    """MFMA flops the bf16 chunked-prefill kernel issues per 32-token chunk
-    and head, from the instructions in its compiled loop body: each of the
+    """MFMA flops the chunked-prefill kernel's fast plan (bf16 inputs) issues
+    per 32-token chunk and head, from the instructions in its compiled loop
+    body: each of the
     4 t wavefronts issues 18 v_mfma_f32_16x16x32_bf16 (its Gram matrix),
     each of the 4 value wavefronts 24 v_mfma_f32_16x16x32_f16 and one
     v_mfma_f32_16x16x16_f16 (T_10), and the two value wavefronts that build
@@ -205,7 +206,17 @@ def chunk_mfma_flops_per_chunk_head() -> int:
     return 4 * 18 * 16384 + 4 * 24 * 16384 + (4 + 20) * 8192
 
 
-CHUNK_L = 32        # chunk length of the bf16 chunked-prefill kernel
+def chunk_mfma_flops_per_chunk_head_precise() -> int:
+    """MFMA flops of the chunked kernel's precise plan per 32-token chunk and
+    head, from the instructions its compiled loop issues (383 per chunk and
+    head in the SQ counters): the 4 t wavefronts' Gram products as in the
+    fast plan, 72 v_mfma_f32_16x16x32_bf16 on each value wavefront (X 18,
+    U 6, O 24, the state 24), and T's 23 v_mfma_f32_16x16x16_f16 on the Gram
+    wavefront."""
+    return 4 * 18 * 16384 + 4 * 72 * 16384 + 23 * 8192
+
+
+CHUNK_L = 32        # chunk length of the chunked-prefill kernel
 
 
 def prefill_alg_flops_per_token_head(L: int = CHUNK_L) -> float:
@@ -319,6 +330,8 @@ def run_prefill_f32(steps: int = 5, warmup: int = 3, seed: int = 2):
     k_ms = float(np.mean(times))
     tokens = n_seq * T
     bytes_alg = tokens * H * (6 * N * 4 + N * 4) + n_seq * H * 2 * 4 * N * N
+    issued = (tokens // CHUNK_L) * H * chunk_mfma_flops_per_chunk_head_precise()
+    sec = k_ms * 1e-3
     return {"workload": "prefill_b8_t4096_h32_f32in_f32state",
             "kernel": "chunk_p_kernel<fp32, precise> (chunks of 32, "
                       "split-bf16 products)",
@@ -328,6 +341,10 @@ def run_prefill_f32(steps: int = 5, warmup: int = 3, seed: int = 2):
                     "frac": bytes_alg / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                     "bytes_per_launch": bytes_alg,
                     "traffic": load_traffic("prefill_f32", bytes_alg)},
+            "mfma": {"issued_tflops": issued / sec / 1e12,
+                     "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "util": issued / sec / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+                     "issued_flops_per_launch": issued},
             "steps": steps, "warmup": warmup}
 
 
