@@ -1022,7 +1022,8 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
     __syncthreads();                                              // TOT of chunk 0
     // fallback flags of chunk step - 1, known from the end of the step
     // before: early (its inputs or decays out of the chunked form's range)
-    // and gram (its Gram matrices or T out of the fp16 range)
+    // and gram (its Gram matrices, in the precise plan also T, out of the
+    // fp16 range; the fast plan checks T in the second interval)
     bool early_prev = false, gram_prev = false;
     // The start state has arrived before the loop: without this wait the
     // compiler keeps S's registers pending from these loads and, at every
