@@ -126,13 +126,14 @@ def test_segment_split_is_batch_invariant():
     assert _bits_equal(Sa, Sb)
 
 
-def test_segment_plan_and_graph_equal_forward():
+@pytest.mark.parametrize("dtype,precise", PATHS)
+def test_segment_plan_and_graph_equal_forward(dtype, precise):
     lens = [1, 900, 70, 1300]
     ids = np.array([2, 0, 3, 1], np.int32)
     init = G.draw_states(np.random.default_rng(11), 4, H, 64)
-    b = G.make_batch(np.random.default_rng(12), ids, lens, H, 64, G.BF16)
+    b = G.make_batch(np.random.default_rng(12), ids, lens, H, 64, dtype)
     x = to_dev(b)
-    pf, pp, pg = _pool(4), _pool(4), _pool(4)
+    pf, pp, pg = (_pool(4, dtype_precise=precise) for _ in range(3))
     plan_p = plan_g = None
     try:
         for p in (pf, pp, pg):
