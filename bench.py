@@ -1249,7 +1249,8 @@ def main(argv=None) -> int:
                     default="decode,prefill,decode_cold,decode_large,"
                             "prefill_f32,prefill_ragged,mixed,prefill_long,"
                             "q8_proj,small,short,ceilings",
-                    help="comma list of legs to run (profiling one kernel)")
+                    help="comma list of legs to run (default: all of them; a "
+                         "subset when profiling one kernel)")
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--pmc-summary", nargs="+", metavar="CSV",
                     help="summarise rocprofv3 counter CSVs (no GPU use) for "
