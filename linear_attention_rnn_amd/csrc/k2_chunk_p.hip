@@ -394,14 +394,15 @@ template <> struct Raw<WKV7_F32> {
 
 // rows 4 rg + e (e < 4): a t wavefront holds r, a and w, an s wavefront k,
 // b, v and w
-template <int DT> struct RawT { typename Raw<DT>::W r[4], a[4], w[4]; };
-template <int DT> struct RawS { typename Raw<DT>::W k[4], b[4], v[4], w[4]; };
+template <int DT> struct RawT { static constexpr int kDT = DT; typename Raw<DT>::W r[4], a[4], w[4]; };
+template <int DT> struct RawS { static constexpr int kDT = DT; typename Raw<DT>::W k[4], b[4], v[4], w[4]; };
 
-// Loads through buffer resources based at the chunk's first row, with a
-// 32-bit lane offset and no branch: a row past the chunk's end re-reads the
-// last valid row (always in bounds). The caller replaces such rows by
-// padding (pad_raw) when it consumes them, so nothing waits on the loads
-// here.
+// Loads through buffer resources based at the chunk's first row and sized
+// to its n rows, with a 32-bit lane offset and no branch: a row past the
+// chunk's end lies outside the resource, and the buffer load returns zero
+// for it without touching memory. Zero is the padding of every input but
+// w, whose padding (1) the caller sets (pad_raw) when it consumes the
+// rows, so nothing waits on the loads here.
 template <int DT, int NA>
 __device__ __forceinline__ void load_rows(typename Raw<DT>::W (*const dst[NA])[4],
                                           const void* const src[NA],
@@ -420,7 +421,7 @@ __device__ __forceinline__ void load_rows(typename Raw<DT>::W (*const dst[NA])[4
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int voff = static_cast<int>(
-        static_cast<uint32_t>(min(4 * rg + e, n - 1)) * rowb + 2 * es * jp);
+        static_cast<uint32_t>(4 * rg + e) * rowb + 2 * es * jp);
 #pragma unroll
     for (int u = 0; u < NA; ++u) (*dst[u])[e] = Raw<DT>::load(rs[u], voff);
   }
@@ -432,29 +433,13 @@ __device__ __forceinline__ void load_raw(RawT<DT>& x, const SeqArgs& p, int t0,
   const void* const src[3] = {p.r, p.a, p.w};
   load_rows<DT, 3>(dst, src, p, t0, n, h, rg, jp);
 }
-// rows 4 rg + e >= n become padding: w = 1, everything else 0 (state unchanged)
-template <int DT>
-__device__ __forceinline__ void pad_raw(RawT<DT>& x, int n, int rg) {
-  typedef Raw<DT> R;
+// rows 4 rg + e >= n become padding: w = 1, everything else 0 (the loads
+// returned zero for them), which leaves the state unchanged
+template <typename X>
+__device__ __forceinline__ void pad_raw(X& x, int n, int rg) {
+  typedef Raw<X::kDT> R;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const bool pad = 4 * rg + e >= n;
-    x.r[e] = pad ? R::zero() : x.r[e];
-    x.a[e] = pad ? R::zero() : x.a[e];
-    x.w[e] = pad ? R::one() : x.w[e];
-  }
-}
-template <int DT>
-__device__ __forceinline__ void pad_raw(RawS<DT>& x, int n, int rg) {
-  typedef Raw<DT> R;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const bool pad = 4 * rg + e >= n;
-    x.k[e] = pad ? R::zero() : x.k[e];
-    x.b[e] = pad ? R::zero() : x.b[e];
-    x.v[e] = pad ? R::zero() : x.v[e];
-    x.w[e] = pad ? R::one() : x.w[e];
-  }
+  for (int e = 0; e < 4; ++e) x.w[e] = 4 * rg + e >= n ? R::one() : x.w[e];
 }
 
 // ---- T = (I - A_ab)^-1 from fp16 fragments (value wavefronts 0 and 1) ----
@@ -655,7 +640,7 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
     s_in = s_out;
   }
   // Every item holds at least one token (the host drops empty sequences,
-  // and segments are never empty); the clamped loads rely on it.
+  // and segments are never empty).
   if (len <= 0) return;
   const bool zero_v = (flags & kSegZeroV) != 0;
   const bool no_out = (flags & kSegNoOut) != 0;
@@ -919,11 +904,11 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
       // ===== interval 1 =====
       load_w(cK + 1);
       bool bad_k = false;
-      float suf0 = 0.f, suf1 = 0.f;
+      // decay-scaled b and k of the thread's rows and channels: the Gram
+      // operands now, the value side's operands in the second interval
+      float bt0[4], bt1[4], kt0[4], kt1[4];
       if (k_on) {
         const Dec d = chunk_decays(Wc);
-        suf0 = d.suf0;
-        suf1 = d.suf1;
         if (rg == 0) { LAMb[bK * 64 + j0] = d.lam0; LAMb[bK * 64 + j0 + 1] = d.lam1; }
         // range of the raw inputs (|Bbar| <= |b| etc. when every |w| <= 1);
         // v is zero on a run with kSegZeroV
@@ -940,8 +925,10 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
   #pragma unroll
         for (int e = 3; e >= 0; --e) {
           const int t = 4 * rg + e;
-          put2p(Bbar, kM64, kP64, t, j0, R::c0(x.b[e]) * sfx0, R::c1(x.b[e]) * sfx1);
-          put2p(Kbar, kM64, kP64, t, j0, R::c0(x.k[e]) * sfx0, R::c1(x.k[e]) * sfx1);
+          bt0[e] = R::c0(x.b[e]) * sfx0; bt1[e] = R::c1(x.b[e]) * sfx1;
+          kt0[e] = R::c0(x.k[e]) * sfx0; kt1[e] = R::c1(x.k[e]) * sfx1;
+          put2p(Bbar, kM64, kP64, t, j0, bt0[e], bt1[e]);
+          put2p(Kbar, kM64, kP64, t, j0, kt0[e], kt1[e]);
           sfx0 *= w0[e]; sfx1 *= w1[e];
         }
       }
@@ -953,20 +940,16 @@ void chunk_p_kernel(SeqArgs p, const SegItem* segs, const WorkItem* dec,
       // ===== interval 2 =====
       if (k_on) {
         // the value side's operands, read in the next step: built here,
-        // where this role waits on the value side anyway, from the same
-        // products as the Gram operands (the same values)
+        // where this role waits on the value side anyway, from the Gram
+        // operands' products
         VE* BbT = VOk + M::BbT;
         VE* KbT = VOk + M::KbT;
         VE* Vt = VOk + M::Vt;
-        float sfx0 = suf0, sfx1 = suf1;
-        float bt0[4], bt1[4], kt0[4], kt1[4], vt0[4], vt1[4];
+        float vt0[4], vt1[4];
   #pragma unroll
-        for (int e = 3; e >= 0; --e) {
-          bt0[e] = R::c0(x.b[e]) * sfx0; bt1[e] = R::c1(x.b[e]) * sfx1;
-          kt0[e] = R::c0(x.k[e]) * sfx0; kt1[e] = R::c1(x.k[e]) * sfx1;
+        for (int e = 0; e < 4; ++e) {
           vt0[e] = zero_v ? 0.f : R::c0(x.v[e]);
           vt1[e] = zero_v ? 0.f : R::c1(x.v[e]);
-          sfx0 *= w0[e]; sfx1 *= w1[e];
         }
         auto put4 = [&](VE* m, int row, const float (&v)[4]) {
           if constexpr (PRE)
