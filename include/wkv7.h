@@ -154,6 +154,13 @@ void* wkv7_pool_state_ptr(wkv7_pool* pool);
 wkv7_status wkv7_pool_shape(const wkv7_pool* pool, int32_t* n_slots,
                             int32_t* H, int32_t* N);
 
+/* The HIP device that holds the pool's memory and runs its launches (the
+ * device current at wkv7_pool_create). The input, output and buffer
+ * pointers of every call on the pool must be memory of this device; the
+ * library cannot check a raw device pointer's device, so a binding that
+ * holds typed tensors checks it (the Python binding does). */
+wkv7_status wkv7_pool_device(const wkv7_pool* pool, int32_t* device);
+
 /* Set a pool option (see WKV7_OPT_*). */
 wkv7_status wkv7_pool_set_option(wkv7_pool* pool, int32_t opt, int64_t val);
 

@@ -602,6 +602,14 @@ wkv7_status wkv7_pool_shape(const wkv7_pool* p, int32_t* n_slots, int32_t* H,
   return WKV7_OK;
 }
 
+wkv7_status wkv7_pool_device(const wkv7_pool* p, int32_t* device) {
+  g_last_error.clear();
+  if (wkv7_status st = check_pool(p)) return st;
+  if (!device) return fail(WKV7_ERR_INVALID_ARG, "device is NULL");
+  *device = p->device;
+  return WKV7_OK;
+}
+
 wkv7_status wkv7_pool_set_option(wkv7_pool* p, int32_t opt, int64_t val) {
   g_last_error.clear();
   if (wkv7_status st = check_pool(p)) return st;

@@ -41,7 +41,8 @@ WKV7_OPT_SEGMENT_LEN = 3
 EXPORTS = (
     "wkv7_last_error", "wkv7_version", "wkv7_pool_create", "wkv7_pool_destroy",
     "wkv7_slot_bytes", "wkv7_pool_state_ptr", "wkv7_pool_shape",
-    "wkv7_pool_set_option", "wkv7_slot_alloc", "wkv7_slot_free",
+    "wkv7_pool_device", "wkv7_pool_set_option", "wkv7_slot_alloc",
+    "wkv7_slot_free",
     "wkv7_forward", "wkv7_forward_noalloc", "wkv7_snapshot", "wkv7_fork", "wkv7_reset",
     "wkv7_hibernate", "wkv7_resume", "wkv7_plan_create", "wkv7_plan_tokens",
     "wkv7_forward_plan", "wkv7_plan_destroy", "wkv7_migrate",
@@ -127,6 +128,8 @@ lib.wkv7_pool_state_ptr.restype = _vp
 lib.wkv7_pool_state_ptr.argtypes = [_vp]
 lib.wkv7_pool_shape.restype = _i32
 lib.wkv7_pool_shape.argtypes = [_vp, _pi32, _pi32, _pi32]
+lib.wkv7_pool_device.restype = _i32
+lib.wkv7_pool_device.argtypes = [_vp, _pi32]
 lib.wkv7_pool_set_option.restype = _i32
 lib.wkv7_pool_set_option.argtypes = [_vp, _i32, _i64]
 lib.wkv7_slot_alloc.restype = _i32
@@ -232,15 +235,16 @@ def _dtype_code(t) -> int:
 
 
 def _check_io(T_tot: Optional[int], H: Optional[int], dtype: Optional[int],
-              ins, o) -> None:
+              ins, o, device: Optional[int] = None) -> None:
     """Argument checks the library cannot make on raw pointers, raised as
     ValueError before any call: r..b must be contiguous tensors of one dtype,
-    o a contiguous float32 tensor, all on one GPU, each with at least
-    T_tot * H * 64 elements (the rows the call reads or writes), and a
-    dtype code given explicitly must match the inputs' element width. An
-    unsupported dtype, a misaligned pointer or a NULL tensor is left to the
-    library, which rejects it with its own status. T_tot/H None: not yet
-    known (the element counts are then checked by the caller's second call).
+    o a contiguous float32 tensor, all on one GPU (the pool's, `device`,
+    when given), each with at least T_tot * H * 64 elements (the rows the
+    call reads or writes), and a dtype code given explicitly must match the
+    inputs' element width. An unsupported dtype, a misaligned pointer or a
+    NULL tensor is left to the library, which rejects it with its own
+    status. T_tot/H/device None: not yet known (checked by the caller's
+    second call, after it has queried the pool).
     """
     import torch
     named = list(zip(("r", "w", "k", "v", "a", "b"), ins)) + [("o", o)]
@@ -278,6 +282,11 @@ def _check_io(T_tot: Optional[int], H: Optional[int], dtype: Optional[int],
             raise ValueError(f"{n} is on {t.device}, not on a GPU")
     if len(devs) > 1:
         raise ValueError("r..b and o must be on one GPU")
+    if device is not None:
+        for n, t in present:
+            if t.device.index != device:
+                raise ValueError(f"{n} is on {t.device}; the pool's memory is "
+                                 f"on device {device}")
 
 
 def wkv7_version() -> int:
@@ -313,6 +322,12 @@ def wkv7_pool_shape(pool: int):
     return n.value, h.value, d.value
 
 
+def wkv7_pool_device(pool: int) -> int:
+    d = _i32()
+    _check(lib.wkv7_pool_device(pool, ctypes.byref(d)))
+    return d.value
+
+
 def wkv7_pool_set_option(pool: int, opt: int, val: int) -> None:
     _check(lib.wkv7_pool_set_option(pool, opt, val))
 
@@ -337,7 +352,7 @@ def wkv7_forward(pool: int, slot_ids, cu_seqlens, r, w, k, v, a, b, o,
         raise ValueError("cu_seqlens must have len(slot_ids) + 1 entries")
     _check_io(None, None, dtype, (r, w, k, v, a, b), o)
     _check_io(int(cu[-1]), wkv7_pool_shape(pool)[1], dtype,
-              (r, w, k, v, a, b), o)
+              (r, w, k, v, a, b), o, wkv7_pool_device(pool))
     code = _dtype_code(r) if dtype is None else dtype
     _check(lib.wkv7_forward(pool, _iptr(ids), _iptr(cu), ids.size, code,
                             _dptr(r), _dptr(w), _dptr(k), _dptr(v), _dptr(a),
@@ -353,7 +368,7 @@ def wkv7_forward_noalloc(pool: int, slot_ids, cu_seqlens, r, w, k, v, a, b,
         raise ValueError("cu_seqlens must have len(slot_ids) + 1 entries")
     _check_io(None, None, dtype, (r, w, k, v, a, b), o)
     _check_io(int(cu[-1]), wkv7_pool_shape(pool)[1], dtype,
-              (r, w, k, v, a, b), o)
+              (r, w, k, v, a, b), o, wkv7_pool_device(pool))
     code = _dtype_code(r) if dtype is None else dtype
     _check(lib.wkv7_forward_noalloc(pool, _iptr(ids), _iptr(cu), ids.size,
                                     code, _dptr(r), _dptr(w), _dptr(k),
@@ -383,7 +398,7 @@ def wkv7_forward_plan(pool: int, plan: int, r, w, k, v, a, b, o, stream=None,
     _check_io(None, None, dtype, (r, w, k, v, a, b), o)
     if plan:
         _check_io(wkv7_plan_tokens(plan), wkv7_pool_shape(pool)[1], dtype,
-                  (r, w, k, v, a, b), o)
+                  (r, w, k, v, a, b), o, wkv7_pool_device(pool))
     code = _dtype_code(r) if dtype is None else dtype
     _check(lib.wkv7_forward_plan(pool, plan, code, _dptr(r), _dptr(w),
                                  _dptr(k), _dptr(v), _dptr(a), _dptr(b),

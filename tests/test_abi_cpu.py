@@ -66,6 +66,7 @@ def test_null_pool_everywhere():
     assert L.wkv7_slot_free(None, None, 0) == W.WKV7_ERR_INVALID_ARG
     assert L.wkv7_pool_set_option(None, 1, 64) == W.WKV7_ERR_INVALID_ARG
     assert L.wkv7_pool_shape(None, None, None, None) == W.WKV7_ERR_INVALID_ARG
+    assert L.wkv7_pool_device(None, None) == W.WKV7_ERR_INVALID_ARG
     assert L.wkv7_slot_bytes(None) == 0
     assert L.wkv7_pool_state_ptr(None) is None
     assert L.wkv7_pool_destroy(None) == W.WKV7_OK

@@ -233,6 +233,12 @@ def test_forward_errors_leave_pool_untouched():
             W.wkv7_forward(pool, [0, 1], [0, 1, 2], rr, x["w"], x["k"],
                            x["v"], x["a"], x["b"], o, dtype=W.WKV7_BF16)
         assert e.value.status == W.WKV7_ERR_INVALID_ARG
+        # the pool's device, and tensors claimed for another one refused by
+        # the binding (a one-GPU machine has no second device to put them on)
+        assert W.wkv7_pool_device(pool) == torch.cuda.current_device()
+        with pytest.raises(ValueError, match="pool's memory is on device"):
+            W._check_io(2, H, None, [x[n] for n in G.NAMES], o,
+                        W.wkv7_pool_device(pool) + 1)
         torch.cuda.synchronize()
         assert torch.equal(o, torch.zeros_like(o))
         after = get_states(pool, ids)
