@@ -14,6 +14,15 @@ import math
 import numpy as np
 
 
+# Summaries the tests report, printed at the end of the pytest run (the
+# terminal summary shows them even when the tests' own output is captured).
+REPORTED: list = []
+
+
+def report(line: str) -> None:
+    REPORTED.append(line)
+
+
 class ParityMeter:
     def __init__(self, name: str = ""):
         self.name = name

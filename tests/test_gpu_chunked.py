@@ -8,6 +8,7 @@ from linear_attention_rnn_amd import wkv7 as W
 from oracle import wkv7_forward as oracle_forward, wkv7_sequence
 from tests.gpu_util import (DEV, say, set_states, get_states, run_forward,
                             rel_err, tol_for)
+from tests.parity import report
 
 pytestmark = pytest.mark.gpu
 
@@ -56,6 +57,9 @@ def test_small_config_chunked(dtype, precise):
     say(f"small config chunked dtype={dtype} precise={precise}")
     e_o, e_s, _, _ = _run([0], [64], 2, dtype, 1, precise=precise)
     say(f"  o err {e_o:.3e}  S err {e_s:.3e}")
+    report(f"small case (H=2, T=64, {dtype}), chunked kernel, "
+           f"{'precise' if precise or dtype == 'f32' else 'fast'} plan: o "
+           f"{e_o:.3e}, S {e_s:.3e}")
     assert e_o < tol_for(dtype) and e_s < tol_for(dtype)
     assert e_o < GUARD[dtype, precise] and e_s < GUARD[dtype, precise]
 

@@ -27,7 +27,7 @@ import wkv7_inputs as G
 from linear_attention_rnn_amd import wkv7 as W
 from oracle import wkv7_cref as C
 from tests.gpu_util import DEV, say, set_states, get_states
-from tests.parity import ParityMeter
+from tests.parity import ParityMeter, report
 
 pytestmark = pytest.mark.gpu
 
@@ -47,6 +47,7 @@ def _bits_equal(a, b):
 def _report(*meters):
     for m in meters:
         say("  " + m.summary())
+        report(m.summary())
 
 
 def test_decode_100_chained_steps():
@@ -121,7 +122,8 @@ def test_prefill_all_pairs(dtype):
     finally:
         W.wkv7_pool_destroy(pool)
     o = o.cpu()
-    m_o, m_s = ParityMeter("prefill o"), ParityMeter("prefill S")
+    m_o = ParityMeter(f"prefill 8 x 4096 ({dtype} inputs) o")
+    m_s = ParityMeter(f"prefill 8 x 4096 ({dtype} inputs) S")
     for s in range(len(b.slot_ids)):
         lo, hi = int(b.cu_seqlens[s]), int(b.cu_seqlens[s + 1])
         S_ref = np.zeros((H, N, N))
@@ -179,7 +181,7 @@ def test_large_pool_every_slot_and_head():
         W.wkv7_pool_destroy(pool)
 
     # decode: all 1024 slots x 64 heads
-    m_do, m_ds = ParityMeter("large decode o"), ParityMeter("large decode S")
+    m_do, m_ds = ParityMeter("4096-slot pool, decode o"), ParityMeter("4096-slot pool, decode S")
     S = np.ascontiguousarray(init_h.double().numpy().reshape(1024 * H, N, N))
     o_ref = C.run_heads(S, {n: xd[n].cpu() for n in G.NAMES}, 1, 1024 * H, N)
     m_do.add(od.cpu(), o_ref.reshape(1024, H, N), where="decode")
@@ -189,7 +191,7 @@ def test_large_pool_every_slot_and_head():
     assert m_do.value() < SEQ_GUARD and m_ds.value() < SEQ_GUARD
 
     # prefill: every sequence and head, one sequence at a time
-    m_po, m_ps = ParityMeter("large prefill o"), ParityMeter("large prefill S")
+    m_po, m_ps = ParityMeter("4096-slot pool, ragged prefill o"), ParityMeter("4096-slot pool, ragged prefill S")
     for s in range(32):
         lo, hi = int(cu_p[s]), int(cu_p[s + 1])
         S_ref = np.zeros((H, N, N))

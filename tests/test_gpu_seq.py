@@ -9,6 +9,7 @@ from linear_attention_rnn_amd import wkv7 as W
 from oracle import wkv7_forward as oracle_forward, wkv7_decode_batch
 from tests.gpu_util import (DEV, say, set_states, get_states, run_forward,
                             rel_err, tol_for)
+from tests.parity import report
 
 pytestmark = pytest.mark.gpu
 
@@ -42,6 +43,8 @@ def test_small_config_sequential(dtype):
     o_ref, S_ref = _oracle(b, {})
     e_o, e_s = rel_err(o, o_ref), rel_err(S[0], S_ref[0])
     say(f"  o err {e_o:.3e}  S err {e_s:.3e}")
+    report(f"small case (H=2, T=64, {dtype}), sequential kernel: o "
+           f"{e_o:.3e}, S {e_s:.3e}")
     assert e_o < 1e-5 and e_s < 1e-5   # fp32 sequential: rounding only
     assert e_o < tol_for(dtype)
 

@@ -16,6 +16,7 @@ from oracle import wkv7_forward as oracle_forward, wkv7_decode_batch
 from oracle import wkv7_cref as C
 from tests.gpu_util import (DEV, say, set_states, get_states, run_forward,
                             rel_err)
+from tests.parity import report
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-2          # bf16 inputs
@@ -63,6 +64,8 @@ def test_mixed_stack_and_fork_continuation(shuffle):
                 e = max(e, rel_err(o[lo:hi], o_p), rel_err(S[n], S_p))
             worst = max(worst, e)
             say(f"  layer {li}: max err {e:.3e}")
+        report(f"12-layer mixed stack (shuffle={shuffle}): worst max|err|/rms "
+               f"{worst:.3e} over the layers' outputs and final states")
         assert worst < TIGHT
 
         # fork 16 of the 68 live slots into 16 free ones, in every layer
