@@ -27,19 +27,39 @@ __device__ __forceinline__ float row_sum16(float x) {
 }
 
 // Raw input fragments: 4 consecutive channels and 16 consecutive channels.
+// With STREAM the loads carry the non-temporal hint: a call reads each
+// input once, and a state that stays in the Infinity Cache (MALL) from one
+// step to the next keeps more of it there when the inputs do not claim
+// cache lines (measured: the 256-slot decode step 45.8 -> 44.8 us with
+// fresh inputs every step; no gain where the state itself streams).
 template <int DT> struct In;
+
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+template <bool STREAM, typename V>
+__device__ __forceinline__ V ld_in(const V* p) {
+  if (STREAM) return __builtin_nontemporal_load(p);
+  return *p;
+}
 
 template <> struct In<WKV7_BF16> {
   typedef uint16_t T;
   struct R4 { uint2 u; };
   struct R16 { uint4 u[2]; };
+  template <bool STREAM = false>
   __device__ static R4 ld4(const T* p) {
-    R4 r; r.u = *reinterpret_cast<const uint2*>(p); return r;
+    const u32x2_t x = ld_in<STREAM>(reinterpret_cast<const u32x2_t*>(p));
+    R4 r; r.u = make_uint2(x[0], x[1]); return r;
   }
+  template <bool STREAM = false>
   __device__ static R16 ld16(const T* p) {
     R16 r;
-    r.u[0] = reinterpret_cast<const uint4*>(p)[0];
-    r.u[1] = reinterpret_cast<const uint4*>(p)[1];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const u32x4_t x = ld_in<STREAM>(reinterpret_cast<const u32x4_t*>(p) + q);
+      r.u[q] = make_uint4(x[0], x[1], x[2], x[3]);
+    }
     return r;
   }
   __device__ static float ld1(const T* p) {
@@ -68,13 +88,19 @@ template <> struct In<WKV7_F32> {
   typedef float T;
   struct R4 { float4 u; };
   struct R16 { float4 u[4]; };
+  template <bool STREAM = false>
   __device__ static R4 ld4(const T* p) {
-    R4 r; r.u = *reinterpret_cast<const float4*>(p); return r;
+    const f32x4_t x = ld_in<STREAM>(reinterpret_cast<const f32x4_t*>(p));
+    R4 r; r.u = make_float4(x[0], x[1], x[2], x[3]); return r;
   }
+  template <bool STREAM = false>
   __device__ static R16 ld16(const T* p) {
     R16 r;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) r.u[q] = reinterpret_cast<const float4*>(p)[q];
+    for (int q = 0; q < 4; ++q) {
+      const f32x4_t x = ld_in<STREAM>(reinterpret_cast<const f32x4_t*>(p) + q);
+      r.u[q] = make_float4(x[0], x[1], x[2], x[3]);
+    }
     return r;
   }
   __device__ static float ld1(const T* p) { return *p; }
@@ -96,17 +122,17 @@ struct TokenRaw {
   typename In<DT>::R16 v;
 };
 
-template <int DT>
+template <int DT, bool STREAM>
 __device__ __forceinline__ void load_token(TokenRaw<DT>& x,
                                            const typename In<DT>::T* const* src,
                                            size_t off, int c, int g) {
   using I = In<DT>;
-  x.r = I::ld4(src[0] + off + 4 * c);
-  x.w = I::ld4(src[1] + off + 4 * c);
-  x.k = I::ld4(src[2] + off + 4 * c);
-  x.a = I::ld4(src[4] + off + 4 * c);
-  x.b = I::ld4(src[5] + off + 4 * c);
-  x.v = I::ld16(src[3] + off + 16 * g);
+  x.r = I::template ld4<STREAM>(src[0] + off + 4 * c);
+  x.w = I::template ld4<STREAM>(src[1] + off + 4 * c);
+  x.k = I::template ld4<STREAM>(src[2] + off + 4 * c);
+  x.a = I::template ld4<STREAM>(src[4] + off + 4 * c);
+  x.b = I::template ld4<STREAM>(src[5] + off + 4 * c);
+  x.v = I::template ld16<STREAM>(src[3] + off + 16 * g);
 }
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -181,10 +207,10 @@ __device__ __forceinline__ void seq_wave(const SeqArgs& p, const WorkItem it,
   size_t off = (static_cast<size_t>(it.tok0) * p.H + h) * kN;
 
   TokenRaw<DT> nxt;
-  load_token<DT>(nxt, src, off, c, g);
+  load_token<DT, !NT>(nxt, src, off, c, g);   // state cached: inputs streamed
   for (int t = 0; t < it.len; ++t) {
     TokenRaw<DT> cur = nxt;
-    if (t + 1 < it.len) load_token<DT>(nxt, src, off + tstride, c, g);
+    if (t + 1 < it.len) load_token<DT, !NT>(nxt, src, off + tstride, c, g);
     float w[4], a[4], b[4], k[4], r[4], v[16];
     I::cvt4(cur.w, w); I::cvt4(cur.a, a); I::cvt4(cur.b, b);
     I::cvt4(cur.k, k); I::cvt4(cur.r, r); I::cvt16(cur.v, v);
