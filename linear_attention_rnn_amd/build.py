@@ -44,9 +44,23 @@ COMMON = [
 ]
 
 
+# Per-source options. The chunked prefill kernel is scheduled by LLVM's
+# max-ILP machine scheduler instead of the default occupancy-driven one: its
+# launch holds one 12-wavefront workgroup per CU whatever the register count,
+# so the default scheduler's register savings buy nothing, while the
+# interleaving of independent work shortens each pipeline step (the same
+# instructions, so the same results bit for bit; measured 3-5% faster on the
+# bf16 prefills and the mixed stack, no spills, at most 163 VGPRs of the 168
+# that three wavefronts per SIMD allow).
+PER_SOURCE = {
+    "k2_chunk_p.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *COMMON, "-c", src, "-o", obj]
+    extra = PER_SOURCE.get(os.path.basename(src), [])
+    cmd = [hipcc(), *COMMON, *extra, "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{res.stdout}\n"
